@@ -1,0 +1,297 @@
+"""ctypes binding of liblora_fused.so.
+
+Argument marshalling only: every function here has the name of a C-ABI entry
+point in include/lora_fused.h, takes torch device tensors, checks their dtype
+and contiguity, and passes raw pointers plus the current HIP stream.  PyTorch
+supplies device memory and streams; every step of the layer runs in the
+library's HIP kernels.  There is no fallback: if the library is missing or was
+built for something else, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblora_fused.so")
+
+LORA_OK = 0
+STATUS_NAMES = {0: "LORA_OK", -1: "LORA_ERR_INVALID_ARG", -2: "LORA_ERR_UNSUPPORTED",
+                -3: "LORA_ERR_WORKSPACE", -4: "LORA_ERR_HIP"}
+
+# Every symbol the header declares (checked by the CPU tests).
+EXPORTS = [
+    "lora_linear_fwd_workspace_size", "lora_linear_fwd", "lora_linear_bwd_workspace_size",
+    "lora_linear_bwd", "multi_lora_fwd_workspace_size", "multi_lora_linear_fwd",
+    "multi_lora_bwd_workspace_size", "multi_lora_linear_bwd", "multi_lora_check_segments",
+    "lora_dropout_mask", "lora_frozen_fwd", "lora_frozen_bwd", "lora_profiling_enable",
+    "lora_profiling_reset", "lora_profiling_query", "lora_status_string",
+    "lora_last_error_message",
+]
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class LoraAdapter(ctypes.Structure):
+    """Mirror of lora_adapter (48 bytes)."""
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("dA", ctypes.c_void_p),
+                ("dB", ctypes.c_void_p), ("r", ctypes.c_int32), ("alpha", ctypes.c_float),
+                ("p", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with __graft_entry__.build() "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, U64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                 ctypes.c_float, ctypes.c_size_t)
+    sigs = {
+        "lora_linear_fwd_workspace_size": (SZ, [I64, I64, I64, I32]),
+        "lora_linear_bwd_workspace_size": (SZ, [I64, I64, I64, I32]),
+        "multi_lora_fwd_workspace_size": (SZ, [I64, I64, I64, I32, I32, I32]),
+        "multi_lora_bwd_workspace_size": (SZ, [I64, I64, I64, I32, I32, I32]),
+        "lora_linear_fwd": (I32, [P, P, P, P, I64, I64, I64, I32, F32, F32, U64, U64, P, P, P, P,
+                                  SZ, P]),
+        "lora_linear_bwd": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, F32, F32, P, P, P, P,
+                                  SZ, P]),
+        "multi_lora_linear_fwd": (I32, [P, P, P, I32, P, P, I32, I64, I64, I64, I32, U64, U64, P,
+                                        P, P, P, SZ, P]),
+        "multi_lora_linear_bwd": (I32, [P, P, P, P, I32, P, P, I32, P, P, I64, I64, I64, I32, P,
+                                        P, SZ, P]),
+        "multi_lora_check_segments": (I32, [P, P, I32, I64, P, I32, I32]),
+        "lora_dropout_mask": (I32, [U64, U64, I64, I64, F32, P, P]),
+        "lora_frozen_fwd": (I32, [P, P, I64, I64, I64, P, P]),
+        "lora_frozen_bwd": (I32, [P, P, I64, I64, I64, P, P]),
+        "lora_profiling_enable": (I32, [I32, I32]),
+        "lora_profiling_reset": (I32, []),
+        "lora_profiling_query": (I32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_double)]),
+        "lora_status_string": (ctypes.c_char_p, [I32]),
+        "lora_last_error_message": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != LORA_OK:
+        msg = load().lora_last_error_message().decode(errors="replace")
+        raise LoraError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------
+def lora_linear_fwd_workspace_size(m, k, n, r) -> int:
+    return int(load().lora_linear_fwd_workspace_size(m, k, n, r))
+
+
+def lora_linear_bwd_workspace_size(m, k, n, r) -> int:
+    return int(load().lora_linear_bwd_workspace_size(m, k, n, r))
+
+
+def multi_lora_fwd_workspace_size(m, k, n, r_max, num_adapters, num_segments) -> int:
+    return int(load().multi_lora_fwd_workspace_size(m, k, n, r_max, num_adapters, num_segments))
+
+
+def multi_lora_bwd_workspace_size(m, k, n, r_max, num_adapters, num_segments) -> int:
+    return int(load().multi_lora_bwd_workspace_size(m, k, n, r_max, num_adapters, num_segments))
+
+
+def lora_linear_fwd(X, W, A, B, alpha: float, p: float, seed: int = 0, offset: int = 0, *,
+                    Y=None, S=None, keep_bits=None, workspace=None, stream=None):
+    """Returns (Y, S, keep_bits); outputs are allocated when not given."""
+    for t, nm in ((X, "X"), (W, "W"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, nm)
+    m, k = X.shape
+    n = W.shape[1]
+    r = A.shape[1]
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    if S is None:
+        S = torch.empty((m, r), dtype=torch.float32, device=dev)
+    if keep_bits is None and p != 0.0:
+        keep_bits = torch.empty((m, (k + 31) // 32), dtype=torch.int32, device=dev)
+    ws = _workspace(lora_linear_fwd_workspace_size(m, k, n, r), dev, workspace)
+    _check(load().lora_linear_fwd(_ptr(X), _ptr(W), _ptr(A), _ptr(B), m, k, n, r, alpha, p, seed,
+                                  offset, _ptr(Y), _ptr(S), _ptr(keep_bits), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return Y, S, keep_bits
+
+
+def lora_linear_bwd(dY, X, W, A, B, S, keep_bits, alpha: float, p: float, *, dX=None, dA=None,
+                    dB=None, workspace=None, stream=None):
+    """Returns (dX, dA, dB)."""
+    for t, nm in ((dY, "dY"), (X, "X"), (W, "W"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, nm)
+    _need(S, torch.float32, "S")
+    m, k = X.shape
+    n = W.shape[1]
+    r = A.shape[1]
+    dev = X.device
+    dX = torch.empty((m, k), dtype=torch.bfloat16, device=dev) if dX is None else dX
+    dA = torch.empty((k, r), dtype=torch.bfloat16, device=dev) if dA is None else dA
+    dB = torch.empty((r, n), dtype=torch.bfloat16, device=dev) if dB is None else dB
+    ws = _workspace(lora_linear_bwd_workspace_size(m, k, n, r), dev, workspace)
+    _check(load().lora_linear_bwd(_ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(S),
+                                  _ptr(keep_bits), m, k, n, r, alpha, p, _ptr(dX), _ptr(dA),
+                                  _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)))
+    return dX, dA, dB
+
+
+def adapter_table(As: Sequence[torch.Tensor], Bs: Sequence[torch.Tensor], alphas, ps,
+                  dAs: Optional[Sequence[torch.Tensor]] = None,
+                  dBs: Optional[Sequence[torch.Tensor]] = None, device=None) -> torch.Tensor:
+    """Pack lora_adapter records into a device uint8 tensor (the table the
+    multi-adapter calls read on the device)."""
+    n = len(As)
+    recs = (LoraAdapter * n)()
+    for i in range(n):
+        recs[i].A = As[i].data_ptr()
+        recs[i].B = Bs[i].data_ptr()
+        recs[i].dA = dAs[i].data_ptr() if dAs is not None else 0
+        recs[i].dB = dBs[i].data_ptr() if dBs is not None else 0
+        recs[i].r = As[i].shape[1]
+        recs[i].alpha = float(alphas[i])
+        recs[i].p = float(ps[i])
+        recs[i].reserved = 0
+    raw = bytes(recs)
+    host = torch.frombuffer(bytearray(raw), dtype=torch.uint8)
+    return host.to(device if device is not None else As[0].device)
+
+
+def multi_lora_linear_fwd(X, W, adapters: torch.Tensor, num_adapters: int, seg_off, seg_adapter,
+                          r_max: int, seed: int = 0, offset: int = 0, *, Y=None, S=None,
+                          keep_bits=None, workspace=None, stream=None):
+    _need(X, torch.bfloat16, "X")
+    _need(W, torch.bfloat16, "W")
+    _need(seg_off, torch.int64, "seg_off")
+    _need(seg_adapter, torch.int32, "seg_adapter")
+    m, k = X.shape
+    n = W.shape[1]
+    nseg = seg_adapter.numel()
+    dev = X.device
+    Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if Y is None else Y
+    S = torch.empty((m, r_max), dtype=torch.float32, device=dev) if S is None else S
+    if keep_bits is None:
+        keep_bits = torch.empty((m, (k + 31) // 32), dtype=torch.int32, device=dev)
+    ws = _workspace(multi_lora_fwd_workspace_size(m, k, n, r_max, num_adapters, nseg), dev,
+                    workspace)
+    _check(load().multi_lora_linear_fwd(_ptr(X), _ptr(W), _ptr(adapters), num_adapters,
+                                        _ptr(seg_off), _ptr(seg_adapter), nseg, m, k, n, r_max,
+                                        seed, offset, _ptr(Y), _ptr(S), _ptr(keep_bits), _ptr(ws),
+                                        ws.numel(), _stream(stream)))
+    return Y, S, keep_bits
+
+
+def multi_lora_linear_bwd(dY, X, W, adapters: torch.Tensor, num_adapters: int, seg_off,
+                          seg_adapter, S, keep_bits, r_max: int, *, dX=None, workspace=None,
+                          stream=None):
+    _need(dY, torch.bfloat16, "dY")
+    _need(X, torch.bfloat16, "X")
+    _need(W, torch.bfloat16, "W")
+    _need(S, torch.float32, "S")
+    m, k = X.shape
+    n = W.shape[1]
+    nseg = seg_adapter.numel()
+    dev = X.device
+    dX = torch.empty((m, k), dtype=torch.bfloat16, device=dev) if dX is None else dX
+    ws = _workspace(multi_lora_bwd_workspace_size(m, k, n, r_max, num_adapters, nseg), dev,
+                    workspace)
+    _check(load().multi_lora_linear_bwd(_ptr(dY), _ptr(X), _ptr(W), _ptr(adapters), num_adapters,
+                                        _ptr(seg_off), _ptr(seg_adapter), nseg, _ptr(S),
+                                        _ptr(keep_bits), m, k, n, r_max, _ptr(dX), _ptr(ws),
+                                        ws.numel(), _stream(stream)))
+    return dX
+
+
+def multi_lora_check_segments(seg_off: Sequence[int], seg_adapter: Sequence[int], m: int,
+                              ranks: Sequence[int], r_max: int) -> None:
+    so = (ctypes.c_int64 * len(seg_off))(*[int(v) for v in seg_off])
+    sa = (ctypes.c_int32 * len(seg_adapter))(*[int(v) for v in seg_adapter])
+    rk = (ctypes.c_int32 * len(ranks))(*[int(v) for v in ranks])
+    _check(load().multi_lora_check_segments(so, sa, len(seg_adapter), m, rk, len(ranks), r_max))
+
+
+def lora_dropout_mask(seed: int, offset: int, m: int, k: int, p: float, keep_bits=None,
+                      device="cuda", stream=None):
+    if keep_bits is None:
+        keep_bits = torch.empty((m, (k + 31) // 32), dtype=torch.int32, device=device)
+    _check(load().lora_dropout_mask(seed, offset, m, k, p, _ptr(keep_bits), _stream(stream)))
+    return keep_bits
+
+
+def lora_frozen_fwd(X, W, *, Y=None, stream=None):
+    m, k = X.shape
+    n = W.shape[1]
+    Y = torch.empty((m, n), dtype=torch.bfloat16, device=X.device) if Y is None else Y
+    _check(load().lora_frozen_fwd(_ptr(X), _ptr(W), m, k, n, _ptr(Y), _stream(stream)))
+    return Y
+
+
+def lora_frozen_bwd(dY, W, *, dX=None, stream=None):
+    m, n = dY.shape
+    k = W.shape[0]
+    dX = torch.empty((m, k), dtype=torch.bfloat16, device=dY.device) if dX is None else dX
+    _check(load().lora_frozen_bwd(_ptr(dY), _ptr(W), m, k, n, _ptr(dX), _stream(stream)))
+    return dX
+
+
+def lora_profiling_enable(enable: bool = True, capacity: int = 4096) -> None:
+    _check(load().lora_profiling_enable(1 if enable else 0, capacity))
+
+
+def lora_profiling_reset() -> None:
+    _check(load().lora_profiling_reset())
+
+
+def lora_profiling_query(name_substring: str):
+    """(launches, total_ms) of timed kernels whose name contains the string."""
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _check(load().lora_profiling_query(name_substring.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

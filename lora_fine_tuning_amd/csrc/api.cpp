@@ -1,0 +1,569 @@
+// C-ABI layer of the gfx950 LoRA library: host-side argument checks,
+// workspace planning and the kernel sequence of each entry point.  No entry
+// point allocates device memory or synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "lora_fused.h"
+
+namespace lora {
+size_t b1_lds_bytes(int C1, int r_lds);
+size_t b2_lds_bytes(int C2, int r_lds);
+}  // namespace lora
+
+using namespace lora;
+
+// ---------------------------------------------------------------------------
+// Error reporting
+// ---------------------------------------------------------------------------
+static thread_local std::string g_last_error;
+
+static lora_status fail(lora_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+static lora_status hip_fail(hipError_t e, const char *what) {
+    return fail(LORA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+extern "C" const char *lora_status_string(lora_status s) {
+    switch (s) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_INVALID_ARG: return "LORA_ERR_INVALID_ARG";
+    case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED";
+    case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE";
+    case LORA_ERR_HIP: return "LORA_ERR_HIP";
+    }
+    return "LORA_ERR_UNKNOWN";
+}
+
+extern "C" const char *lora_last_error_message(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------
+// Kernel timing pool
+// ---------------------------------------------------------------------------
+namespace {
+struct ProfSlot {
+    const char *name;
+    hipEvent_t ev0, ev1;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfSlot> g_prof_pool;
+size_t g_prof_used = 0;
+}  // namespace
+
+namespace lora {
+int prof_begin(const char *name, hipStream_t stream) {
+    if (!g_prof_on) return -1;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_used >= g_prof_pool.size()) return -1;
+    const int slot = (int)g_prof_used++;
+    g_prof_pool[slot].name = name;
+    (void)hipEventRecord(g_prof_pool[slot].ev0, stream);
+    return slot;
+}
+void prof_end(int slot, hipStream_t stream) {
+    if (slot < 0) return;
+    (void)hipEventRecord(g_prof_pool[slot].ev1, stream);
+}
+}  // namespace lora
+
+extern "C" lora_status lora_profiling_enable(int32_t enable, int32_t capacity) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto &s : g_prof_pool) {
+        (void)hipEventDestroy(s.ev0);
+        (void)hipEventDestroy(s.ev1);
+    }
+    g_prof_pool.clear();
+    g_prof_used = 0;
+    g_prof_on = false;
+    if (!enable) return LORA_OK;
+    if (capacity <= 0 || capacity > (1 << 20)) return fail(LORA_ERR_INVALID_ARG, "profiling capacity %d", capacity);
+    g_prof_pool.resize((size_t)capacity);
+    for (auto &s : g_prof_pool) {
+        s.name = "";
+        hipError_t e0 = hipEventCreate(&s.ev0);
+        hipError_t e1 = hipEventCreate(&s.ev1);
+        if (e0 != hipSuccess || e1 != hipSuccess) {
+            g_prof_pool.clear();
+            return hip_fail(e0 != hipSuccess ? e0 : e1, "hipEventCreate");
+        }
+    }
+    g_prof_on = true;
+    return LORA_OK;
+}
+
+extern "C" lora_status lora_profiling_reset(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_used = 0;
+    return LORA_OK;
+}
+
+extern "C" lora_status lora_profiling_query(const char *name_substring, int64_t *launches, double *total_ms) {
+    if (!name_substring || !launches || !total_ms) return fail(LORA_ERR_INVALID_ARG, "NULL argument");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    int64_t n = 0;
+    double tot = 0.0;
+    for (size_t i = 0; i < g_prof_used; ++i) {
+        const ProfSlot &s = g_prof_pool[i];
+        if (!std::strstr(s.name, name_substring)) continue;
+        hipError_t e = hipEventSynchronize(s.ev1);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, s.ev0, s.ev1);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        ++n;
+        tot += ms;
+    }
+    *launches = n;
+    *total_ms = tot;
+    return LORA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Argument checks
+// ---------------------------------------------------------------------------
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQUIRE(cond, ...)                                        \
+    do {                                                          \
+        if (!(cond)) return fail(LORA_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+static lora_status check_shape(int64_t m, int64_t k, int64_t n) {
+    REQUIRE(m >= 0 && m < (1LL << 31), "m = %lld out of range [0, 2^31)", (long long)m);
+    REQUIRE(k > 0 && k < (1LL << 31), "k = %lld out of range (0, 2^31)", (long long)k);
+    REQUIRE(n > 0 && n < (1LL << 31), "n = %lld out of range (0, 2^31)", (long long)n);
+    REQUIRE(k % 8 == 0, "k = %lld must be a multiple of 8", (long long)k);
+    REQUIRE(n % 8 == 0, "n = %lld must be a multiple of 8", (long long)n);
+    REQUIRE(m * k < (1LL << 46) && m * n < (1LL << 46), "tensor too large");
+    return LORA_OK;
+}
+
+static lora_status check_rank(int32_t r) {
+    REQUIRE(r >= 1 && r <= 256, "rank r = %d must be in [1, 256]", r);
+    return LORA_OK;
+}
+
+static lora_status check_p(float p) {
+    REQUIRE(p >= 0.0f && p < 1.0f, "dropout p = %g must be in [0, 1)", (double)p);
+    return LORA_OK;
+}
+
+#define CHECK(x)                          \
+    do {                                  \
+        lora_status _st = (x);            \
+        if (_st != LORA_OK) return _st;   \
+    } while (0)
+
+#define REQ_PTR(p, align) \
+    REQUIRE((p) != nullptr && aligned((p), (align)), #p " must be non-NULL and %d-byte aligned", (int)(align))
+
+// ---------------------------------------------------------------------------
+// Workspace plans
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+struct Carve {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    }
+};
+
+struct FwdPlan {
+    int RS;
+    int chunk_cap_f1;  // grid size of F1 (upper bound on chunks)
+    int chunk_cap_bwd;
+    int KS, ksl;
+    size_t off_spart, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
+    size_t bytes;
+};
+
+// F1 splits k into KS slices (multiples of its 128-column staging slice) so
+// the grid has about 1024 work-groups; partials are summed by a second pass.
+FwdPlan plan_fwd(int64_t m, int64_t k, int32_t RS, bool multi, int32_t nseg) {
+    FwdPlan p{};
+    p.RS = RS;
+    p.chunk_cap_f1 = cdiv(m, kF1Rows) + (multi ? nseg : 0);
+    p.chunk_cap_bwd = cdiv(m, kBwdRows) + (multi ? nseg : 0);
+    const int kslices = cdiv(k, kF1KSub);
+    int KS = std::max(1, std::min(kslices, cdiv(1024, std::max(1, p.chunk_cap_f1))));
+    const int per = cdiv(kslices, KS);
+    p.ksl = per * kF1KSub;
+    p.KS = cdiv(k, p.ksl);
+    Carve c;
+    p.off_spart = c.take(p.KS > 1 ? (size_t)p.KS * m * RS * sizeof(float) : 0);
+    if (multi) {
+        p.off_t_f1 = c.take((size_t)p.chunk_cap_f1 * sizeof(ChunkEntry));
+        p.off_c_f1 = c.take(sizeof(int32_t));
+        p.off_t_bwd = c.take((size_t)p.chunk_cap_bwd * sizeof(ChunkEntry));
+        p.off_c_bwd = c.take(sizeof(int32_t));
+    }
+    p.bytes = c.off;
+    return p;
+}
+
+struct BwdPlan {
+    int RS;
+    int chunk_cap_bwd;
+    int chunk_cap_f1;
+    int C1, C2, CT;
+    size_t off_ds, off_dspart, off_dbpart, off_dapart, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
+    size_t bytes;
+};
+
+BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_t nseg) {
+    BwdPlan p{};
+    p.RS = RS;
+    p.chunk_cap_bwd = cdiv(m, kBwdRows) + (multi ? nseg : 0);
+    p.chunk_cap_f1 = cdiv(m, kF1Rows) + (multi ? nseg : 0);
+    const int rl = ((RS + 15) / 16) * 16;
+    p.C1 = rl <= 128 ? 256 : 128;
+    p.C2 = rl <= 128 ? 256 : 128;
+    p.CT = cdiv(n, p.C1);
+    Carve c;
+    p.off_ds = c.take((size_t)m * RS * sizeof(float));
+    p.off_dspart = c.take(p.CT > 1 ? (size_t)p.CT * m * RS * sizeof(float) : 0);
+    p.off_dbpart = c.take((size_t)p.chunk_cap_bwd * RS * n * sizeof(float));
+    p.off_dapart = c.take((size_t)p.chunk_cap_bwd * k * RS * sizeof(float));
+    if (multi) {
+        p.off_t_f1 = c.take((size_t)p.chunk_cap_f1 * sizeof(ChunkEntry));
+        p.off_c_f1 = c.take(sizeof(int32_t));
+        p.off_t_bwd = c.take((size_t)p.chunk_cap_bwd * sizeof(ChunkEntry));
+        p.off_c_bwd = c.take(sizeof(int32_t));
+    }
+    p.bytes = c.off;
+    return p;
+}
+
+char *ws_at(void *ws, size_t off) { return (char *)ws + off; }
+
+AdapterSource single_source(const void *A, const void *B, void *dA, void *dB, int32_t r, float alpha, float p) {
+    AdapterSource s{};
+    s.A = A;
+    s.B = B;
+    s.dA = dA;
+    s.dB = dB;
+    s.r = r;
+    s.alpha = alpha;
+    s.p = p;
+    s.table = nullptr;
+    s.r_cap = r;
+    return s;
+}
+}  // namespace
+
+#define HIPCHK(call, what)                         \
+    do {                                           \
+        hipError_t _e = (call);                    \
+        if (_e != hipSuccess) return hip_fail(_e, what); \
+    } while (0)
+
+// ---------------------------------------------------------------------------
+// Single adapter
+// ---------------------------------------------------------------------------
+extern "C" size_t lora_linear_fwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r) {
+    (void)n;
+    if (m < 0 || k <= 0 || r < 1) return 0;
+    return plan_fwd(m, k, r, false, 0).bytes;
+}
+
+extern "C" size_t lora_linear_bwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r) {
+    if (m < 0 || k <= 0 || n <= 0 || r < 1) return 0;
+    return plan_bwd(m, k, n, r, false, 0).bytes;
+}
+
+extern "C" lora_status lora_linear_fwd(const void *X, const void *W, const void *A, const void *B,
+                                       int64_t m, int64_t k, int64_t n, int32_t r, float alpha,
+                                       float p, uint64_t seed, uint64_t offset, void *Y, float *S,
+                                       uint32_t *keep_bits, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    CHECK(check_shape(m, k, n));
+    CHECK(check_rank(r));
+    CHECK(check_p(p));
+    REQUIRE(offset % 8 == 0, "offset = %llu must be a multiple of 8", (unsigned long long)offset);
+    REQ_PTR(W, 16);
+    REQ_PTR(A, 2);
+    REQ_PTR(B, 2);
+    if (m == 0) return LORA_OK;  // nothing to compute; m-sized buffers may be NULL
+    REQ_PTR(X, 16);
+    REQ_PTR(Y, 16);
+    REQ_PTR(S, 4);
+    REQUIRE(keep_bits != nullptr || p == 0.0f, "keep_bits may be NULL only when p == 0");
+    REQUIRE(aligned(keep_bits, 4), "keep_bits must be 4-byte aligned");
+    const FwdPlan pl = plan_fwd(m, k, r, false, 0);
+    if (workspace_bytes < pl.bytes)
+        return fail(LORA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, pl.bytes);
+    if (pl.bytes) REQ_PTR(workspace, 16);
+
+    AdapterSource src = single_source(A, B, nullptr, nullptr, r, alpha, p);
+    float *sout = pl.KS > 1 ? (float *)ws_at(workspace, pl.off_spart) : S;
+    HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r, pl.KS,
+                     pl.ksl, stream), "F1 launch");
+    if (pl.KS > 1)
+        HIPCHK(launch_sum_partials(sout, pl.KS, (size_t)m * r, (size_t)m * r, S, "sum_s_partials", stream),
+               "S reduction launch");
+    HIPCHK(launch_gemm(true, 1, X, W, Y, (int)m, (int)n, (int)k, S, r, nullptr, 0, src, stream), "F2 launch");
+    return LORA_OK;
+}
+
+extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void *W, const void *A,
+                                       const void *B, const float *S, const uint32_t *keep_bits,
+                                       int64_t m, int64_t k, int64_t n, int32_t r, float alpha,
+                                       float p, void *dX, void *dA, void *dB, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    CHECK(check_shape(m, k, n));
+    CHECK(check_rank(r));
+    CHECK(check_p(p));
+    REQ_PTR(W, 16);
+    REQ_PTR(A, 2);
+    REQ_PTR(B, 2);
+    REQ_PTR(dA, 2);
+    REQ_PTR(dB, 2);
+    if (m > 0) {  // m-sized buffers may be NULL when m == 0 (then dA = dB = 0)
+        REQ_PTR(dY, 16);
+        REQ_PTR(X, 16);
+        REQ_PTR(S, 4);
+        REQ_PTR(dX, 16);
+        REQUIRE(keep_bits != nullptr || p == 0.0f, "keep_bits may be NULL only when p == 0");
+        REQUIRE(aligned(keep_bits, 4), "keep_bits must be 4-byte aligned");
+    }
+    const BwdPlan pl = plan_bwd(m, k, n, r, false, 0);
+    if (workspace_bytes < pl.bytes)
+        return fail(LORA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, pl.bytes);
+    if (pl.bytes) REQ_PTR(workspace, 16);
+
+    AdapterSource src = single_source(A, B, dA, dB, r, alpha, p);
+    float *dS = (float *)ws_at(workspace, pl.off_ds);
+    float *dSpart = pl.CT > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
+    float *dBpart = (float *)ws_at(workspace, pl.off_dbpart);
+    float *dApart = (float *)ws_at(workspace, pl.off_dapart);
+    const int chunks = pl.chunk_cap_bwd;
+    if (m > 0) {
+        HIPCHK(launch_b1(dY, S, (int)m, (int)n, r, src, chunks, pl.C1, dSpart, dBpart, stream), "B1 launch");
+        if (pl.CT > 1)
+            HIPCHK(launch_sum_partials(dSpart, pl.CT, (size_t)m * r, (size_t)m * r, dS, "sum_ds_partials", stream),
+                   "dS reduction launch");
+    }
+    HIPCHK(launch_grad_reduce(0, dBpart, (int)m, (int)k, (int)n, r, src, chunks, stream), "dB reduction launch");
+    if (m > 0)
+        HIPCHK(launch_b2(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, src, chunks, pl.C2, dApart,
+                         stream), "B2 launch");
+    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r, src, chunks, stream), "dA reduction launch");
+    if (m > 0)
+        HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r, p == 0.0f ? nullptr : keep_bits,
+                           (int)((k + 31) / 32), src, stream), "B3 launch");
+    return LORA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Multi adapter
+// ---------------------------------------------------------------------------
+static lora_status check_multi(const lora_adapter *adapters, int32_t num_adapters, const int64_t *seg_off,
+                               const int32_t *seg_adapter, int32_t num_segments, int32_t r_max) {
+    REQUIRE(adapters != nullptr && aligned(adapters, 8), "adapters must be a non-NULL 8-byte aligned device array");
+    REQUIRE(num_adapters >= 1 && num_adapters <= (1 << 20), "num_adapters = %d out of range", num_adapters);
+    REQUIRE(seg_off != nullptr && aligned(seg_off, 8), "seg_off must be non-NULL and 8-byte aligned");
+    REQUIRE(seg_adapter != nullptr && aligned(seg_adapter, 4), "seg_adapter must be non-NULL and 4-byte aligned");
+    REQUIRE(num_segments >= 1 && num_segments <= (1 << 24), "num_segments = %d out of range", num_segments);
+    CHECK(check_rank(r_max));
+    return LORA_OK;
+}
+
+extern "C" size_t multi_lora_fwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r_max,
+                                                int32_t num_adapters, int32_t num_segments) {
+    (void)n;
+    (void)num_adapters;
+    if (m < 0 || k <= 0 || r_max < 1 || num_segments < 0) return 0;
+    return plan_fwd(m, k, r_max, true, num_segments).bytes;
+}
+
+extern "C" size_t multi_lora_bwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r_max,
+                                                int32_t num_adapters, int32_t num_segments) {
+    (void)num_adapters;
+    if (m < 0 || k <= 0 || n <= 0 || r_max < 1 || num_segments < 0) return 0;
+    return plan_bwd(m, k, n, r_max, true, num_segments).bytes;
+}
+
+static AdapterSource multi_source(const lora_adapter *adapters, int32_t nad, const int64_t *seg_off,
+                                  const int32_t *seg_adapter, int32_t nseg, int32_t r_max) {
+    AdapterSource s{};
+    s.table = adapters;
+    s.num_adapters = nad;
+    s.r_cap = r_max;
+    s.seg_off = seg_off;
+    s.seg_adapter = seg_adapter;
+    s.num_segments = nseg;
+    s.r = r_max;
+    return s;
+}
+
+extern "C" lora_status multi_lora_linear_fwd(const void *X, const void *W, const lora_adapter *adapters,
+                                             int32_t num_adapters, const int64_t *seg_off,
+                                             const int32_t *seg_adapter, int32_t num_segments, int64_t m,
+                                             int64_t k, int64_t n, int32_t r_max, uint64_t seed,
+                                             uint64_t offset, void *Y, float *S, uint32_t *keep_bits,
+                                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    CHECK(check_shape(m, k, n));
+    CHECK(check_multi(adapters, num_adapters, seg_off, seg_adapter, num_segments, r_max));
+    REQUIRE(offset % 8 == 0, "offset = %llu must be a multiple of 8", (unsigned long long)offset);
+    REQ_PTR(W, 16);
+    if (m == 0) return LORA_OK;
+    REQ_PTR(X, 16);
+    REQ_PTR(Y, 16);
+    REQ_PTR(S, 4);
+    REQ_PTR(keep_bits, 4);
+    const FwdPlan pl = plan_fwd(m, k, r_max, true, num_segments);
+    if (workspace_bytes < pl.bytes)
+        return fail(LORA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, pl.bytes);
+    REQ_PTR(workspace, 16);
+
+    AdapterSource src = multi_source(adapters, num_adapters, seg_off, seg_adapter, num_segments, r_max);
+    src.chunks_f1 = (const ChunkEntry *)ws_at(workspace, pl.off_t_f1);
+    src.count_f1 = (const int32_t *)ws_at(workspace, pl.off_c_f1);
+    src.chunks_bwd = (const ChunkEntry *)ws_at(workspace, pl.off_t_bwd);
+    src.count_bwd = (const int32_t *)ws_at(workspace, pl.off_c_bwd);
+    HIPCHK(launch_router(seg_off, seg_adapter, num_segments, (int)m, adapters, num_adapters, r_max,
+                         (ChunkEntry *)src.chunks_f1, (int32_t *)src.count_f1, pl.chunk_cap_f1,
+                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd, stream),
+           "router launch");
+    float *sout = pl.KS > 1 ? (float *)ws_at(workspace, pl.off_spart) : S;
+    HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r_max, pl.KS,
+                     pl.ksl, stream), "F1 launch");
+    if (pl.KS > 1)
+        HIPCHK(launch_sum_partials(sout, pl.KS, (size_t)m * r_max, (size_t)m * r_max, S, "sum_s_partials",
+                                   stream), "S reduction launch");
+    HIPCHK(launch_gemm(true, 1, X, W, Y, (int)m, (int)n, (int)k, S, r_max, nullptr, 0, src, stream), "F2 launch");
+    return LORA_OK;
+}
+
+extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, const void *W,
+                                             const lora_adapter *adapters, int32_t num_adapters,
+                                             const int64_t *seg_off, const int32_t *seg_adapter,
+                                             int32_t num_segments, const float *S, const uint32_t *keep_bits,
+                                             int64_t m, int64_t k, int64_t n, int32_t r_max, void *dX,
+                                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    CHECK(check_shape(m, k, n));
+    CHECK(check_multi(adapters, num_adapters, seg_off, seg_adapter, num_segments, r_max));
+    REQ_PTR(W, 16);
+    if (m > 0) {
+        REQ_PTR(dY, 16);
+        REQ_PTR(X, 16);
+        REQ_PTR(S, 4);
+        REQ_PTR(keep_bits, 4);
+        REQ_PTR(dX, 16);
+    }
+    const BwdPlan pl = plan_bwd(m, k, n, r_max, true, num_segments);
+    if (workspace_bytes < pl.bytes)
+        return fail(LORA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, pl.bytes);
+    REQ_PTR(workspace, 16);
+
+    AdapterSource src = multi_source(adapters, num_adapters, seg_off, seg_adapter, num_segments, r_max);
+    src.chunks_f1 = (const ChunkEntry *)ws_at(workspace, pl.off_t_f1);
+    src.count_f1 = (const int32_t *)ws_at(workspace, pl.off_c_f1);
+    src.chunks_bwd = (const ChunkEntry *)ws_at(workspace, pl.off_t_bwd);
+    src.count_bwd = (const int32_t *)ws_at(workspace, pl.off_c_bwd);
+    HIPCHK(launch_router(seg_off, seg_adapter, num_segments, (int)m, adapters, num_adapters, r_max,
+                         (ChunkEntry *)src.chunks_f1, (int32_t *)src.count_f1, pl.chunk_cap_f1,
+                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd, stream),
+           "router launch");
+    float *dS = (float *)ws_at(workspace, pl.off_ds);
+    float *dSpart = pl.CT > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
+    float *dBpart = (float *)ws_at(workspace, pl.off_dbpart);
+    float *dApart = (float *)ws_at(workspace, pl.off_dapart);
+    const int chunks = pl.chunk_cap_bwd;
+    if (m > 0) {
+        HIPCHK(launch_b1(dY, S, (int)m, (int)n, r_max, src, chunks, pl.C1, dSpart, dBpart, stream), "B1 launch");
+        if (pl.CT > 1)
+            HIPCHK(launch_sum_partials(dSpart, pl.CT, (size_t)m * r_max, (size_t)m * r_max, dS, "sum_ds_partials",
+                                       stream), "dS reduction launch");
+    }
+    HIPCHK(launch_grad_reduce(0, dBpart, (int)m, (int)k, (int)n, r_max, src, chunks, stream), "dB reduction launch");
+    if (m > 0)
+        HIPCHK(launch_b2(X, keep_bits, dS, (int)m, (int)k, r_max, src, chunks, pl.C2, dApart, stream), "B2 launch");
+    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r_max, src, chunks, stream), "dA reduction launch");
+    if (m > 0)
+        HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r_max, keep_bits, (int)((k + 31) / 32),
+                           src, stream), "B3 launch");
+    return LORA_OK;
+}
+
+extern "C" lora_status multi_lora_check_segments(const int64_t *seg_off_host, const int32_t *seg_adapter_host,
+                                                 int32_t num_segments, int64_t m, const int32_t *adapter_r_host,
+                                                 int32_t num_adapters, int32_t r_max) {
+    REQUIRE(seg_off_host && seg_adapter_host && adapter_r_host, "NULL host array");
+    REQUIRE(num_segments >= 1, "num_segments = %d must be >= 1", num_segments);
+    REQUIRE(num_adapters >= 1, "num_adapters = %d must be >= 1", num_adapters);
+    REQUIRE(seg_off_host[0] == 0, "seg_off[0] = %lld must be 0", (long long)seg_off_host[0]);
+    REQUIRE(seg_off_host[num_segments] == m, "seg_off[last] = %lld must equal m = %lld",
+            (long long)seg_off_host[num_segments], (long long)m);
+    for (int32_t s = 0; s < num_segments; ++s) {
+        REQUIRE(seg_off_host[s + 1] >= seg_off_host[s], "segment %d has negative length", s);
+        REQUIRE(seg_adapter_host[s] >= 0 && seg_adapter_host[s] < num_adapters,
+                "segment %d uses adapter %d outside [0, %d)", s, seg_adapter_host[s], num_adapters);
+    }
+    for (int32_t a = 0; a < num_adapters; ++a)
+        REQUIRE(adapter_r_host[a] >= 1 && adapter_r_host[a] <= r_max, "adapter %d rank %d outside [1, r_max = %d]",
+                a, adapter_r_host[a], r_max);
+    return LORA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Pieces
+// ---------------------------------------------------------------------------
+extern "C" lora_status lora_dropout_mask(uint64_t seed, uint64_t offset, int64_t m, int64_t k, float p,
+                                         uint32_t *keep_bits, hipStream_t stream) {
+    REQUIRE(m >= 0 && m < (1LL << 31), "m out of range");
+    REQUIRE(k > 0 && k < (1LL << 31) && k % 8 == 0, "k must be a positive multiple of 8");
+    CHECK(check_p(p));
+    REQUIRE(offset % 8 == 0, "offset must be a multiple of 8");
+    REQ_PTR(keep_bits, 4);
+    HIPCHK(launch_mask(seed, offset, (int)m, (int)k, p, keep_bits, stream), "mask launch");
+    return LORA_OK;
+}
+
+extern "C" lora_status lora_frozen_fwd(const void *X, const void *W, int64_t m, int64_t k, int64_t n, void *Y,
+                                       hipStream_t stream) {
+    CHECK(check_shape(m, k, n));
+    REQ_PTR(X, 16);
+    REQ_PTR(W, 16);
+    REQ_PTR(Y, 16);
+    AdapterSource src{};
+    HIPCHK(launch_gemm(true, 0, X, W, Y, (int)m, (int)n, (int)k, nullptr, 0, nullptr, 0, src, stream),
+           "frozen fwd launch");
+    return LORA_OK;
+}
+
+extern "C" lora_status lora_frozen_bwd(const void *dY, const void *W, int64_t m, int64_t k, int64_t n, void *dX,
+                                       hipStream_t stream) {
+    CHECK(check_shape(m, k, n));
+    REQ_PTR(dY, 16);
+    REQ_PTR(W, 16);
+    REQ_PTR(dX, 16);
+    AdapterSource src{};
+    HIPCHK(launch_gemm(false, 0, dY, W, dX, (int)m, (int)k, (int)n, nullptr, 0, nullptr, 0, src, stream),
+           "frozen bwd launch");
+    return LORA_OK;
+}

@@ -1,0 +1,207 @@
+// Device-side building blocks of the gfx950 LoRA path: bf16 bit helpers,
+// MFMA wrappers, the dropout counter generator, and the parameter blocks the
+// host launcher hands to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora_fused.h"
+
+namespace lora {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (raw 16-bit patterns)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Split v into bf16 hi + lo with v ~= hi + lo to ~2^-17 relative.
+__device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo) {
+    hi = f32_to_bf16_rne(v);
+    lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
+
+// ---------------------------------------------------------------------------
+// MFMA: D = A*B + C with 8 bf16 per lane for each operand.
+// 32x32x16: operand lane l holds row/column (l % 32) and K slots 8*(l/32)..+7;
+//           result lane l, register v holds D[8*(v/4) + 4*(l/32) + v%4][l % 32].
+// 16x16x32: operand lane l holds row/column (l % 16) and K slots 8*(l/16)..+7;
+//           result lane l, register v holds D[4*(l/16) + v][l % 16].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16_t mfma32x32x16(const uint4 &a, const uint4 &b, const f32x16_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 &a, const uint4 &b, const f32x4_t &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Eight fp32 values -> hi and lo bf16 fragments.
+__device__ __forceinline__ void split_frag(const float v[8], uint4 &hi, uint4 &lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split_bf16(v[e], h[e], l[e]);
+    hi = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+    lo = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+}
+
+// 8x8 bf16 transpose held in one thread: in[e] is row e (8 elements, 16 B);
+// out[c] becomes column c (rows 0..7).  v_perm picks the 16-bit halves.
+__device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 &r0 = in[2 * q];
+            const uint4 &r1 = in[2 * q + 1];
+            uint32_t a0 = (c >> 1) == 0 ? r0.x : (c >> 1) == 1 ? r0.y : (c >> 1) == 2 ? r0.z : r0.w;
+            uint32_t a1 = (c >> 1) == 0 ? r1.x : (c >> 1) == 1 ? r1.y : (c >> 1) == 2 ? r1.z : r1.w;
+            w[q] = __builtin_amdgcn_perm(a1, a0, sel);
+        }
+        out[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dropout counter generator: Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+// SC'11).  Each round multiplies words 0 and 2 by two fixed odd constants,
+// keeps both halves of the products and mixes the high halves with words 1
+// and 3 and the round key; the key advances by two Weyl increments between
+// rounds.  Counter words 2 and 3 are always zero here.
+// ---------------------------------------------------------------------------
+struct PhiloxOut {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ PhiloxOut philox10(uint64_t block, uint64_t seed) {
+    uint32_t c0 = (uint32_t)block, c1 = (uint32_t)(block >> 32), c2 = 0u, c3 = 0u;
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+    for (int rnd = 0; rnd < 10; ++rnd) {
+        const uint32_t p0lo = c0 * 0xD2511F53u, p0hi = __umulhi(c0, 0xD2511F53u);
+        const uint32_t p1lo = c2 * 0xCD9E8D57u, p1hi = __umulhi(c2, 0xCD9E8D57u);
+        const uint32_t n0 = p1hi ^ c1 ^ k0;
+        const uint32_t n2 = p0hi ^ c3 ^ k1;
+        c0 = n0;
+        c1 = p1lo;
+        c2 = n2;
+        c3 = p0lo;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    PhiloxOut o;
+    o.w[0] = c0; o.w[1] = c1; o.w[2] = c2; o.w[3] = c3;
+    return o;
+}
+
+// Keep bits of the 8 elements with counters c8 .. c8+7 (c8 % 8 == 0): bit e
+// set iff uniform e >= T.  Uniform e is 16-bit half (e & 1) of word e >> 1.
+__device__ __forceinline__ uint32_t keep_byte(uint64_t c8, uint64_t seed, uint32_t T) {
+    const PhiloxOut o = philox10(c8 >> 3, seed);
+    uint32_t b = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        b |= ((o.w[q] & 0xFFFFu) >= T ? 1u : 0u) << (2 * q);
+        b |= ((o.w[q] >> 16) >= T ? 1u : 0u) << (2 * q + 1);
+    }
+    return b;
+}
+
+// Zero the bf16 elements of an 8-element fragment whose keep bit is clear.
+__device__ __forceinline__ uint4 apply_keep(uint4 v, uint32_t byte) {
+    uint32_t m[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        m[q] = ((byte >> (2 * q)) & 1u ? 0x0000FFFFu : 0u) | ((byte >> (2 * q + 1)) & 1u ? 0xFFFF0000u : 0u);
+    return make_uint4(v.x & m[0], v.y & m[1], v.z & m[2], v.w & m[3]);
+}
+
+// Dropout threshold and inverted-dropout scale from p (identical arithmetic on
+// every device and the host: T in double, exact for float p in [0, 1)).
+__host__ __device__ __forceinline__ uint32_t drop_threshold(float p) {
+    return (uint32_t)((double)p * 65536.0 + 0.5);
+}
+__host__ __device__ __forceinline__ float drop_scale(float p) { return 1.0f / (1.0f - p); }
+
+// ---------------------------------------------------------------------------
+// Work items of the low-rank kernels: a run of rows inside one segment.
+// ---------------------------------------------------------------------------
+struct ChunkEntry {
+    int32_t row_lo;
+    int32_t row_hi;
+    int32_t adapter;
+    int32_t pad;
+};
+
+struct AdapterView {
+    const uint16_t *A;  // k x r
+    const uint16_t *B;  // r x n
+    uint16_t *dA;
+    uint16_t *dB;
+    int32_t r;
+    float alpha;
+    float p;
+};
+
+__device__ __forceinline__ AdapterView load_adapter(const lora_adapter *tab, int a) {
+    const lora_adapter e = tab[a];
+    AdapterView v;
+    v.A = (const uint16_t *)e.A;
+    v.B = (const uint16_t *)e.B;
+    v.dA = (uint16_t *)e.dA;
+    v.dB = (uint16_t *)e.dB;
+    v.r = e.r;
+    v.alpha = e.alpha;
+    v.p = e.p;
+    return v;
+}
+
+// Where a kernel finds its rows and adapter: either one adapter over all rows
+// (chunk c = rows [c*rows_per_chunk, ...)), or a device chunk table built by
+// the router from the segment table.
+struct RowWork {
+    const ChunkEntry *chunks;  // NULL: single adapter
+    const int32_t *chunk_count;
+    const lora_adapter *adapters;
+    int32_t num_adapters;
+    int32_t rows_per_chunk;
+    int32_t r_cap;             // ranks above this are treated as invalid (r_max)
+    AdapterView single;
+};
+
+// Returns false if this chunk index has no work.
+__device__ __forceinline__ bool resolve_chunk(const RowWork &w, int chunk, int m, int &row_lo,
+                                              int &row_hi, AdapterView &ad) {
+    if (w.chunks == nullptr) {
+        row_lo = chunk * w.rows_per_chunk;
+        if (row_lo >= m) return false;
+        row_hi = min(m, row_lo + w.rows_per_chunk);
+        ad = w.single;
+        return true;
+    }
+    if (chunk >= w.chunk_count[0]) return false;
+    const ChunkEntry e = w.chunks[chunk];
+    row_lo = e.row_lo;
+    row_hi = e.row_hi;
+    ad = load_adapter(w.adapters, e.adapter);
+    if (ad.r < 1 || ad.r > w.r_cap) return false;
+    return row_hi > row_lo;
+}
+
+}  // namespace lora

@@ -1,0 +1,174 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is ever launched).
+
+* the library loads and exports every function include/lora_fused.h declares;
+* every invalid argument is rejected on the host with the documented status
+  (the pointers used are fake but aligned; every call here fails validation
+  before anything could be enqueued);
+* the host-side segment-table checker;
+* workspace-size queries are monotone and zero-free where work exists.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lora_fine_tuning_amd as lf
+from lora_fine_tuning_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_fused.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    if torch.cuda.is_available():
+        # fake pointers must never reach a real device, even by a test mistake
+        pytest.skip("host-only checks; a GPU is visible")
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keep = [n for n in names if n.startswith(("lora_", "multi_lora_"))]
+    return sorted(set(keep))
+
+
+def test_header_and_binding_agree():
+    assert sorted(_lib.EXPORTS) == header_functions()
+
+
+def test_library_exports_every_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in header_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def _fwd(lib, **kw):
+    a = dict(X=FAKE, W=FAKE, A=FAKE, B=FAKE, m=64, k=64, n=64, r=8, alpha=1.0, p=0.1, seed=0,
+             offset=0, Y=FAKE, S=FAKE, keep=FAKE, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.lora_linear_fwd(a["X"], a["W"], a["A"], a["B"], a["m"], a["k"], a["n"], a["r"],
+                               a["alpha"], a["p"], a["seed"], a["offset"], a["Y"], a["S"],
+                               a["keep"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), INVALID),
+    (dict(W=FAKE + 8), INVALID),          # W must be 16-byte aligned
+    (dict(k=60), INVALID),                # k % 8
+    (dict(n=12), INVALID),                # n % 8
+    (dict(m=-1), INVALID),
+    (dict(r=0), INVALID),
+    (dict(r=257), INVALID),
+    (dict(p=1.0), INVALID),
+    (dict(p=-0.1), INVALID),
+    (dict(offset=4), INVALID),            # offset % 8
+    (dict(keep=None), INVALID),           # keep_bits required when p > 0
+    (dict(S=FAKE + 2), INVALID),          # S 4-byte aligned
+    (dict(m=512, k=4096, wsb=0), WORKSPACE),  # needs split-k partials
+])
+def test_fwd_rejects(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.lora_last_error_message()
+
+
+def test_fwd_m0_is_noop(lib):
+    # m == 0 returns before any launch (workspace may be absent)
+    assert _fwd(lib, m=0, ws=None, wsb=0) == OK
+
+
+def _bwd(lib, **kw):
+    a = dict(dY=FAKE, X=FAKE, W=FAKE, A=FAKE, B=FAKE, S=FAKE, keep=FAKE, m=64, k=64, n=64, r=8,
+             alpha=1.0, p=0.1, dX=FAKE, dA=FAKE, dB=FAKE, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.lora_linear_bwd(a["dY"], a["X"], a["W"], a["A"], a["B"], a["S"], a["keep"], a["m"],
+                               a["k"], a["n"], a["r"], a["alpha"], a["p"], a["dX"], a["dA"],
+                               a["dB"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dY=None), INVALID),
+    (dict(dX=FAKE + 4), INVALID),
+    (dict(k=20), INVALID),
+    (dict(r=300), INVALID),
+    (dict(p=1.5), INVALID),
+    (dict(keep=None), INVALID),
+    (dict(dA=None), INVALID),
+    (dict(wsb=0), WORKSPACE),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_multi_rejects(lib):
+    f = lib.multi_lora_linear_fwd
+    # num_adapters 0
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1, 64, 64, 64, 16, 0, 0, FAKE, FAKE, FAKE, FAKE, 0,
+             None) == INVALID
+    # no segments
+    assert f(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 0, 64, 64, 64, 16, 0, 0, FAKE, FAKE, FAKE, FAKE, 0,
+             None) == INVALID
+    # keep_bits required
+    assert f(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1, 64, 64, 64, 16, 0, 0, FAKE, FAKE, None, FAKE, 0,
+             None) == INVALID
+    # workspace too small
+    assert f(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1, 64, 64, 64, 16, 0, 0, FAKE, FAKE, FAKE, FAKE, 0,
+             None) == WORKSPACE
+    b = lib.multi_lora_linear_bwd
+    assert b(FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1, FAKE, FAKE, 64, 64, 64, 0, FAKE, FAKE, 0,
+             None) == INVALID  # r_max 0
+    assert b(FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1, FAKE, FAKE, 64, 64, 64, 16, FAKE, FAKE, 0,
+             None) == WORKSPACE
+
+
+def test_mask_and_frozen_reject(lib):
+    assert lib.lora_dropout_mask(0, 3, 4, 64, 0.1, FAKE, None) == INVALID   # offset % 8
+    assert lib.lora_dropout_mask(0, 0, 4, 63, 0.1, FAKE, None) == INVALID   # k % 8
+    assert lib.lora_dropout_mask(0, 0, 4, 64, 0.1, None, None) == INVALID
+    assert lib.lora_frozen_fwd(FAKE, FAKE, 8, 12, 8, FAKE, None) == INVALID
+    assert lib.lora_frozen_bwd(FAKE, FAKE + 8, 8, 16, 8, FAKE, None) == INVALID
+
+
+def test_check_segments():
+    lf.multi_lora_check_segments([0, 5, 5, 12], [1, 0, 1], 12, [4, 8], 8)
+    bad = [
+        ([1, 5, 12], [0, 1], 12, [4, 8], 8),     # does not start at 0
+        ([0, 5, 11], [0, 1], 12, [4, 8], 8),     # does not end at m
+        ([0, 7, 5, 12], [0, 1, 0], 12, [4, 8], 8),  # decreasing
+        ([0, 5, 12], [0, 2], 12, [4, 8], 8),     # adapter out of range
+        ([0, 5, 12], [0, 1], 12, [4, 9], 8),     # rank above r_max
+    ]
+    for args in bad:
+        with pytest.raises(lf.LoraError) as e:
+            lf.multi_lora_check_segments(*args)
+        assert e.value.status == INVALID
+
+
+def test_status_strings(lib):
+    assert lib.lora_status_string(0) == b"LORA_OK"
+    assert lib.lora_status_string(-3) == b"LORA_ERR_WORKSPACE"
+
+
+def test_workspace_sizes():
+    s1 = lf.lora_linear_bwd_workspace_size(8192, 4096, 4096, 16)
+    s2 = lf.lora_linear_bwd_workspace_size(16384, 4096, 4096, 16)
+    assert 0 < s1 < s2
+    assert lf.lora_linear_fwd_workspace_size(512, 1024, 1024, 16) > 0
+    assert lf.multi_lora_bwd_workspace_size(8192, 28672, 8192, 128, 8, 8) > \
+        lf.lora_linear_bwd_workspace_size(8192, 28672, 8192, 128)
+
+
+def test_adapter_record_layout():
+    assert ctypes.sizeof(_lib.LoraAdapter) == 48
+    assert _lib.LoraAdapter.r.offset == 32 and _lib.LoraAdapter.p.offset == 40
