@@ -30,7 +30,7 @@
 
 namespace lora {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
+constexpr int GBM = 256, GBN = 256;
 
 struct GemmParams {
     const uint16_t *Arow;  // M x K
@@ -64,10 +64,6 @@ __device__ __forceinline__ void tile_coords(int wg, int G, int tiles_m, int tile
     const int in = lid - group * width;
     tm = first + in % gsz;
     tn = in / gsz;
-}
-
-__device__ __forceinline__ uint4 ld16_or_zero(const uint16_t *p, bool ok) {
-    return ok ? *(const uint4 *)p : make_uint4(0, 0, 0, 0);
 }
 
 // One item of the LoRA epilogue: rows [lo, hi) with one adapter.
@@ -144,16 +140,77 @@ __device__ __forceinline__ int first_segment(const GemmParams &P, int m0) {
     return lo;
 }
 
+// Buffer resource over `bytes` bytes from `base`; loads past the end return 0
+// and stores past the end are dropped, so edge tiles need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+    const uint32_t nrec = (uint32_t)(bytes < 0x7FFFFFF0ull ? bytes : 0x7FFFFFF0ull);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nrec, 0x00020000);
+}
+constexpr uint32_t kOOB = 0x80000000u;  // an offset beyond every resource
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+constexpr int BK = 64;              // K depth of one LDS stage
+constexpr int NST = 2;              // stages in the LDS ring
+constexpr int ROWB = BK * 2;        // bytes per LDS row of a K-contiguous tile
+constexpr int CPR = BK / 8;         // 16-byte chunks per such row
+constexpr int TILE_BYTES = GBM * ROWB;  // one operand tile (the NN W tile is BK x 512 B, same size)
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+constexpr int LPW = BK / 8;         // 1-KiB direct-to-LDS loads per wave per operand per stage
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// XOR swizzle of 16-byte chunks: conflict-free 16-lane b128 reads of 16
+// consecutive rows (K-contiguous tiles) and 32-lane transposing b64 reads of
+// 4 consecutive k-rows (the NN W tile, 32 chunks per row).
+__device__ __forceinline__ int swz_rows(int r) {
+    return CPR == 8 ? (((r >> 1) & 7) ^ ((r & 1) << 2)) : ((r >> 2) & 3);
+}
+__device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
+
+// s_waitcnt with only the vector-memory counter constrained (vmcnt in bits
+// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Raw buffer descriptor words (base, stride 0, num_records, gfx9 dword3).
+typedef int sgpr4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ sgpr4_t make_desc(const void *base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    return sgpr4_t{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+// 16-byte direct-to-LDS load: lane l's 16 bytes from desc+voff land at LDS
+// byte lds_base + 16*l.  Issued as inline asm so the compiler's wait-count
+// insertion does not serialise later LDS reads behind it; completion is
+// tracked by the explicit vmcnt waits of the K loop.
+// M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(sgpr4_t desc, uint32_t voff, uint32_t lds_base) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voff), "s"(desc), "s"(lds_base)
+        : "memory");
+}
+
 template <bool NN, int EPI, bool MULTI>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     extern __shared__ uint4 gemm_smem[];
-    uint16_t *As = (uint16_t *)gemm_smem;  // [2][GBM][GLD]
-    uint16_t *Bs = As + 2 * GBM * GLD;     // [2][GBN][GLD]
+    char *smem = (char *)gemm_smem;
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char *)smem;
 
     int tmi, tni;
     tile_coords(blockIdx.x, gridDim.x, P.tiles_m, P.tiles_n, tmi, tni);
     const int m0 = tmi * GBM, n0 = tni * GBN;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, lhi = lane >> 5;
 
@@ -165,74 +222,173 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-    // global -> register staging
-    uint4 ra[8], rb[8];
-    const int a_row = tid >> 3, a_col = (tid & 7) * 8;     // row-side / nt col-side
-    const int nn_kb = tid & 7, nn_nb = tid >> 3;            // nn col-side 8x8 block
+    const size_t K2 = (size_t)P.K * 2, N2 = (size_t)P.N * 2;
+    auto clamp_bytes = [](uint64_t v) { return (uint32_t)(v < 0x7FFFFFF0ull ? v : 0x7FFFFFF0ull); };
+    const sgpr4_t dA = make_desc(P.Arow + (size_t)m0 * P.K, clamp_bytes((uint64_t)(P.M - m0) * K2));
+    const sgpr4_t dBt = make_desc(P.Bcol + (size_t)n0 * P.K, NN ? 0u : clamp_bytes((uint64_t)(P.N - n0) * K2));
+    const uint32_t nn_maxrows = 0x7FFFFFF0u / (uint32_t)N2;
 
-    auto load_tiles = [&](int k0) {
+    // ---- per-lane load geometry (constant over the K loop)
+    // K-contiguous tiles: instruction j of this wave fills rows (wave*LPW+j)*RPI ..
+    constexpr int RPI = 1024 / ROWB;  // rows per 1-KiB instruction
+    uint32_t offK[LPW];   // byte offset of this lane's 16 B inside the global row panel (k0 = 0)
+    int colK[LPW];        // its first column (for the K tail test)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int row = m0 + c * 32 + a_row, col = k0 + a_col;
-            ra[c] = ld16_or_zero(P.Arow + (size_t)row * P.K + col, row < P.M && col < P.K);
-        }
-        if (NN) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int krow = k0 + nn_kb * 8 + e, col = n0 + nn_nb * 8;
-                rb[e] = ld16_or_zero(P.Bcol + (size_t)krow * P.N + col, krow < P.K && col < P.N);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int nrow = n0 + c * 32 + a_row, col = k0 + a_col;
-                rb[c] = ld16_or_zero(P.Bcol + (size_t)nrow * P.K + col, nrow < P.N && col < P.K);
-            }
-        }
-    };
-    auto store_tiles = [&](int buf) {
-        uint16_t *as = As + buf * GBM * GLD;
-        uint16_t *bs = Bs + buf * GBN * GLD;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *(uint4 *)&as[(c * 32 + a_row) * GLD + a_col] = ra[c];
-        if (NN) {
-            uint4 o[8];
-            transpose8x8(rb, o);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) *(uint4 *)&bs[(nn_nb * 8 + c) * GLD + nn_kb * 8] = o[c];
-        } else {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) *(uint4 *)&bs[(c * 32 + a_row) * GLD + a_col] = rb[c];
-        }
-    };
-
-    const int nk = (P.K + GBK - 1) / GBK;
-    if (nk > 0) {
-        load_tiles(0);
-        store_tiles(0);
-        __syncthreads();
+    for (int j = 0; j < LPW; ++j) {
+        const int r = (wave * LPW + j) * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swz_rows(r);
+        offK[j] = (uint32_t)(r * K2 + c * 16);
+        colK[j] = c * 8;
     }
+    // NN W tile: instruction j fills k-rows (wave*LPW+j)*2 .. +1, 32 chunks each
+    uint32_t offW[LPW];
+    if (NN) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int kr = (wave * LPW + j) * 2 + lane / 32;
+            const int c = (lane % 32) ^ swz_w(kr);
+            offW[j] = (uint32_t)(kr * N2 + (size_t)(n0 + c * 8) * 2);
+        }
+    }
+
+    auto issue_loads = [&](int k0, int stage) {
+        const uint32_t sa = smem_lds + stage * STAGE_BYTES + wave * LPW * 1024;
+        const uint32_t sb = sa + TILE_BYTES;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const uint32_t off = (k0 + colK[j] < P.K) ? offK[j] + (uint32_t)(k0 * 2) : kOOB;
+            dma16(dA, off, sa + j * 1024);
+        }
+        if (NN) {
+            const int kk = min(k0, P.K);
+            const uint32_t rows = (uint32_t)min(P.K - kk, (int)nn_maxrows);
+            const sgpr4_t dB = make_desc(P.Bcol + (size_t)kk * P.N, rows * (uint32_t)N2);
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) dma16(dB, offW[j], sb + j * 1024);
+        } else {
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) {
+                const uint32_t off = (k0 + colK[j] < P.K) ? offK[j] + (uint32_t)(k0 * 2) : kOOB;
+                dma16(dBt, off, sb + j * 1024);
+            }
+        }
+    };
+
+    // ---- fragment reads
+    int rowA[4], swA[4], rowB[4], swB[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        rowA[t] = wm * 128 + t * 32 + l32;
+        swA[t] = swz_rows(rowA[t]);
+        rowB[t] = wn * 128 + t * 32 + l32;
+        swB[t] = swz_rows(rowB[t]);
+    }
+    // NN transposing reads: lane = 16*G + a; source row k = 8*(G>>1) + (a>>2) (+4),
+    // chunk (col base)/8 + ((a&3)>>1), byte (a&1)*8 inside the chunk
+    const int trG = lane >> 4, tra = lane & 15;
+    const int tr_k = 8 * (trG >> 1) + (tra >> 2);
+    const int tr_c = (wn * 128 + (trG & 1) * 16) / 8 + ((tra & 3) >> 1);
+    const int tr_b = (tra & 1) * 8;
+
+    uint4 af[2][4], bf[2][4];
+    // One fragment (t-th of the row side if which == 0, of the column side if
+    // which == 1) of sub-step ks from LDS stage `stage` into register slot `slot`.
+    auto read_frag = [&](int stage, int ks, int slot, int which, int t) {
+        const char *sa = smem + stage * STAGE_BYTES;
+        const char *sb = sa + TILE_BYTES;
+        const int c = 2 * ks + lhi;
+        if (which == 0) {
+            af[slot][t] = *(const uint4 *)(sa + rowA[t] * ROWB + ((c ^ swA[t]) << 4));
+        } else if (NN) {
+            const int k = ks * 16 + tr_k;
+            const int ch = tr_c + 4 * t;
+            const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t *)((lds_char *)sb + k * 512 + ((ch ^ swz_w(k)) << 4) + tr_b));
+            const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t *)((lds_char *)sb + (k + 4) * 512 + ((ch ^ swz_w(k + 4)) << 4) + tr_b));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            bf[slot][t] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+        } else {
+            bf[slot][t] = *(const uint4 *)(sb + rowB[t] * ROWB + ((c ^ swB[t]) << 4));
+        }
+    };
+    auto read_frags = [&](int stage, int ks, int slot) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            read_frag(stage, ks, slot, 0, t);
+            read_frag(stage, ks, slot, 1, t);
+        }
+    };
+
+    // DMA of one operand tile slice: load j (0..2*LPW-1) of tile k0 into `stage`
+    auto dma_one = [&](int k0, int stage, int j) {
+        const uint32_t sa = smem_lds + stage * STAGE_BYTES + wave * LPW * 1024;
+        if (j < LPW) {
+            const uint32_t off = (k0 + colK[j] < P.K) ? offK[j] + (uint32_t)(k0 * 2) : kOOB;
+            dma16(dA, off, sa + j * 1024);
+        } else {
+            const int jj = j - LPW;
+            const uint32_t sb = sa + TILE_BYTES;
+            if (NN) {
+                const int kk = min(k0, P.K);
+                const uint32_t rows = (uint32_t)min(P.K - kk, (int)nn_maxrows);
+                const sgpr4_t dB = make_desc(P.Bcol + (size_t)kk * P.N, rows * (uint32_t)N2);
+                dma16(dB, offW[jj], sb + jj * 1024);
+            } else {
+                const uint32_t off = (k0 + colK[jj] < P.K) ? offK[jj] + (uint32_t)(k0 * 2) : kOOB;
+                dma16(dBt, off, sb + jj * 1024);
+            }
+        }
+    };
+
+    constexpr int KS = BK / 16;
+    constexpr int NDMA = 2 * LPW;                 // DMA instructions per wave per tile
+    constexpr int INFLIGHT = (NST - 2) * NDMA;    // loads allowed outstanding at a stage switch
+    // 16 MFMAs of slot `sl`; MFMA i is followed by the i-th item of the side
+    // work: fragment reads of (rstage, rks) into slot `rsl` for i < 8 and DMA
+    // loads d0 + i/2 (every other MFMA) while they last.
+    auto mfma_group = [&](int sl, bool do_read, int rstage, int rks, int rsl, int dk0, int dstage, int d0, int dn) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int tm = i >> 2, tn = i & 3;
+            acc[tm][tn] = mfma32x32x16(bf[sl][tn], af[sl][tm], acc[tm][tn]);
+            if (do_read && i < 8) read_frag(rstage, rks, rsl, i >> 2, i & 3);
+            if ((i & 1) == 0 && (i >> 1) < dn) dma_one(dk0, dstage, d0 + (i >> 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int nk = (P.K + BK - 1) / BK;
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) dma_one(st * BK, st, j);
+    wait_vmcnt<INFLIGHT>();
+    __syncthreads();
+    read_frags(0, 0, 0);
+    int stage = 0, lstage = NST - 1;
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load_tiles((kt + 1) * GBK);
-        const uint16_t *as = As + cur * GBM * GLD;
-        const uint16_t *bs = Bs + cur * GBN * GLD;
+        const int kload = (kt + NST - 1) * BK;
+        // sub-steps 0..KS-2: MFMAs of ks with reads of ks+1; the tile's DMA
+        // loads are spread over the first sub-steps (8 per sub-step)
 #pragma unroll
-        for (int ks = 0; ks < GBK / 16; ++ks) {
-            uint4 af[4], bf[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                af[t] = *(const uint4 *)&as[(wm * 128 + t * 32 + l32) * GLD + ks * 16 + lhi * 8];
-                bf[t] = *(const uint4 *)&bs[(wn * 128 + t * 32 + l32) * GLD + ks * 16 + lhi * 8];
-            }
-#pragma unroll
-            for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-                for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32x32x16(bf[tn], af[tm], acc[tm][tn]);
+        for (int ks = 0; ks < KS - 1; ++ks) {
+            const int d0 = ks * 8;
+            const int dn = d0 < NDMA ? min(8, NDMA - d0) : 0;
+            mfma_group(ks & 1, true, stage, ks + 1, (ks + 1) & 1, kload, lstage, d0, dn);
         }
-        if (kt + 1 < nk) store_tiles(cur ^ 1);
+        if ((KS - 1) * 8 < NDMA) {
+#pragma unroll
+            for (int j = (KS - 1) * 8; j < NDMA; ++j) dma_one(kload, lstage, j);
+        }
+        wait_vmcnt<INFLIGHT>();
         __syncthreads();
+        stage = stage + 1 == NST ? 0 : stage + 1;
+        lstage = lstage + 1 == NST ? 0 : lstage + 1;
+        // last sub-step after the barrier, overlapping the next tile's first reads
+        mfma_group((KS - 1) & 1, kt + 1 < nk, stage, 0, 0, 0, 0, 0, 0);
     }
+    wait_vmcnt<0>();
 
     const int wrow0 = m0 + wm * 128;  // first row of this wave
     const int wcol0 = n0 + wn * 128;  // first column of this wave
@@ -268,6 +424,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     }
 
     // ---- output (B3 adds the masked rank-deep term one 32-row band at a time)
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(P.C + (size_t)m0 * P.N, (size_t)(P.M - m0) * N2);
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
         const int row = wrow0 + tm * 32 + l32;
@@ -321,14 +478,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                         }
                         h[e] = f32_to_bf16_rne(v);
                     }
-                    *(uint2 *)(P.C + (size_t)row * P.N + col) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                           make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]))),
+                        rC, (uint32_t)((size_t)(row - m0) * N2 + (size_t)col * 2), 0, 0);
                 }
             }
         }
     }
 }
 
-size_t gemm_lds_bytes() { return (size_t)2 * (GBM + GBN) * GLD * sizeof(uint16_t); }
+size_t gemm_lds_bytes() { return (size_t)NST * STAGE_BYTES; }
 
 template <bool NN, int EPI, bool MULTI>
 static hipError_t launch_gemm_t(const GemmParams &P, hipStream_t stream, const char *name) {
