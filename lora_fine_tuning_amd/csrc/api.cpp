@@ -230,6 +230,7 @@ struct BwdPlan {
     int chunk_cap_bwd;
     int chunk_cap_f1;
     int C1, C2, CT;
+    int ds_parts;  // dS partials written by B1 (two per column tile for ranks <= 32)
     size_t off_ds, off_dspart, off_dbpart, off_dapart, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
     size_t bytes;
 };
@@ -243,9 +244,10 @@ BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_
     p.C1 = rl <= 128 ? 256 : 128;
     p.C2 = rl <= 128 ? 256 : 128;
     p.CT = cdiv(n, p.C1);
+    p.ds_parts = rl <= 32 ? 2 * p.CT : p.CT;
     Carve c;
     p.off_ds = c.take((size_t)m * RS * sizeof(float));
-    p.off_dspart = c.take(p.CT > 1 ? (size_t)p.CT * m * RS * sizeof(float) : 0);
+    p.off_dspart = c.take(p.ds_parts > 1 ? (size_t)p.ds_parts * m * RS * sizeof(float) : 0);
     p.off_dbpart = c.take((size_t)p.chunk_cap_bwd * RS * n * sizeof(float));
     p.off_dapart = c.take((size_t)p.chunk_cap_bwd * k * RS * sizeof(float));
     if (multi) {
@@ -357,14 +359,14 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
 
     AdapterSource src = single_source(A, B, dA, dB, r, alpha, p);
     float *dS = (float *)ws_at(workspace, pl.off_ds);
-    float *dSpart = pl.CT > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
+    float *dSpart = pl.ds_parts > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
     float *dBpart = (float *)ws_at(workspace, pl.off_dbpart);
     float *dApart = (float *)ws_at(workspace, pl.off_dapart);
     const int chunks = pl.chunk_cap_bwd;
     if (m > 0) {
         HIPCHK(launch_b1(dY, S, (int)m, (int)n, r, src, chunks, pl.C1, dSpart, dBpart, stream), "B1 launch");
-        if (pl.CT > 1)
-            HIPCHK(launch_sum_partials(dSpart, pl.CT, (size_t)m * r, (size_t)m * r, dS, "sum_ds_partials", stream),
+        if (pl.ds_parts > 1)
+            HIPCHK(launch_sum_partials(dSpart, pl.ds_parts, (size_t)m * r, (size_t)m * r, dS, "sum_ds_partials", stream),
                    "dS reduction launch");
     }
     HIPCHK(launch_grad_reduce(0, dBpart, (int)m, (int)k, (int)n, r, src, chunks, stream), "dB reduction launch");
@@ -490,14 +492,14 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
                          (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd, stream),
            "router launch");
     float *dS = (float *)ws_at(workspace, pl.off_ds);
-    float *dSpart = pl.CT > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
+    float *dSpart = pl.ds_parts > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
     float *dBpart = (float *)ws_at(workspace, pl.off_dbpart);
     float *dApart = (float *)ws_at(workspace, pl.off_dapart);
     const int chunks = pl.chunk_cap_bwd;
     if (m > 0) {
         HIPCHK(launch_b1(dY, S, (int)m, (int)n, r_max, src, chunks, pl.C1, dSpart, dBpart, stream), "B1 launch");
-        if (pl.CT > 1)
-            HIPCHK(launch_sum_partials(dSpart, pl.CT, (size_t)m * r_max, (size_t)m * r_max, dS, "sum_ds_partials",
+        if (pl.ds_parts > 1)
+            HIPCHK(launch_sum_partials(dSpart, pl.ds_parts, (size_t)m * r_max, (size_t)m * r_max, dS, "sum_ds_partials",
                                        stream), "dS reduction launch");
     }
     HIPCHK(launch_grad_reduce(0, dBpart, (int)m, (int)k, (int)n, r_max, src, chunks, stream), "dB reduction launch");

@@ -94,14 +94,15 @@ __device__ __forceinline__ PhiloxOut philox10(uint64_t block, uint64_t seed) {
     uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
 #pragma unroll
     for (int rnd = 0; rnd < 10; ++rnd) {
-        const uint32_t p0lo = c0 * 0xD2511F53u, p0hi = __umulhi(c0, 0xD2511F53u);
-        const uint32_t p1lo = c2 * 0xCD9E8D57u, p1hi = __umulhi(c2, 0xCD9E8D57u);
-        const uint32_t n0 = p1hi ^ c1 ^ k0;
-        const uint32_t n2 = p0hi ^ c3 ^ k1;
+        // one 32x32->64 multiply gives both halves of each product
+        const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
         c0 = n0;
-        c1 = p1lo;
+        c1 = (uint32_t)p1;
         c2 = n2;
-        c3 = p0lo;
+        c3 = (uint32_t)p0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
@@ -138,6 +139,51 @@ __host__ __device__ __forceinline__ uint32_t drop_threshold(float p) {
     return (uint32_t)((double)p * 65536.0 + 0.5);
 }
 __host__ __device__ __forceinline__ float drop_scale(float p) { return 1.0f / (1.0f - p); }
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS loads and LDS transposing reads (gfx950)
+// ---------------------------------------------------------------------------
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// s_waitcnt with only the vector-memory counter constrained (vmcnt in bits
+// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Raw buffer descriptor words (base, stride 0, num_records, gfx9 dword3).
+typedef int sgpr4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ sgpr4_t make_desc(const void *base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    return sgpr4_t{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+// 16-byte direct-to-LDS load: lane l's 16 bytes from desc+voff land at LDS
+// byte lds_base + 16*l.  Issued as inline asm so the compiler's wait-count
+// insertion does not serialise later LDS reads behind it; completion is
+// tracked by the explicit vmcnt waits of the K loop.
+// M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(sgpr4_t desc, uint32_t voff, uint32_t lds_base) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voff), "s"(desc), "s"(lds_base)
+        : "memory");
+}
+
+// Transposing LDS read of 4 bf16 (8 bytes): within each 16-lane group, lane
+// l receives element (l % 4) of the 8-byte rows addressed by lanes
+// 4*i + l/4, i = 0..3 -- i.e. given 4 rows x 16 columns addressed as 4-column
+// pieces, every lane gets one column's 4 consecutive rows.
+__device__ __forceinline__ uint2 lds_read_tr4(const lds_char *p) {
+    const v4s_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t *)p);
+    return __builtin_bit_cast(uint2, v);
+}
 
 // ---------------------------------------------------------------------------
 // Work items of the low-rank kernels: a run of rows inside one segment.

@@ -159,9 +159,6 @@ constexpr int CPR = BK / 8;         // 16-byte chunks per such row
 constexpr int TILE_BYTES = GBM * ROWB;  // one operand tile (the NN W tile is BK x 512 B, same size)
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr int LPW = BK / 8;         // 1-KiB direct-to-LDS loads per wave per operand per stage
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
 // XOR swizzle of 16-byte chunks: conflict-free 16-lane b128 reads of 16
 // consecutive rows (K-contiguous tiles) and 32-lane transposing b64 reads of
 // 4 consecutive k-rows (the NN W tile, 32 chunks per row).
@@ -169,36 +166,6 @@ __device__ __forceinline__ int swz_rows(int r) {
     return CPR == 8 ? (((r >> 1) & 7) ^ ((r & 1) << 2)) : ((r >> 2) & 3);
 }
 __device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
-
-// s_waitcnt with only the vector-memory counter constrained (vmcnt in bits
-// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Raw buffer descriptor words (base, stride 0, num_records, gfx9 dword3).
-typedef int sgpr4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ sgpr4_t make_desc(const void *base, uint32_t bytes) {
-    const uint64_t b = (uint64_t)base;
-    return sgpr4_t{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
-}
-// 16-byte direct-to-LDS load: lane l's 16 bytes from desc+voff land at LDS
-// byte lds_base + 16*l.  Issued as inline asm so the compiler's wait-count
-// insertion does not serialise later LDS reads behind it; completion is
-// tracked by the explicit vmcnt waits of the K loop.
-// M0 is saved and restored around the load.
-__device__ __forceinline__ void dma16(sgpr4_t desc, uint32_t voff, uint32_t lds_base) {
-    uint32_t saved_m0;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved_m0)
-        : "v"(voff), "s"(desc), "s"(lds_base)
-        : "memory");
-}
 
 template <bool NN, int EPI, bool MULTI>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {

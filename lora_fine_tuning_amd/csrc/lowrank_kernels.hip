@@ -129,14 +129,22 @@ struct F1Params {
     int ksl;
     int KW;
     int r_lds;  // rows of the staged At buffer (>= every rank, multiple of 16)
+    int slab;   // columns of A staged at once (multiple of kF1KSub)
 };
 
-constexpr int kF1Ld = kF1KSub + 8;  // LDS row stride of At (elements)
-
+// F1: dropout mask + down-projection (juhe.plus blog, section 4.1, forward
+// item 1: dropout and X -> S in one kernel so X is read once).
+// Work-group = 4 waves x 16 rows of one chunk, over one k-slice.  Lane l of a
+// wave owns row (l % 16) and the 8 columns 8*(l/16).. of each 32-wide K step:
+// exactly one Philox block and one MFMA A-fragment.  A is staged transposed
+// in LDS (At[rr][kk]) one slab of columns at a time, and the X loads of the
+// next 128-column sub-slice are in flight while the current one is hashed,
+// masked and multiplied.
 template <int MAXT>
 __global__ __launch_bounds__(256) void f1_kernel(F1Params P) {
     extern __shared__ uint4 f1_smem[];
     uint16_t *At = (uint16_t *)f1_smem;
+    const int lda = P.slab + 8;  // LDS row stride of At (elements)
 
     int row_lo, row_hi;
     AdapterView ad;
@@ -155,47 +163,80 @@ __global__ __launch_bounds__(256) void f1_kernel(F1Params P) {
     const bool rvalid = row < row_hi;
     const uint16_t *xrow = P.X + (size_t)(rvalid ? row : row_lo) * P.k;
     const uint64_t ctr_row = P.offset + (uint64_t)(rvalid ? row : row_lo) * (uint64_t)P.k;
+    const bool vecA = (r & 7) == 0 && (((uintptr_t)ad.A) & 15) == 0;
 
     f32x4_t acc[MAXT];
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = kb; k0 < ke; k0 += kF1KSub) {
-        __syncthreads();
-        for (int idx = tid; idx < kF1KSub * rpad; idx += 256) {
-            const int kk = idx / rpad, rr = idx - kk * rpad;
-            uint16_t v = 0;
-            if (rr < r && k0 + kk < ke) v = ad.A[(size_t)(k0 + kk) * r + rr];
-            At[rr * kF1Ld + kk] = v;
-        }
-        __syncthreads();
-
-        uint4 xv[4];
+    auto load_x = [&](int k0, uint4 (&xv)[4]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int c0 = k0 + 32 * t + 8 * g;
             xv[t] = (rvalid && c0 < ke) ? *(const uint4 *)(xrow + c0) : make_uint4(0, 0, 0, 0);
         }
+    };
+
+    for (int s0 = kb; s0 < ke; s0 += P.slab) {
+        const int s1 = min(ke, s0 + P.slab);
+        const int cols = s1 - s0;
+        __syncthreads();
+        if (vecA) {
+            const int vpr = r >> 3;  // 16-byte vectors per A row
+            for (int idx = tid; idx < cols * vpr; idx += 256) {
+                const int kk = idx / vpr, v = idx - kk * vpr;
+                const uint4 a = *(const uint4 *)(ad.A + (size_t)(s0 + kk) * r + 8 * v);
+                const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int c0 = k0 + 32 * t + 8 * g;
-            uint32_t byte = 0;
-            if (rvalid && c0 < ke) byte = (T == 0) ? 0xFFu : keep_byte(ctr_row + (uint64_t)c0, P.seed, T);
-            xv[t] = apply_keep(xv[t], byte);
-            if (P.keep_bits != nullptr) {
-                uint32_t w = byte << (8 * g);
-                w |= (uint32_t)__shfl_xor((int)w, 16);
-                w |= (uint32_t)__shfl_xor((int)w, 32);
-                if (g == 0 && rvalid && k0 + 32 * t < ke)
-                    P.keep_bits[(size_t)row * P.KW + ((k0 + 32 * t) >> 5)] = w;
+                for (int e = 0; e < 8; ++e)
+                    At[(8 * v + e) * lda + kk] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
             }
+            for (int idx = tid; idx < (rpad - r) * cols; idx += 256) {
+                const int rr = r + idx / cols, kk = idx % cols;
+                At[rr * lda + kk] = 0;
+            }
+        } else {
+            for (int idx = tid; idx < cols * rpad; idx += 256) {
+                const int kk = idx / rpad, rr = idx - kk * rpad;
+                uint16_t v = 0;
+                if (rr < r) v = ad.A[(size_t)(s0 + kk) * r + rr];
+                At[rr * lda + kk] = v;
+            }
+        }
+        // zero the tail of a ragged slab so every 128-column step reads defined values
+        for (int idx = tid; idx < rpad * (P.slab - cols); idx += 256) {
+            const int rr = idx / (P.slab - cols), kk = cols + idx % (P.slab - cols);
+            At[rr * lda + kk] = 0;
+        }
+        __syncthreads();
+
+        uint4 xa[4], xb[4];
+        load_x(s0, xa);
+        for (int k0 = s0; k0 < s1; k0 += kF1KSub) {
+            load_x(k0 + kF1KSub, xb);  // next sub-slice (columns past ke read as zero)
 #pragma unroll
-            for (int bt = 0; bt < MAXT; ++bt) {
-                if (bt < nbt) {
-                    const uint4 bf = *(const uint4 *)&At[(bt * 16 + li) * kF1Ld + 32 * t + 8 * g];
-                    acc[bt] = mfma16x16x32(xv[t], bf, acc[bt]);
+            for (int t = 0; t < 4; ++t) {
+                const int c0 = k0 + 32 * t + 8 * g;
+                uint32_t byte = 0;
+                if (rvalid && c0 < ke) byte = (T == 0) ? 0xFFu : keep_byte(ctr_row + (uint64_t)c0, P.seed, T);
+                const uint4 xm = apply_keep(xa[t], byte);
+                if (P.keep_bits != nullptr) {
+                    uint32_t w = byte << (8 * g);
+                    w |= (uint32_t)__shfl_xor((int)w, 16);
+                    w |= (uint32_t)__shfl_xor((int)w, 32);
+                    if (g == 0 && rvalid && k0 + 32 * t < ke)
+                        P.keep_bits[(size_t)row * P.KW + ((k0 + 32 * t) >> 5)] = w;
+                }
+#pragma unroll
+                for (int bt = 0; bt < MAXT; ++bt) {
+                    if (bt < nbt) {
+                        const uint4 bf = *(const uint4 *)&At[(bt * 16 + li) * lda + (k0 - s0) + 32 * t + 8 * g];
+                        acc[bt] = mfma16x16x32(xm, bf, acc[bt]);
+                    }
                 }
             }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xa[t] = xb[t];
         }
     }
 
@@ -221,26 +262,45 @@ __global__ __launch_bounds__(256) void f1_kernel(F1Params P) {
 }
 
 // ===========================================================================
-// Fixed-order sum of split partials: out[i] = sum_p part[p*stride + i].
+// Fixed-order sum of split partials: out[i] = sum_p part[p*stride + i].  A
+// work-group covers 64 float4 columns; its four waves each sum every fourth
+// part, and the four partial sums are added in a fixed order (bitwise
+// reproducible).
 // ===========================================================================
 __global__ __launch_bounds__(256) void sum_partials_kernel(const float *part, int nparts,
                                                            size_t stride, size_t count, float *out) {
-    const size_t i4 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i4 >= count) return;
-    const bool vec = (stride & 3) == 0 && ((uintptr_t)out & 15) == 0 && ((uintptr_t)part & 15) == 0;
-    if (i4 + 4 <= count && vec) {
-        float4 a = *(const float4 *)(part + i4);
-        for (int p = 1; p < nparts; ++p) {
-            const float4 b = *(const float4 *)(part + (size_t)p * stride + i4);
-            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    __shared__ float4 red[4][64];
+    const int t = threadIdx.x, pg = t >> 6, c = t & 63;
+    const size_t i4 = ((size_t)blockIdx.x * 64 + c) * 4;
+    const bool vec = (stride & 3) == 0 && (((uintptr_t)part) & 15) == 0;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i4 < count) {
+        if (vec && i4 + 4 <= count) {
+#pragma unroll 4
+            for (int p = pg; p < nparts; p += 4) {
+                const float4 b = *(const float4 *)(part + (size_t)p * stride + i4);
+                a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+            }
+        } else {
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int p = pg; p < nparts; p += 4)
+                for (int e = 0; e < 4; ++e)
+                    if (i4 + e < count) v[e] += part[(size_t)p * stride + i4 + e];
+            a = make_float4(v[0], v[1], v[2], v[3]);
         }
-        *(float4 *)(out + i4) = a;
-    } else {
-        for (size_t i = i4; i < count && i < i4 + 4; ++i) {
-            float a = part[i];
-            for (int p = 1; p < nparts; ++p) a += part[(size_t)p * stride + i];
-            out[i] = a;
+    }
+    red[pg][c] = a;
+    __syncthreads();
+    if (pg == 0 && i4 < count) {
+        float4 r0 = red[0][c];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+            const float4 b = red[q][c];
+            r0.x += b.x; r0.y += b.y; r0.z += b.z; r0.w += b.w;
         }
+        const float rv[4] = {r0.x, r0.y, r0.z, r0.w};
+        for (int e = 0; e < 4; ++e)
+            if (i4 + e < count) out[i4 + e] = rv[e];
     }
 }
 
@@ -298,23 +358,47 @@ __global__ __launch_bounds__(256) void b1_kernel(B1Params P) {
 #pragma unroll
         for (int b = 0; b < NBW; ++b) accB[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int rs = row_lo; rs < row_hi; rs += 64) {
-        __syncthreads();
-        for (int v = tid; v < 64 * (C1 / 8); v += 256) {
+    // Register staging of one 64-row sub-block: dY (64 x C1) and alpha*S (64 x rpad).
+    constexpr int NLY = C1 / 32;      // 16-byte dY loads per thread
+    constexpr int NLS = MAXT * 4;     // S values per thread (64 * 16*MAXT / 256)
+    uint4 yv[NLY];
+    float sv[NLS];
+    auto load_sub = [&](int rs) {
+#pragma unroll
+        for (int j = 0; j < NLY; ++j) {
+            const int v = tid + 256 * j;
             const int rrow = v / (C1 / 8), cv = v - rrow * (C1 / 8);
             const int row = rs + rrow, col = n0 + cv * 8;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (row < row_hi && col < P.n) val = *(const uint4 *)(P.dY + (size_t)row * P.n + col);
-            *(uint4 *)&Ys[rrow * LDY + cv * 8] = val;
+            yv[j] = (row < row_hi && col < P.n) ? *(const uint4 *)(P.dY + (size_t)row * P.n + col)
+                                                : make_uint4(0, 0, 0, 0);
         }
-        for (int idx = tid; idx < 64 * rpad; idx += 256) {
+#pragma unroll
+        for (int j = 0; j < NLS; ++j) {
+            const int idx = tid + 256 * j;
             const int rrow = idx / rpad, rr = idx - rrow * rpad;
             const int row = rs + rrow;
-            float v = 0.f;
-            if (row < row_hi && rr < r) v = alpha * P.S[(size_t)row * P.RS + rr];
-            Sts[rr * LDS_S + rrow] = v;
+            sv[j] = (idx < 64 * rpad && row < row_hi && rr < r) ? alpha * P.S[(size_t)row * P.RS + rr] : 0.f;
+        }
+    };
+    load_sub(row_lo);
+    for (int rs = row_lo; rs < row_hi; rs += 64) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NLY; ++j) {
+            const int v = tid + 256 * j;
+            const int rrow = v / (C1 / 8), cv = v - rrow * (C1 / 8);
+            *(uint4 *)&Ys[rrow * LDY + cv * 8] = yv[j];
+        }
+#pragma unroll
+        for (int j = 0; j < NLS; ++j) {
+            const int idx = tid + 256 * j;
+            if (idx < 64 * rpad) {
+                const int rrow = idx / rpad, rr = idx - rrow * rpad;
+                Sts[rr * LDS_S + rrow] = sv[j];
+            }
         }
         __syncthreads();
+        if (rs + 64 < row_hi) load_sub(rs + 64);  // in flight during the MFMA work below
 
         // ---- dS partial for rows rs + 16*wave .. +16 over this column tile
         {
@@ -445,38 +529,61 @@ __global__ __launch_bounds__(256) void b2_kernel(B2Params P) {
 #pragma unroll
         for (int b = 0; b < MAXT; ++b) accA[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int rs = row_lo; rs < row_hi; rs += 64) {
-        __syncthreads();
-        for (int blk = tid; blk < 8 * (C2 / 8); blk += 256) {
+    // Register staging of one 64-row sub-block: an 8x8 block of X with its
+    // keep bytes per thread (C2 == 256: every thread; 128: half) and s*dS.
+    constexpr int NBLK = (8 * (C2 / 8) + 255) / 256;  // 8x8 blocks per thread
+    constexpr int NLS = MAXT * 4;
+    uint4 xv[NBLK][8];
+    uint32_t kb8[NBLK][8];
+    float dv[NLS];
+    auto load_sub = [&](int rs) {
+#pragma unroll
+        for (int q = 0; q < NBLK; ++q) {
+            const int blk = tid + 256 * q;
             const int rb = blk / (C2 / 8), cb = blk - rb * (C2 / 8);
             const int col = k0 + cb * 8;
-            uint4 v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int row = rs + rb * 8 + e;
-                uint4 x = make_uint4(0, 0, 0, 0);
-                if (row < row_hi && col < P.k) {
-                    x = *(const uint4 *)(P.X + (size_t)row * P.k + col);
-                    if (P.keep != nullptr) {
-                        const uint32_t word = P.keep[(size_t)row * P.KW + (col >> 5)];
-                        x = apply_keep(x, (word >> (col & 31)) & 0xFFu);
-                    }
-                }
-                v[e] = x;
+                const bool ok = blk < 8 * (C2 / 8) && row < row_hi && col < P.k;
+                xv[q][e] = ok ? *(const uint4 *)(P.X + (size_t)row * P.k + col) : make_uint4(0, 0, 0, 0);
+                kb8[q][e] = (ok && P.keep != nullptr) ? P.keep[(size_t)row * P.KW + (col >> 5)] >> (col & 31) : 0xFFu;
             }
-            uint4 o[8];
-            transpose8x8(v, o);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) *(uint4 *)&Xt[(cb * 8 + c) * LDX + rb * 8] = o[c];
         }
-        for (int idx = tid; idx < 64 * rpad; idx += 256) {
+#pragma unroll
+        for (int j = 0; j < NLS; ++j) {
+            const int idx = tid + 256 * j;
             const int rrow = idx / rpad, rr = idx - rrow * rpad;
             const int row = rs + rrow;
-            float v = 0.f;
-            if (row < row_hi && rr < r) v = s * P.dS[(size_t)row * P.RS + rr];
-            dSts[rr * LDS_S + rrow] = v;
+            dv[j] = (idx < 64 * rpad && row < row_hi && rr < r) ? s * P.dS[(size_t)row * P.RS + rr] : 0.f;
+        }
+    };
+    load_sub(row_lo);
+    for (int rs = row_lo; rs < row_hi; rs += 64) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NBLK; ++q) {
+            const int blk = tid + 256 * q;
+            if (blk < 8 * (C2 / 8)) {
+                const int rb = blk / (C2 / 8), cb = blk - rb * (C2 / 8);
+                uint4 v[8], o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = apply_keep(xv[q][e], kb8[q][e] & 0xFFu);
+                transpose8x8(v, o);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) *(uint4 *)&Xt[(cb * 8 + c) * LDX + rb * 8] = o[c];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NLS; ++j) {
+            const int idx = tid + 256 * j;
+            if (idx < 64 * rpad) {
+                const int rrow = idx / rpad, rr = idx - rrow * rpad;
+                dSts[rr * LDS_S + rrow] = dv[j];
+            }
         }
         __syncthreads();
+        if (rs + 64 < row_hi) load_sub(rs + 64);  // in flight during the MFMA work below
 
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -520,6 +627,320 @@ __global__ __launch_bounds__(256) void b2_kernel(B2Params P) {
 }
 
 // ===========================================================================
+// Streaming variants of B1 and B2 for ranks <= 32.  The full-size operand
+// (dY or X) and the small per-row operands (alpha*S or dS, the keep words)
+// flow global -> LDS through a 3-stage ring of direct-to-LDS loads, so two
+// sub-blocks are in flight while a third is consumed and no VGPRs stage data.
+// Tiles of 256 bf16 columns have 512-byte LDS rows with an XOR swizzle of
+// their 16-byte chunks that is conflict-free both for 16-lane b128 reads of
+// 16 consecutive rows and for 32-lane transposing reads of rows {0-3, 8-11}
+// (or {4-7, 12-15}) over two chunks.  The transposing reads hand each lane 8
+// consecutive rows of one column: the MFMA operand of a contraction over rows.
+// ===========================================================================
+__device__ __forceinline__ int swz512(int r) {
+    return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
+}
+__device__ __forceinline__ uint32_t swz512_off(int row, int chunk) {
+    return (uint32_t)(row * 512 + ((chunk ^ swz512(row)) << 4));
+}
+// 8 consecutive rows (row0 .. row0+7, row0 % 8 == 0) of column 16*cb + (lane % 16)
+// of a swizzled 512-byte-row tile, as one MFMA operand.
+__device__ __forceinline__ uint4 tile_rows8(const lds_char *tile, int row0, int cb, int lane) {
+    const int a = lane & 15;
+    const int chunk = 2 * cb + ((a & 3) >> 1);
+    const int row = row0 + (a >> 2);
+    const uint2 lo = lds_read_tr4(tile + swz512_off(row, chunk) + (a & 1) * 8);
+    const uint2 hi = lds_read_tr4(tile + swz512_off(row + 4, chunk) + (a & 1) * 8);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+constexpr uint32_t kOOBL = 0x80000000u;  // an offset beyond every descriptor range
+
+// ----- B2 streaming: sub-blocks of 32 rows; stage = X 16 KiB + 8 aux KiB
+constexpr int B2S_ROWS = 32, B2S_X = 32 * 512, B2S_STAGE = B2S_X + 8 * 1024, B2S_NST = 3;
+
+template <int MAXT>
+__global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
+    extern __shared__ uint4 b2s_smem[];
+    lds_char *smem = (lds_char *)b2s_smem;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    int row_lo, row_hi;
+    AdapterView ad;
+    if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
+    const int r = ad.r;
+    const int nbt = (r + 15) >> 4;
+    const float s = drop_scale(ad.p);
+    const int k0 = blockIdx.y * 256;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, li = lane & 15;
+    const int nrows = row_hi - row_lo;
+    const int nsb = (nrows + B2S_ROWS - 1) / B2S_ROWS;
+    const bool has_mask = P.keep != nullptr;
+    auto clampb = [](uint64_t v) { return (uint32_t)(v < 0x7FFFFFF0ull ? v : 0x7FFFFFF0ull); };
+    const sgpr4_t dX = make_desc(P.X + (size_t)row_lo * P.k, clampb((uint64_t)nrows * P.k * 2));
+    const sgpr4_t dK = make_desc(has_mask ? P.keep + (size_t)row_lo * P.KW : P.keep,
+                                 has_mask ? clampb((uint64_t)nrows * P.KW * 4) : 0u);
+    const sgpr4_t dD = make_desc(P.dS + (size_t)row_lo * P.RS, clampb((uint64_t)nrows * P.RS * 4));
+
+    // this lane's DMA offsets inside sub-block 0 (X: 4 loads, aux: slots 2w, 2w+1)
+    uint32_t offX[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rr = 2 * (4 * wave + j) + (lane >> 5);
+        const int col = k0 + 8 * ((lane & 31) ^ swz512(rr));
+        offX[j] = col < P.k ? (uint32_t)(((size_t)rr * P.k + col) * 2) : kOOBL;
+    }
+    const uint32_t dsb = (uint32_t)(B2S_ROWS * P.RS * 4);  // dS bytes per sub-block
+    auto issue = [&](int sb, int stage) {
+        const uint32_t base = lds0 + stage * B2S_STAGE;
+        const uint32_t xo = (uint32_t)((size_t)sb * B2S_ROWS * P.k * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(dX, offX[j] == kOOBL ? kOOBL : offX[j] + xo, base + (4 * wave + j) * 1024);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int slot = 2 * wave + q;
+            const uint32_t dst = base + B2S_X + slot * 1024;
+            if (slot == 0) {
+                const int w0 = (k0 >> 5) + 4 * (lane & 1);
+                const uint32_t off = (has_mask && w0 < P.KW)
+                    ? (uint32_t)((((size_t)sb * B2S_ROWS + (lane >> 1)) * P.KW + w0) * 4) : kOOBL;
+                dma16(dK, off, dst);
+            } else {
+                const uint32_t b = (uint32_t)(slot - 1) * 1024 + lane * 16;
+                dma16(dD, b < dsb ? (uint32_t)sb * dsb + b : kOOBL, dst);
+            }
+        }
+    };
+
+    f32x4_t acc[4][MAXT];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < MAXT; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    issue(1, 1);
+    wait_vmcnt<6>();
+    __syncthreads();
+    int stage = 0, lstage = 2;
+    for (int sb = 0; sb < nsb; ++sb) {
+        issue(sb + 2, lstage);
+        const lds_char *xt = smem + stage * B2S_STAGE;
+        const uint32_t *mk = (const uint32_t *)(xt + B2S_X);
+        const float *ds = (const float *)(xt + B2S_X + 1024);
+        // dS operand (N = rank): rows 8g..8g+7 of rank column 16*bt + li, times s
+        uint4 bhi[MAXT], blo[MAXT];
+#pragma unroll
+        for (int bt = 0; bt < MAXT; ++bt) {
+            float v[8];
+            const int rr = 16 * bt + li;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (bt < nbt && rr < r) ? s * ds[(8 * g + e) * P.RS + rr] : 0.f;
+            split_frag(v, bhi[bt], blo[bt]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int cb = 4 * wave + mb;  // 16-column block of this work-group's 256
+            uint4 xf = tile_rows8(xt, 8 * g, cb, lane);
+            if (has_mask) {
+                const int bit = 16 * (cb & 1) + li;
+                uint32_t m[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w0 = mk[(8 * g + 2 * q) * 8 + (cb >> 1)];
+                    const uint32_t w1 = mk[(8 * g + 2 * q + 1) * 8 + (cb >> 1)];
+                    m[q] = (((w0 >> bit) & 1u) ? 0x0000FFFFu : 0u) | (((w1 >> bit) & 1u) ? 0xFFFF0000u : 0u);
+                }
+                xf = make_uint4(xf.x & m[0], xf.y & m[1], xf.z & m[2], xf.w & m[3]);
+            }
+#pragma unroll
+            for (int bt = 0; bt < MAXT; ++bt) {
+                if (bt < nbt) {
+                    acc[mb][bt] = mfma16x16x32(xf, bhi[bt], acc[mb][bt]);
+                    acc[mb][bt] = mfma16x16x32(xf, blo[bt], acc[mb][bt]);
+                }
+            }
+        }
+        wait_vmcnt<6>();
+        __syncthreads();
+        stage = stage == B2S_NST - 1 ? 0 : stage + 1;
+        lstage = lstage == B2S_NST - 1 ? 0 : lstage + 1;
+    }
+    wait_vmcnt<0>();
+
+    float *dap = P.dApart + (size_t)blockIdx.x * P.k * P.RS;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int bt = 0; bt < MAXT; ++bt) {
+            if (bt < nbt) {
+                const int rr = bt * 16 + li;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int kk = k0 + (4 * wave + mb) * 16 + 4 * g + v;
+                    if (kk < P.k && rr < r) dap[(size_t)kk * P.RS + rr] = acc[mb][bt][v];
+                }
+            }
+        }
+    }
+}
+
+// ----- B1 streaming: sub-blocks of 32 rows; stage = dY 16 KiB + 4 KiB S (ranks <= 32).
+// Waves (w & 1) own 16 rows for dS and split the 256 columns in halves
+// (w >> 1), each half writing its own dS partial: partial index 2*ct + half.
+constexpr int B1S_ROWS = 32, B1S_Y = 32 * 512, B1S_STAGE = B1S_Y + 4 * 1024, B1S_NST = 3;
+constexpr int B1S_LDB = 256 + 8;  // row stride of the staged B chunk (elements)
+
+template <int MAXT>
+__global__ __launch_bounds__(256) void b1s_kernel(B1Params P) {
+    extern __shared__ uint4 b1s_smem[];
+    lds_char *smem = (lds_char *)b1s_smem;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    uint16_t *Bs = (uint16_t *)(smem + B1S_NST * B1S_STAGE);  // [r_lds][B1S_LDB]
+
+    int row_lo, row_hi;
+    AdapterView ad;
+    if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
+    const int r = ad.r;
+    const int nbt = (r + 15) >> 4;
+    const int rpad = nbt * 16;
+    const float alpha = ad.alpha;
+    const int ct = blockIdx.y, n0 = ct * 256;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, li = lane & 15;
+    const int rb = wave & 1, half = wave >> 1;
+    const int nrows = row_hi - row_lo;
+    const int nsb = (nrows + B1S_ROWS - 1) / B1S_ROWS;
+    auto clampb = [](uint64_t v) { return (uint32_t)(v < 0x7FFFFFF0ull ? v : 0x7FFFFFF0ull); };
+    const sgpr4_t dYd = make_desc(P.dY + (size_t)row_lo * P.n, clampb((uint64_t)nrows * P.n * 2));
+    const sgpr4_t dS = make_desc(P.S + (size_t)row_lo * P.RS, clampb((uint64_t)nrows * P.RS * 4));
+
+    // B chunk (rank x 256 columns), zero-padded, staged once
+    for (int idx = tid; idx < rpad * 256; idx += 256) {
+        const int rr = idx >> 8, j = idx & 255;
+        uint16_t v = 0;
+        if (rr < r && n0 + j < P.n) v = ad.B[(size_t)rr * P.n + n0 + j];
+        Bs[rr * B1S_LDB + j] = v;
+    }
+
+    uint32_t offY[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rr = 2 * (4 * wave + j) + (lane >> 5);
+        const int col = n0 + 8 * ((lane & 31) ^ swz512(rr));
+        offY[j] = col < P.n ? (uint32_t)(((size_t)rr * P.n + col) * 2) : kOOBL;
+    }
+    const uint32_t sbb = (uint32_t)(B1S_ROWS * P.RS * 4);  // S bytes per sub-block
+    auto issue = [&](int sb, int stage) {
+        const uint32_t base = lds0 + stage * B1S_STAGE;
+        const uint32_t yo = (uint32_t)((size_t)sb * B1S_ROWS * P.n * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(dYd, offY[j] == kOOBL ? kOOBL : offY[j] + yo, base + (4 * wave + j) * 1024);
+        const uint32_t b = (uint32_t)wave * 1024 + lane * 16;
+        dma16(dS, b < sbb ? (uint32_t)sb * sbb + b : kOOBL, base + B1S_Y + wave * 1024);
+    };
+
+    f32x4_t accB[MAXT][4];
+#pragma unroll
+    for (int a = 0; a < MAXT; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) accB[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    issue(1, 1);
+    wait_vmcnt<5>();
+    __syncthreads();
+    int stage = 0, lstage = 2;
+    float *dsp = P.dSpart + (size_t)(2 * ct + half) * P.m * P.RS;
+    for (int sb = 0; sb < nsb; ++sb) {
+        issue(sb + 2, lstage);
+        const lds_char *yt = smem + stage * B1S_STAGE;
+        const float *st = (const float *)(yt + B1S_Y);
+        const int rs = row_lo + sb * B1S_ROWS;
+
+        // ---- dS partial: 16 rows x rank over this wave's 128 columns
+        f32x4_t accS[MAXT];
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) accS[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int arow = 16 * rb + li;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t = 4 * half + tt;
+            const uint4 af = *(const uint4 *)(yt + swz512_off(arow, 4 * t + g));
+#pragma unroll
+            for (int bt = 0; bt < MAXT; ++bt) {
+                if (bt < nbt) {
+                    const uint4 bf = *(const uint4 *)&Bs[(bt * 16 + li) * B1S_LDB + 32 * t + 8 * g];
+                    accS[bt] = mfma16x16x32(af, bf, accS[bt]);
+                }
+            }
+        }
+#pragma unroll
+        for (int bt = 0; bt < MAXT; ++bt) {
+            if (bt < nbt) {
+                const int col = bt * 16 + li;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int orow = rs + rb * 16 + 4 * g + v;
+                    if (orow < row_hi && col < P.RS) dsp[(size_t)orow * P.RS + col] = col < r ? alpha * accS[bt][v] : 0.f;
+                }
+            }
+        }
+        for (int col = rpad + li; col < P.RS; col += 16) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int orow = rs + rb * 16 + 4 * g + v;
+                if (orow < row_hi) dsp[(size_t)orow * P.RS + col] = 0.f;
+            }
+        }
+
+        // ---- dB partial: rank x wave's 64 columns, K = the 32 rows
+        uint4 bfr[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) bfr[nb] = tile_rows8(yt, 8 * g, 4 * wave + nb, lane);
+#pragma unroll
+        for (int bt = 0; bt < MAXT; ++bt) {
+            if (bt < nbt) {
+                float v[8];
+                const int rr = 16 * bt + li;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = rr < r ? alpha * st[(8 * g + e) * P.RS + rr] : 0.f;
+                uint4 ahi, alo;
+                split_frag(v, ahi, alo);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    accB[bt][nb] = mfma16x16x32(ahi, bfr[nb], accB[bt][nb]);
+                    accB[bt][nb] = mfma16x16x32(alo, bfr[nb], accB[bt][nb]);
+                }
+            }
+        }
+        wait_vmcnt<5>();
+        __syncthreads();
+        stage = stage == B1S_NST - 1 ? 0 : stage + 1;
+        lstage = lstage == B1S_NST - 1 ? 0 : lstage + 1;
+    }
+    wait_vmcnt<0>();
+
+    float *dbp = P.dBpart + (size_t)blockIdx.x * P.RS * P.n;
+#pragma unroll
+    for (int bt = 0; bt < MAXT; ++bt) {
+        if (bt < nbt) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int col = n0 + (wave * 4 + nb) * 16 + li;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int rr = bt * 16 + 4 * g + v;
+                    if (rr < r && col < P.n) dbp[(size_t)rr * P.n + col] = accB[bt][nb][v];
+                }
+            }
+        }
+    }
+}
+
+// ===========================================================================
 // Per-adapter gradient reduction: sum the chunk partials that belong to the
 // adapter, in chunk order, and write bf16 (zeros if the adapter has no rows).
 // ===========================================================================
@@ -532,6 +953,7 @@ struct GradReduceParams {
 };
 
 __global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceParams P) {
+    __shared__ float red[4][64];
     const int a = blockIdx.y;
     AdapterView ad;
     if (P.work.chunks == nullptr) {
@@ -552,17 +974,27 @@ __global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceParams P) {
     if (P.work.chunks == nullptr) nch = (P.m + P.work.rows_per_chunk - 1) / P.work.rows_per_chunk;
     else nch = min(P.work.chunk_count[0], P.chunk_cap);
 
-    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
-        const size_t ro = e / cols_out, co = e - ro * cols_out;
+    // 64 outputs per work-group pass; wave pg sums chunks pg, pg+4, ...
+    const int t = threadIdx.x, pg = t >> 6, c = t & 63;
+    for (size_t base = (size_t)blockIdx.x * 64; base < total; base += (size_t)gridDim.x * 64) {
+        const size_t e = base + c;
         float acc = 0.f;
-        for (int c = 0; c < nch; ++c) {
-            if (P.work.chunks != nullptr) {
-                const ChunkEntry ce = P.work.chunks[c];
-                if (ce.adapter != a) continue;
+        if (e < total) {
+            const size_t ro = e / cols_out, co = e - ro * cols_out;
+            const float *src = P.part + ro * row_stride + co;
+#pragma unroll 4
+            for (int ch = pg; ch < nch; ch += 4) {
+                if (P.work.chunks != nullptr && P.work.chunks[ch].adapter != a) continue;
+                acc += src[(size_t)ch * chunk_stride];
             }
-            acc += P.part[(size_t)c * chunk_stride + ro * row_stride + co];
         }
-        outp[e] = (uint16_t)f32_to_bf16_rne(acc);
+        __syncthreads();
+        red[pg][c] = acc;
+        __syncthreads();
+        if (pg == 0 && e < total) {
+            const float v = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+            outp[e] = (uint16_t)f32_to_bf16_rne(v);
+        }
     }
 }
 
@@ -643,7 +1075,10 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
     P.ksl = ksl;
     P.KW = (k + 31) / 32;
     P.r_lds = r_lds_of(src);
-    const size_t lds = (size_t)P.r_lds * kF1Ld * sizeof(uint16_t);
+    // A slab: about 20 KiB of LDS so several work-groups share a CU
+    const int slab_cols = std::max(kF1KSub, (20480 / (P.r_lds * 2)) / kF1KSub * kF1KSub);
+    P.slab = std::min(ksl, slab_cols);
+    const size_t lds = (size_t)P.r_lds * (P.slab + 8) * sizeof(uint16_t);
     const dim3 grid(chunk_cap, KS);
     (void)hipGetLastError();
     const int slot = prof_begin("f1_mask_down", stream);
@@ -662,7 +1097,7 @@ hipError_t launch_sum_partials(const float *part, int nparts, size_t part_stride
     if (count == 0) return hipSuccess;
     (void)hipGetLastError();
     const int slot = prof_begin(name, stream);
-    const size_t blocks = (count + 1023) / 1024;
+    const size_t blocks = (count + 255) / 256;
     hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part,
                        nparts, part_stride, count, out);
     return finish_launch(slot, stream);
@@ -689,7 +1124,11 @@ hipError_t launch_b1(const void *dY, const float *S, int m, int n, int RS, const
     (void)hipGetLastError();
     const int slot = prof_begin("b1_ds_db", stream);
     const dim3 grid(chunk_cap, cdiv(n, C1));
-    if (C1 == 256) {
+    if (C1 == 256 && P.r_lds <= 32) {
+        const size_t slds = (size_t)B1S_NST * B1S_STAGE + (size_t)P.r_lds * B1S_LDB * 2;
+        if (P.r_lds <= 16) launch_with_lds(b1s_kernel<1>, grid, slds, stream, P);
+        else launch_with_lds(b1s_kernel<2>, grid, slds, stream, P);
+    } else if (C1 == 256) {
         switch (rank_blocks(P.r_lds)) {
         case 1: launch_with_lds(b1_kernel<256, 1>, grid, lds, stream, P); break;
         case 2: launch_with_lds(b1_kernel<256, 2>, grid, lds, stream, P); break;
@@ -720,7 +1159,11 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
     (void)hipGetLastError();
     const int slot = prof_begin("b2_da", stream);
     const dim3 grid(chunk_cap, cdiv(k, C2));
-    if (C2 == 256) {
+    if (C2 == 256 && P.r_lds <= 32) {
+        const size_t slds = (size_t)B2S_NST * B2S_STAGE;
+        if (P.r_lds <= 16) launch_with_lds(b2s_kernel<1>, grid, slds, stream, P);
+        else launch_with_lds(b2s_kernel<2>, grid, slds, stream, P);
+    } else if (C2 == 256) {
         switch (rank_blocks(P.r_lds)) {
         case 1: launch_with_lds(b2_kernel<256, 1>, grid, lds, stream, P); break;
         case 2: launch_with_lds(b2_kernel<256, 2>, grid, lds, stream, P); break;
@@ -746,7 +1189,7 @@ hipError_t launch_grad_reduce(int which, const float *part, int m, int k, int n,
     P.chunk_cap = chunk_cap;
     const int nad = src.table ? src.num_adapters : 1;
     const size_t per = (size_t)(which == 0 ? n : k) * (size_t)RS;
-    const int gx = (int)std::min<size_t>((per + 255) / 256, 4096);
+    const int gx = (int)std::min<size_t>((per + 63) / 64, 8192);
     (void)hipGetLastError();
     const int slot = prof_begin(which == 0 ? "reduce_db" : "reduce_da", stream);
     hipLaunchKernelGGL(grad_reduce_kernel, dim3(gx, nad), dim3(256), 0, stream, P);
