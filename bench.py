@@ -34,13 +34,47 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=32,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows (tokens) of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shapes", default="4096,14336", help="n of each projection (k = 4096)")
     ap.add_argument("--m", type=int, default=8192)
     ap.add_argument("--r", type=int, default=16)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB (byte-counter calibration)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama8b_m8192_hbm_traffic.md")
+
+
+def source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_kernels.hip", "device_common.hpp"):
+        with open(os.path.join(ROOT, "lora_fine_tuning_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if
+    it was taken on the current GEMM source; else None."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    digest, vals = None, {}
+    for ln in lines:
+        ln = ln.strip().strip("`")
+        if ln.startswith("source_digest:"):
+            digest = ln.split(":", 1)[1].strip()
+        elif ln.startswith("traffic_bytes_per_launch["):
+            name = ln[len("traffic_bytes_per_launch["):ln.index("]")]
+            vals[name] = float(ln.split(":", 1)[1])
+    if digest != source_digest():
+        return None
+    return vals.get(kernel)
 
 
 def main():
@@ -143,9 +177,22 @@ def main():
     dom = max(flops, key=lambda nm: kernels[nm]["total_ms"])
     kd = kernels[dom]
     achieved = flops[dom] / (kd["total_ms"] / args.steps * 1e-3) / 1e12  # TFLOP/s
+    traffic = committed_traffic(dom)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else round(traffic)}
+    # HBM-bound kernels: algorithmic bytes per launch (both shapes) / event time
+    kw = (k + 31) // 32
+    hbm_bytes = {
+        "f1_mask_down": sum(m * k * 2 + m * kw * 4 + m * r * 4 + k * r * 2 for _ in shapes),
+        "b1_ds_db": sum(m * st["n"] * 2 + 2 * m * r * 4 + 2 * r * st["n"] * 2 for st in shapes),
+        "b2_da": sum(m * k * 2 + m * kw * 4 + m * r * 4 + k * r * 2 for _ in shapes),
+    }
+    hbm = {}
+    for nm, b in hbm_bytes.items():
+        t = kernels[nm]["total_ms"] / args.steps * 1e-3
+        hbm[nm] = {"GB/s": round(b / t / 1e9, 1), "frac": round(b / t / 1e9 / PEAK_HBM_GBS, 4)}
 
     tokens_per_s = m / (ms * 1e-3)
     result = {
@@ -170,7 +217,18 @@ def main():
         "kernels": {nm: {kk: (round(v, 3) if isinstance(v, float) else v) for kk, v in d.items()}
                     for nm, d in kernels.items()},
         "ms_per_step_with_kernel_events": round(ms_prof, 4),
+        "hbm_kernels": hbm,
+        "gemm_source_digest": source_digest(),
     }
+    if args.copy_calib_mib:
+        nel = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + written per copy, 3 copies",
+              file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(m, k, ns, r, alpha, p, args.cpu_rows)
     print(json.dumps(result), flush=True)

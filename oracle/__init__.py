@@ -277,3 +277,67 @@ def multi_lora_bwd(dY, X, W, adapters, seg_off, seg_adapter, r_max, seed, offset
         dA[a] += out["dA"]
         dB[a] += out["dB"]
     return {"dX": dX, "dA": dA, "dB": dB, "dS": dS}
+
+
+# ----------------------------------------------------------------------------
+# Sampled evaluation for large shapes
+# ----------------------------------------------------------------------------
+def lora_sampled(X, W, A, B, dY, alpha, p, seed, offset, out_rows, a_rows, b_cols, rows=None):
+    """Forward and backward of one adapter where the m*k*n-sized results are
+    evaluated only at samples: Y and dX on local rows ``out_rows``, dA on rows
+    ``a_rows`` (input features), dB on columns ``b_cols``.  The mask, S and dS
+    are computed in full.  Every sampled entry is what ``lora_fwd`` /
+    ``lora_bwd`` give at that position: the same functions run on a subset of
+    rows (Y, dX) or columns (dA, dB), each entry's sum in the same order."""
+    X, dY = _f64(X), _f64(dY)
+    m, k = X.shape
+    if rows is None:
+        rows = np.arange(m, dtype=np.int64)
+    out_rows = np.asarray(out_rows, dtype=np.int64)
+    a_rows = np.asarray(a_rows, dtype=np.int64)
+    b_cols = np.asarray(b_cols, dtype=np.int64)
+    r = np.asarray(A).shape[1]
+    keep = keep_mask(seed, offset, rows, k, p)
+    S = lora_s(X, keep, A, p)
+    dS = lora_ds(dY, B, alpha)
+    Y = lora_y(X[out_rows], W, S[out_rows], B, alpha)
+    dX = lora_dx(dY[out_rows], W, dS[out_rows], A, np.ascontiguousarray(keep[out_rows]), p)
+    dB = np.zeros((r, b_cols.size))
+    lora_db_acc(S, np.ascontiguousarray(dY[:, b_cols]), alpha, dB)
+    dA = np.zeros((a_rows.size, r))
+    lora_da_acc(np.ascontiguousarray(X[:, a_rows]), np.ascontiguousarray(keep[:, a_rows]), dS, p, dA)
+    return {"Y": Y, "dX": dX, "dA": dA, "dB": dB, "S": S, "dS": dS, "keep": keep}
+
+
+def multi_lora_sampled(X, W, adapters, dY, seg_off, seg_adapter, r_max, seed, offset, out_rows,
+                       a_rows, b_cols):
+    """Mixed-adapter counterpart of ``lora_sampled``: ``out_rows`` are sorted
+    global row indices; Y and dX come back in that order, dA / dB per adapter
+    on the sampled features / columns (summed over the adapter's segments, in
+    segment order, as in ``multi_lora_bwd``), S (m x r_max) and the mask in
+    full."""
+    X, dY = _f64(X), _f64(dY)
+    m, k = X.shape
+    n = np.asarray(W).shape[1]
+    out_rows = np.asarray(out_rows, dtype=np.int64)
+    a_rows = np.asarray(a_rows, dtype=np.int64)
+    b_cols = np.asarray(b_cols, dtype=np.int64)
+    Y = np.zeros((out_rows.size, n))
+    dX = np.zeros((out_rows.size, k))
+    S = np.zeros((m, r_max))
+    keep = np.ones((m, k), dtype=np.uint8)
+    dA = [np.zeros((a_rows.size, np.asarray(ad["A"]).shape[1])) for ad in adapters]
+    dB = [np.zeros((np.asarray(ad["B"]).shape[0], b_cols.size)) for ad in adapters]
+    for lo, hi, a in segments_rows(seg_off, seg_adapter):
+        ad = adapters[a]
+        sel = np.nonzero((out_rows >= lo) & (out_rows < hi))[0]
+        out = lora_sampled(X[lo:hi], W, ad["A"], ad["B"], dY[lo:hi], ad["alpha"], ad["p"], seed,
+                           offset, out_rows[sel] - lo, a_rows, b_cols,
+                           rows=np.arange(lo, hi, dtype=np.int64))
+        Y[sel] = out["Y"]
+        dX[sel] = out["dX"]
+        S[lo:hi, : out["S"].shape[1]] = out["S"]
+        keep[lo:hi] = out["keep"]
+        dA[a] += out["dA"]
+        dB[a] += out["dB"]
+    return {"Y": Y, "dX": dX, "dA": dA, "dB": dB, "S": S, "keep": keep}

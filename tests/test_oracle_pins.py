@@ -351,6 +351,50 @@ def test_multi_unused_adapter_gets_zero_gradients():
 
 
 # ---------------------------------------------------------------------------
+# Sampled evaluation (used for the full-size GPU checks) = the full oracle
+# restricted to the samples, exactly
+# ---------------------------------------------------------------------------
+def test_sampled_equals_full_single():
+    rng = np.random.default_rng(11)
+    m, k, n, r = 40, 24, 32, 3
+    X, W, A, B, dY = (rand((m, k), rng), rand((k, n), rng, 0.3), rand((k, r), rng, 0.3),
+                      rand((r, n), rng, 0.3), rand((m, n), rng))
+    out_rows, a_rows, b_cols = [0, 7, 39], [1, 23], [0, 5, 31]
+    f = oracle.lora_fwd(X, W, A, B, 2.0, np.float32(0.3), 9, 16)
+    g = oracle.lora_bwd(dY, X, W, A, B, 2.0, np.float32(0.3), 9, 16)
+    s = oracle.lora_sampled(X, W, A, B, dY, 2.0, np.float32(0.3), 9, 16, out_rows, a_rows, b_cols)
+    np.testing.assert_array_equal(s["keep"], f["keep"])
+    np.testing.assert_array_equal(s["S"], f["S"])
+    np.testing.assert_array_equal(s["dS"], g["dS"])
+    np.testing.assert_array_equal(s["Y"], f["Y"][out_rows])
+    np.testing.assert_array_equal(s["dX"], g["dX"][out_rows])
+    np.testing.assert_array_equal(s["dA"], g["dA"][a_rows])
+    np.testing.assert_array_equal(s["dB"], g["dB"][:, b_cols])
+
+
+def test_sampled_equals_full_multi():
+    rng = np.random.default_rng(12)
+    m, k, n = 50, 24, 16
+    X, W, dY = rand((m, k), rng), rand((k, n), rng, 0.3), rand((m, n), rng)
+    adapters = [{"A": rand((k, rr), rng, 0.3), "B": rand((rr, n), rng, 0.3),
+                 "alpha": a, "p": np.float32(p)}
+                for rr, a, p in zip((2, 5, 3), (1.0, 2.0, 0.5), (0.0, 0.2, 0.4))]
+    seg_off, seg_ad = np.array([0, 7, 7, 20, 33, 50]), np.array([1, 0, 2, 1, 0])
+    out_rows, a_rows, b_cols = [0, 6, 7, 19, 20, 49], [0, 11, 23], [3, 15]
+    f = oracle.multi_lora_fwd(X, W, adapters, seg_off, seg_ad, 5, 5, 24)
+    g = oracle.multi_lora_bwd(dY, X, W, adapters, seg_off, seg_ad, 5, 5, 24)
+    s = oracle.multi_lora_sampled(X, W, adapters, dY, seg_off, seg_ad, 5, 5, 24, out_rows,
+                                  a_rows, b_cols)
+    np.testing.assert_array_equal(s["keep"], f["keep"])
+    np.testing.assert_array_equal(s["S"], f["S"])
+    np.testing.assert_array_equal(s["Y"], f["Y"][out_rows])
+    np.testing.assert_array_equal(s["dX"], g["dX"][out_rows])
+    for a in range(3):
+        np.testing.assert_array_equal(s["dA"][a], g["dA"][a][a_rows])
+        np.testing.assert_array_equal(s["dB"][a], g["dB"][a][:, b_cols])
+
+
+# ---------------------------------------------------------------------------
 # Brute force: pure-Python loops on a tiny case
 # ---------------------------------------------------------------------------
 def test_against_python_loops():
