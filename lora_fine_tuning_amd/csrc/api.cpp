@@ -161,6 +161,14 @@ static lora_status check_rank(int32_t r) {
     return LORA_OK;
 }
 
+// The fused epilogue of the forward GEMM addresses B (r x n bf16) with 32-bit
+// byte offsets.
+static lora_status check_b_size(int32_t r, int64_t n) {
+    if ((int64_t)r * n * 2 >= (1LL << 31))
+        return fail(LORA_ERR_UNSUPPORTED, "B of %d x %lld bf16 exceeds 2 GiB", r, (long long)n);
+    return LORA_OK;
+}
+
 static lora_status check_p(float p) {
     REQUIRE(p >= 0.0f && p < 1.0f, "dropout p = %g must be in [0, 1)", (double)p);
     return LORA_OK;
@@ -305,6 +313,7 @@ extern "C" lora_status lora_linear_fwd(const void *X, const void *W, const void 
     CHECK(check_shape(m, k, n));
     CHECK(check_rank(r));
     CHECK(check_p(p));
+    CHECK(check_b_size(r, n));
     REQUIRE(offset % 8 == 0, "offset = %llu must be a multiple of 8", (unsigned long long)offset);
     REQ_PTR(W, 16);
     REQ_PTR(A, 2);
@@ -430,6 +439,7 @@ extern "C" lora_status multi_lora_linear_fwd(const void *X, const void *W, const
                                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
     CHECK(check_shape(m, k, n));
     CHECK(check_multi(adapters, num_adapters, seg_off, seg_adapter, num_segments, r_max));
+    CHECK(check_b_size(r_max, n));
     REQUIRE(offset % 8 == 0, "offset = %llu must be a multiple of 8", (unsigned long long)offset);
     REQ_PTR(W, 16);
     if (m == 0) return LORA_OK;

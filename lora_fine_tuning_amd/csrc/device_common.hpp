@@ -50,6 +50,21 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 &a, const uint4 &b, 
                                                     __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// acc += a * b on the accumulator's own AGPRs.  The tied operand keeps each
+// accumulator at a fixed register across a K loop (the builtin leaves the
+// allocator free to rotate 256 accumulator registers every trip).  The
+// compiler does not model the latency of this form: mfma_drain() must run
+// before anything but another in-place MFMA touches the accumulators.
+__device__ __forceinline__ void mfma16x16x32_inplace(f32x4_t &acc, const uint4 &a, const uint4 &b) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(acc)
+                 : "v"(__builtin_bit_cast(i32x4_t, a)), "v"(__builtin_bit_cast(i32x4_t, b)));
+}
+// Wait states after the last in-place MFMA before its result is read by any
+// other instruction (a 16x16x32 MFMA needs at most 11; this gives 32).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
+
 // Eight fp32 values -> hi and lo bf16 fragments.
 __device__ __forceinline__ void split_frag(const float v[8], uint4 &hi, uint4 &lo) {
     uint32_t h[8], l[8];

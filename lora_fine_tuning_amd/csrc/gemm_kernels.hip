@@ -8,22 +8,36 @@
 //        partial input gradient is re-read or re-written)
 //   frozen (epi 0):  Y = X W and dX = dY W^T, the baseline layer.
 //
-// Tiling: 256 x 256 output tile per work-group of 4 waves (2 x 2), 64-deep K
-// steps through double-buffered LDS (2 x 72 KiB), v_mfma_f32_32x32x16_bf16
-// with fp32 accumulators (each wave a 4 x 4 grid of 32 x 32 tiles).  The
-// column-side operand is the MFMA's first source so every lane ends up with 4
-// consecutive output columns of one row (8-byte stores).  For the forward W is
-// k x n (n contiguous): each thread loads an 8 x 8 block and transposes it in
-// registers so the LDS copy is K-contiguous.  Work-group ids are remapped so
-// each XCD gets a contiguous range of tiles, visited in groups of 8 row panels.
+// Tiling: a 256 x 256 output tile per work-group of 4 waves (2 x 2, one wave
+// per SIMD), each wave an 8 x 8 grid of v_mfma_f32_16x16x32_bf16 tiles with
+// fp32 accumulators.  (The 16x16x32 form moves a quarter of the accumulator
+// bytes per flop of the 32x32x16 form; under sustained load the chip holds a
+// clock about 15% higher with it.)  The column-side operand is the MFMA's
+// first source, so each lane ends with 4 consecutive output columns of one
+// row (8-byte stores).
+//
+// K advances in 64-deep stages through a 2-stage LDS ring (2 x 64 KiB) filled
+// by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds); a stage is two
+// 32-deep MFMA steps.  The loads of stage t+2 are issued right after the
+// barrier that retires stage t's buffer, interleaved with the MFMAs of the
+// second step of stage t and so covered by two MFMA steps.  Fragment reads for
+// the next step interleave with the MFMAs of the current one (double-buffered
+// fragments).  K-contiguous tiles use 128-byte rows with a 16-byte-chunk XOR
+// swizzle (conflict-free 16-lane b128 reads of 16 consecutive rows); the
+// forward's W tile is k-row major (512-byte rows, n contiguous) and is read
+// with ds_read_b64_tr_b16, which gives each lane 4 consecutive k of one
+// column; its swizzle keeps the 32 lanes of a half-wave (8 k-rows x 32 bytes)
+// on distinct banks.  Work-group ids are remapped so each XCD gets a
+// contiguous range of tiles, visited in groups of 8 row panels.
 //
 // The LoRA terms run after the K loop as extra rank-deep MFMA steps whose
 // operands come straight from global memory: fp32 S (or dS) as hi+lo bf16
 // pairs times B (or A).  For the masked backward term the rank-deep product
-// goes to a second accumulator, one 32-row band at a time, and is added under
+// goes to a second accumulator, one 16-row band at a time, and is added under
 // the stored keep bits.  Mixed-adapter tiles run one such pass per segment
 // overlapping the tile (rows of other segments contribute zero).
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -66,6 +80,14 @@ __device__ __forceinline__ void tile_coords(int wg, int G, int tiles_m, int tile
     tn = in / gsz;
 }
 
+// Buffer resource over `bytes` bytes from `base`; loads past the end return 0
+// and stores past the end are dropped, so edge tiles need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+    const uint32_t nrec = (uint32_t)(bytes < 0x7FFFFFF0ull ? bytes : 0x7FFFFFF0ull);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nrec, 0x00020000);
+}
+constexpr uint32_t kOOB = 0x80000000u;  // an offset beyond every resource
+
 // One item of the LoRA epilogue: rows [lo, hi) with one adapter.
 struct ExtItem {
     int lo, hi;
@@ -74,36 +96,71 @@ struct ExtItem {
     float scale;
 };
 
-// Rank-deep MFMA step inputs for one 32-row band: fp32 rows of S/dS times
-// `scale`, split into hi/lo fragments; rows outside [lo, hi) give zero.
-__device__ __forceinline__ void row_ext_frags(const GemmParams &P, const ExtItem &it, int row, int rr0,
-                                              int lane, uint4 &hi, uint4 &lo) {
+// Rank-deep MFMA step, row side: fp32 S/dS of `row` for ranks rr0 + 8*(lane/16)
+// .. +7, times `scale`, split into hi/lo fragments; rows outside [lo, hi) and
+// ranks past r read as zero (out-of-range buffer offsets, no branches).  rS
+// starts at row `row0` (the wave's first row), so offsets stay small.
+// `vec`: r and RS are multiples of 8 and Sx is 16-byte aligned, so the 8
+// values are two aligned 16-byte loads.
+__device__ __forceinline__ void row_ext_frags(const GemmParams &P, __amdgpu_buffer_rsrc_t rS, int row0,
+                                              const ExtItem &it, int row, int rr0, int lane, bool vec,
+                                              uint4 &hi, uint4 &lo) {
     float v[8];
     const bool ok = row >= it.lo && row < it.hi;
-    const float *src = P.Sx + (size_t)(ok ? row : 0) * P.RS;
+    const int rb = rr0 + 8 * (lane >> 4);
+    const uint32_t base = (uint32_t)((row - row0) * P.RS + rb) * 4u;
+    if (vec) {
+        const uint32_t off = (ok && rb < it.r) ? base : kOOB;
+        const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off, 0, 0));
+        const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off == kOOB ? kOOB : off + 16, 0, 0));
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int rr = rr0 + 8 * (lane >> 5) + e;
-        v[e] = (ok && rr < it.r) ? it.scale * src[rr] : 0.f;
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t off = (ok && rb + e < it.r) ? base + 4u * e : kOOB;
+            v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, off, 0, 0));
+        }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= it.scale;
     split_frag(v, hi, lo);
 }
 
-// Column-side fragment of the rank-deep step: 8 consecutive ranks of output
-// column `col`.  epi 1 reads B[rr][col] (stride N); epi 2 reads A[col][rr].
+// Rank-deep step, column side: 8 consecutive ranks of output column `col`
+// (zero past r or N).  epi 1 reads B[rr][col] (stride N); epi 2 reads
+// A[col][rr], 16 contiguous bytes, one load when `vec` (r a multiple of 8, A
+// 16-byte aligned).  rW is a buffer resource over B (r x N) or A (N x r)
+// starting at column `col0` (B's whole rows stay under 2 GiB: checked by the
+// launcher).
 template <int EPI>
-__device__ __forceinline__ uint4 col_ext_frag(const GemmParams &P, const ExtItem &it, int col, int rr0,
-                                              int lane) {
-    uint32_t h[8];
+__device__ __forceinline__ uint4 col_ext_frag(const GemmParams &P, __amdgpu_buffer_rsrc_t rW, int col0,
+                                              const ExtItem &it, int col, int rr0, int lane, bool vec) {
     const bool cok = col < P.N;
+    const int rb = rr0 + 8 * (lane >> 4);
+    const int cr = col - col0;
+    if (EPI == 2 && vec) {
+        const uint32_t off = (cok && rb < it.r) ? (uint32_t)(cr * it.r + rb) * 2u : kOOB;
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
+    }
+    uint32_t h[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int rr = rr0 + 8 * (lane >> 5) + e;
-        uint32_t x = 0;
-        if (cok && rr < it.r) x = EPI == 1 ? it.w[(size_t)rr * P.N + col] : it.w[(size_t)col * it.r + rr];
-        h[e] = x;
+        const int rr = rb + e;
+        const uint32_t idx = EPI == 1 ? (uint32_t)rr * (uint32_t)P.N + (uint32_t)cr : (uint32_t)(cr * it.r + rr);
+        const uint32_t off = (cok && rr < it.r) ? idx * 2u : kOOB;
+        h[e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rW, off, 0, 0);
     }
     return make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+}
+
+// Buffer resource over an adapter's rank-side matrix (r x N for B, N x r for
+// A) from column col0 on.
+template <int EPI>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ext_rsrc(const GemmParams &P, const ExtItem &it, int col0) {
+    const uint64_t total = (uint64_t)it.r * (uint64_t)P.N * 2u;
+    const uint64_t skip = (uint64_t)min(col0, P.N) * (EPI == 1 ? 2u : 2u * (uint64_t)it.r);
+    return make_rsrc(it.w + (EPI == 1 ? (size_t)min(col0, P.N) : (size_t)min(col0, P.N) * it.r), total - skip);
 }
 
 template <int EPI, bool MULTI>
@@ -140,17 +197,6 @@ __device__ __forceinline__ int first_segment(const GemmParams &P, int m0) {
     return lo;
 }
 
-// Buffer resource over `bytes` bytes from `base`; loads past the end return 0
-// and stores past the end are dropped, so edge tiles need no branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes) {
-    const uint32_t nrec = (uint32_t)(bytes < 0x7FFFFFF0ull ? bytes : 0x7FFFFFF0ull);
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nrec, 0x00020000);
-}
-constexpr uint32_t kOOB = 0x80000000u;  // an offset beyond every resource
-
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 constexpr int BK = 64;              // K depth of one LDS stage
 constexpr int NST = 2;              // stages in the LDS ring
@@ -159,13 +205,16 @@ constexpr int CPR = BK / 8;         // 16-byte chunks per such row
 constexpr int TILE_BYTES = GBM * ROWB;  // one operand tile (the NN W tile is BK x 512 B, same size)
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr int LPW = BK / 8;         // 1-KiB direct-to-LDS loads per wave per operand per stage
-// XOR swizzle of 16-byte chunks: conflict-free 16-lane b128 reads of 16
-// consecutive rows (K-contiguous tiles) and 32-lane transposing b64 reads of
-// 4 consecutive k-rows (the NN W tile, 32 chunks per row).
-__device__ __forceinline__ int swz_rows(int r) {
-    return CPR == 8 ? (((r >> 1) & 7) ^ ((r & 1) << 2)) : ((r >> 2) & 3);
-}
-__device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
+constexpr int NDMA = 2 * LPW;       // DMA instructions per wave per stage
+constexpr int NT16 = 8;             // 16 x 16 MFMA tiles per wave side
+
+// XOR swizzle of the 16-byte chunks of a 128-byte row: 16 consecutive rows
+// read at one chunk position land on 16 distinct chunks of a 256-byte bank window.
+__device__ __forceinline__ int swz_rows(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+// W tile (512-byte k-rows): k-rows {0..3, 8..11} (mod 16) get 8 distinct even
+// chunk offsets, so the 8 rows x 32 bytes of a half-wave transposing read are
+// conflict-free.
+__device__ __forceinline__ int swz_w(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
 
 template <bool NN, int EPI, bool MULTI>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
@@ -179,15 +228,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wm = wave >> 1, wn = wave & 1;
-    const int l32 = lane & 31, lhi = lane >> 5;
+    const int l16 = lane & 15, lg = lane >> 4;
 
-    f32x16_t acc[4][4];
+    f32x4_t acc[NT16][NT16];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < NT16; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+        for (int b = 0; b < NT16; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const size_t K2 = (size_t)P.K * 2, N2 = (size_t)P.N * 2;
     auto clamp_bytes = [](uint64_t v) { return (uint32_t)(v < 0x7FFFFFF0ull ? v : 0x7FFFFFF0ull); };
@@ -218,76 +265,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         }
     }
 
-    auto issue_loads = [&](int k0, int stage) {
-        const uint32_t sa = smem_lds + stage * STAGE_BYTES + wave * LPW * 1024;
-        const uint32_t sb = sa + TILE_BYTES;
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const uint32_t off = (k0 + colK[j] < P.K) ? offK[j] + (uint32_t)(k0 * 2) : kOOB;
-            dma16(dA, off, sa + j * 1024);
-        }
-        if (NN) {
-            const int kk = min(k0, P.K);
-            const uint32_t rows = (uint32_t)min(P.K - kk, (int)nn_maxrows);
-            const sgpr4_t dB = make_desc(P.Bcol + (size_t)kk * P.N, rows * (uint32_t)N2);
-#pragma unroll
-            for (int j = 0; j < LPW; ++j) dma16(dB, offW[j], sb + j * 1024);
-        } else {
-#pragma unroll
-            for (int j = 0; j < LPW; ++j) {
-                const uint32_t off = (k0 + colK[j] < P.K) ? offK[j] + (uint32_t)(k0 * 2) : kOOB;
-                dma16(dBt, off, sb + j * 1024);
-            }
-        }
-    };
-
-    // ---- fragment reads
-    int rowA[4], swA[4], rowB[4], swB[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        rowA[t] = wm * 128 + t * 32 + l32;
-        swA[t] = swz_rows(rowA[t]);
-        rowB[t] = wn * 128 + t * 32 + l32;
-        swB[t] = swz_rows(rowB[t]);
-    }
-    // NN transposing reads: lane = 16*G + a; source row k = 8*(G>>1) + (a>>2) (+4),
-    // chunk (col base)/8 + ((a&3)>>1), byte (a&1)*8 inside the chunk
-    const int trG = lane >> 4, tra = lane & 15;
-    const int tr_k = 8 * (trG >> 1) + (tra >> 2);
-    const int tr_c = (wn * 128 + (trG & 1) * 16) / 8 + ((tra & 3) >> 1);
-    const int tr_b = (tra & 1) * 8;
-
-    uint4 af[2][4], bf[2][4];
-    // One fragment (t-th of the row side if which == 0, of the column side if
-    // which == 1) of sub-step ks from LDS stage `stage` into register slot `slot`.
-    auto read_frag = [&](int stage, int ks, int slot, int which, int t) {
-        const char *sa = smem + stage * STAGE_BYTES;
-        const char *sb = sa + TILE_BYTES;
-        const int c = 2 * ks + lhi;
-        if (which == 0) {
-            af[slot][t] = *(const uint4 *)(sa + rowA[t] * ROWB + ((c ^ swA[t]) << 4));
-        } else if (NN) {
-            const int k = ks * 16 + tr_k;
-            const int ch = tr_c + 4 * t;
-            const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s_t *)((lds_char *)sb + k * 512 + ((ch ^ swz_w(k)) << 4) + tr_b));
-            const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s_t *)((lds_char *)sb + (k + 4) * 512 + ((ch ^ swz_w(k + 4)) << 4) + tr_b));
-            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-            bf[slot][t] = make_uint4(l2.x, l2.y, h2.x, h2.y);
-        } else {
-            bf[slot][t] = *(const uint4 *)(sb + rowB[t] * ROWB + ((c ^ swB[t]) << 4));
-        }
-    };
-    auto read_frags = [&](int stage, int ks, int slot) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            read_frag(stage, ks, slot, 0, t);
-            read_frag(stage, ks, slot, 1, t);
-        }
-    };
-
-    // DMA of one operand tile slice: load j (0..2*LPW-1) of tile k0 into `stage`
+    // DMA load j (0..NDMA-1) of the stage starting at k0 into LDS stage `stage`
     auto dma_one = [&](int k0, int stage, int j) {
         const uint32_t sa = smem_lds + stage * STAGE_BYTES + wave * LPW * 1024;
         if (j < LPW) {
@@ -308,59 +286,112 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         }
     };
 
-    constexpr int KS = BK / 16;
-    constexpr int NDMA = 2 * LPW;                 // DMA instructions per wave per tile
-    constexpr int INFLIGHT = (NST - 2) * NDMA;    // loads allowed outstanding at a stage switch
-    // 16 MFMAs of slot `sl`; MFMA i is followed by the i-th item of the side
-    // work: fragment reads of (rstage, rks) into slot `rsl` for i < 8 and DMA
-    // loads d0 + i/2 (every other MFMA) while they last.
-    auto mfma_group = [&](int sl, bool do_read, int rstage, int rks, int rsl, int dk0, int dstage, int d0, int dn) {
+    // ---- fragment reads.  Row side: 16 rows x 32 K per tile, lane l reads row
+    // l%16 of the tile, K chunk 4*ks + l/16; swz_rows of the row depends only
+    // on l%16, so tile t is at a fixed 2048-byte stride.  Column side (nt): the
+    // same on the B tile.
+    const int swl = swz_rows(l16);
+    int rdA[2], rdB[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tm = i >> 2, tn = i & 3;
-            acc[tm][tn] = mfma32x32x16(bf[sl][tn], af[sl][tm], acc[tm][tn]);
-            if (do_read && i < 8) read_frag(rstage, rks, rsl, i >> 2, i & 3);
-            if ((i & 1) == 0 && (i >> 1) < dn) dma_one(dk0, dstage, d0 + (i >> 1));
-            __builtin_amdgcn_sched_barrier(0);
+    for (int ks = 0; ks < 2; ++ks) {
+        rdA[ks] = (wm * 128 + l16) * ROWB + (((4 * ks + lg) ^ swl) << 4);
+        rdB[ks] = TILE_BYTES + (wn * 128 + l16) * ROWB + (((4 * ks + lg) ^ swl) << 4);
+    }
+    // NN transposing reads: within 16-lane group g (K slots 8g..8g+7) source
+    // lane s points at k-row 8g + s/4 (+4 for the second read), columns
+    // colbase + 4*(s%4) .. +3, so output lane s gets column colbase + s.  The
+    // swizzle of those k-rows depends only on the lane, so each tile t has one
+    // address; +4 rows is +2048 bytes and the second K step +16384.
+    int rdW[NT16];
+    if (NN) {
+        const int tr_k = 8 * lg + (l16 >> 2);
+        const int sww = swz_w(tr_k);
+#pragma unroll
+        for (int t = 0; t < NT16; ++t) {
+            const int ch = (wn * 128 + t * 16) / 8 + ((l16 & 3) >> 1);
+            rdW[t] = TILE_BYTES + tr_k * 512 + ((ch ^ sww) << 4) + (l16 & 1) * 8;
+        }
+    }
+
+    uint4 af[2][NT16], bf[2][NT16];
+    // the `which`-side fragment t of step ks (0/1) of LDS stage `stage` into slot `slot`
+    auto read_frag = [&](int stage, int ks, int slot, int which, int t) {
+        const char *base = smem + stage * STAGE_BYTES;
+        if (which == 0) {
+            af[slot][t] = *(const uint4 *)(base + rdA[ks] + t * 2048);
+        } else if (NN) {
+            const lds_char *p = (const lds_char *)base + rdW[t] + ks * 16384;
+            const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t *)p);
+            const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t *)(p + 2048));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            bf[slot][t] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+        } else {
+            bf[slot][t] = *(const uint4 *)(base + rdB[ks] + t * 2048);
         }
     };
 
+    // 64 MFMAs of fragment slot `sl`; MFMA i is followed by side work: for
+    // i % 4 == 0 the fragment read i/4 of (rstage, rks) into slot rsl, and for
+    // i % 4 == 2 the DMA load i/4 of the stage at dk0 into dstage.  READ and
+    // DMA are compile-time flags so the MFMA stream carries no branches.
+    auto mfma_step = [&](int sl, auto read_c, int rstage, int rks, int rsl, auto dma_c, int dk0, int dstage) {
+        constexpr bool READ = decltype(read_c)::value, DMA = decltype(dma_c)::value;
+#pragma unroll
+        for (int i = 0; i < NT16 * NT16; ++i) {
+            const int tm = i >> 3, tn = i & 7;
+            mfma16x16x32_inplace(acc[tm][tn], bf[sl][tn], af[sl][tm]);
+            if constexpr (READ) {
+                if ((i & 3) == 0) read_frag(rstage, rks, rsl, (i >> 2) & 1, i >> 3);
+            }
+            if constexpr (DMA) {
+                if ((i & 3) == 2) dma_one(dk0, dstage, i >> 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+
     const int nk = (P.K + BK - 1) / BK;
+    // prologue: stages 0 and 1 in flight, wait for stage 0
 #pragma unroll
-    for (int st = 0; st < NST - 1; ++st)
+    for (int j = 0; j < NDMA; ++j) dma_one(0, 0, j);
 #pragma unroll
-        for (int j = 0; j < NDMA; ++j) dma_one(st * BK, st, j);
-    wait_vmcnt<INFLIGHT>();
-    __syncthreads();
-    read_frags(0, 0, 0);
-    int stage = 0, lstage = NST - 1;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int kload = (kt + NST - 1) * BK;
-        // sub-steps 0..KS-2: MFMAs of ks with reads of ks+1; the tile's DMA
-        // loads are spread over the first sub-steps (8 per sub-step)
+    for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j);
+    wait_vmcnt<NDMA>();
+    asm volatile("" ::: "memory");  // keep the LDS reads below the barrier
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
-        for (int ks = 0; ks < KS - 1; ++ks) {
-            const int d0 = ks * 8;
-            const int dn = d0 < NDMA ? min(8, NDMA - d0) : 0;
-            mfma_group(ks & 1, true, stage, ks + 1, (ks + 1) & 1, kload, lstage, d0, dn);
-        }
-        if ((KS - 1) * 8 < NDMA) {
-#pragma unroll
-            for (int j = (KS - 1) * 8; j < NDMA; ++j) dma_one(kload, lstage, j);
-        }
-        wait_vmcnt<INFLIGHT>();
-        __syncthreads();
-        stage = stage + 1 == NST ? 0 : stage + 1;
-        lstage = lstage + 1 == NST ? 0 : lstage + 1;
-        // last sub-step after the barrier, overlapping the next tile's first reads
-        mfma_group((KS - 1) & 1, kt + 1 < nk, stage, 0, 0, 0, 0, 0, 0);
+    for (int t = 0; t < NT16; ++t) {
+        read_frag(0, 0, 0, 0, t);
+        read_frag(0, 0, 0, 1, t);
     }
+    // One stage: step 0 (reads of its step 1), then -- once stage kt+1 has
+    // landed everywhere and stage kt's buffer is no longer read -- step 1 with
+    // the reads of step 0 of stage kt+1 and the loads of stage kt+2 into the
+    // buffer stage kt released.  The last two stages drop the loads / reads.
+    auto stage_body = [&](int kt, auto read_next, auto load_next2) {
+        const int stage = kt & 1;
+        mfma_step(0, T_{}, stage, 1, 1, F_{}, 0, 0);
+        wait_vmcnt<0>();
+        __syncthreads();
+        mfma_step(1, read_next, stage ^ 1, 0, 0, load_next2, (kt + 2) * BK, stage);
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) stage_body(kt, T_{}, T_{});
+    if (kt + 1 < nk) stage_body(kt++, T_{}, F_{});
+    if (kt < nk) stage_body(kt, F_{}, F_{});
+    mfma_drain();
     wait_vmcnt<0>();
 
     const int wrow0 = m0 + wm * 128;  // first row of this wave
     const int wcol0 = n0 + wn * 128;  // first column of this wave
 
     // ---- F2: alpha * S * B accumulated into acc
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(P.Sx + (size_t)min(wrow0, P.M) * P.RS,
+                                                (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.RS * 4u);
+    const bool svec = (P.RS & 7) == 0 && (((uintptr_t)P.Sx) & 15) == 0;
     if (EPI == 1) {
         int s_begin = 0, s_end = 1;
         if (MULTI) {
@@ -372,84 +403,109 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             ExtItem it;
             if (!get_item<EPI, MULTI>(P, s, it)) continue;
             if (it.hi <= wrow0 || it.lo >= wrow0 + 128) continue;
-            for (int rr0 = 0; rr0 < it.r; rr0 += 16) {
-                uint4 cf[4];
+            const bool rvec = svec && (it.r & 7) == 0;
+            const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it, wcol0);
+            for (int rr0 = 0; rr0 < it.r; rr0 += 32) {
+                uint4 cf[NT16];
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn) cf[tn] = col_ext_frag<EPI>(P, it, wcol0 + tn * 32 + l32, rr0, lane);
+                for (int tn = 0; tn < NT16; ++tn) cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, rr0, lane, false);
 #pragma unroll
-                for (int tm = 0; tm < 4; ++tm) {
+                for (int tm = 0; tm < NT16; ++tm) {
                     uint4 hi, lo;
-                    row_ext_frags(P, it, wrow0 + tm * 32 + l32, rr0, lane, hi, lo);
+                    row_ext_frags(P, rS, wrow0, it, wrow0 + tm * 16 + l16, rr0, lane, rvec, hi, lo);
 #pragma unroll
-                    for (int tn = 0; tn < 4; ++tn) {
-                        acc[tm][tn] = mfma32x32x16(cf[tn], hi, acc[tm][tn]);
-                        acc[tm][tn] = mfma32x32x16(cf[tn], lo, acc[tm][tn]);
+                    for (int tn = 0; tn < NT16; ++tn) {
+                        acc[tm][tn] = mfma16x16x32(cf[tn], hi, acc[tm][tn]);
+                        acc[tm][tn] = mfma16x16x32(cf[tn], lo, acc[tm][tn]);
                     }
                 }
             }
         }
     }
 
-    // ---- output (B3 adds the masked rank-deep term one 32-row band at a time)
+    // ---- B3, single adapter with r <= 32: the column-side A fragments are
+    // the same for every 16-row band, loaded once
+    uint4 cf1[NT16];
+    bool one_chunk = false;
+    ExtItem it1;
+    bool rvec1 = false;
+    if (EPI == 2 && !MULTI) {
+        get_item<EPI, MULTI>(P, 0, it1);
+        one_chunk = it1.r <= 32;
+        rvec1 = svec && (it1.r & 7) == 0;
+        if (one_chunk) {
+            const bool avec = (it1.r & 7) == 0 && (((uintptr_t)it1.w) & 15) == 0;
+            const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it1, wcol0);
+#pragma unroll
+            for (int tn = 0; tn < NT16; ++tn) cf1[tn] = col_ext_frag<EPI>(P, rW, wcol0, it1, wcol0 + tn * 16 + l16, 0, lane, avec);
+        }
+    }
+
+    // ---- output (B3 adds the masked rank-deep term one 16-row band at a time)
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(P.C + (size_t)m0 * P.N, (size_t)(P.M - m0) * N2);
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        const int row = wrow0 + tm * 32 + l32;
-        f32x16_t acc2[4];
+    for (int tm = 0; tm < NT16; ++tm) {
+        const int row = wrow0 + tm * 16 + l16;
+        f32x4_t acc2[NT16];
         if (EPI == 2) {
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn)
+            for (int tn = 0; tn < NT16; ++tn) acc2[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (!MULTI && one_chunk) {
+                uint4 hi, lo;
+                row_ext_frags(P, rS, wrow0, it1, row, 0, lane, rvec1, hi, lo);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc2[tn][v] = 0.f;
-            const int band0 = wrow0 + tm * 32;
-            int s_begin = 0, s_end = 1;
-            if (MULTI) {
-                s_begin = first_segment(P, band0);
-                s_end = P.nseg;
-            }
-            for (int s = s_begin; s < s_end; ++s) {
-                if (MULTI && P.seg_off[s] >= (int64_t)(band0 + 32)) break;
-                ExtItem it;
-                if (!get_item<EPI, MULTI>(P, s, it)) continue;
-                if (it.hi <= band0 || it.lo >= band0 + 32) continue;
-                for (int rr0 = 0; rr0 < it.r; rr0 += 16) {
-                    uint4 hi, lo;
-                    row_ext_frags(P, it, row, rr0, lane, hi, lo);
+                for (int tn = 0; tn < NT16; ++tn) {
+                    acc2[tn] = mfma16x16x32(cf1[tn], hi, acc2[tn]);
+                    acc2[tn] = mfma16x16x32(cf1[tn], lo, acc2[tn]);
+                }
+            } else {
+                const int band0 = wrow0 + tm * 16;
+                int s_begin = 0, s_end = 1;
+                if (MULTI) {
+                    s_begin = first_segment(P, band0);
+                    s_end = P.nseg;
+                }
+                for (int s = s_begin; s < s_end; ++s) {
+                    if (MULTI && P.seg_off[s] >= (int64_t)(band0 + 16)) break;
+                    ExtItem it;
+                    if (!get_item<EPI, MULTI>(P, s, it)) continue;
+                    if (it.hi <= band0 || it.lo >= band0 + 16) continue;
+                    const bool rvec = svec && (it.r & 7) == 0;
+                    const bool avec = (it.r & 7) == 0 && (((uintptr_t)it.w) & 15) == 0;
+                    const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it, wcol0);
+                    for (int rr0 = 0; rr0 < it.r; rr0 += 32) {
+                        uint4 hi, lo;
+                        row_ext_frags(P, rS, wrow0, it, row, rr0, lane, rvec, hi, lo);
 #pragma unroll
-                    for (int tn = 0; tn < 4; ++tn) {
-                        const uint4 cf = col_ext_frag<EPI>(P, it, wcol0 + tn * 32 + l32, rr0, lane);
-                        acc2[tn] = mfma32x32x16(cf, hi, acc2[tn]);
-                        acc2[tn] = mfma32x32x16(cf, lo, acc2[tn]);
+                        for (int tn = 0; tn < NT16; ++tn) {
+                            const uint4 cf = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, rr0, lane, avec);
+                            acc2[tn] = mfma16x16x32(cf, hi, acc2[tn]);
+                            acc2[tn] = mfma16x16x32(cf, lo, acc2[tn]);
+                        }
                     }
                 }
             }
         }
         if (row < P.M) {
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-                const int tcol = wcol0 + tn * 32;
-                if (tcol >= P.N) continue;
+            for (int tn = 0; tn < NT16; ++tn) {
+                const int col = wcol0 + tn * 16 + 4 * lg;
+                if (col >= P.N) continue;
                 uint32_t kw = 0xFFFFFFFFu;
-                if (EPI == 2 && P.keep != nullptr) kw = P.keep[(size_t)row * P.KW + (tcol >> 5)];
+                if (EPI == 2 && P.keep != nullptr) kw = P.keep[(size_t)row * P.KW + (col >> 5)] >> (col & 31);
+                uint32_t h[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int cofs = 8 * q + 4 * lhi;
-                    const int col = tcol + cofs;
-                    if (col >= P.N) continue;
-                    uint32_t h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float v = acc[tm][tn][4 * q + e];
-                        if (EPI == 2) {
-                            if ((kw >> (cofs + e)) & 1u) v += acc2[tn][4 * q + e];
-                        }
-                        h[e] = f32_to_bf16_rne(v);
+                for (int e = 0; e < 4; ++e) {
+                    float v = acc[tm][tn][e];
+                    if (EPI == 2) {
+                        if ((kw >> e) & 1u) v += acc2[tn][e];
                     }
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                                           make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]))),
-                        rC, (uint32_t)((size_t)(row - m0) * N2 + (size_t)col * 2), 0, 0);
+                    h[e] = f32_to_bf16_rne(v);
                 }
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                       make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]))),
+                    rC, (uint32_t)((size_t)(row - m0) * N2 + (size_t)col * 2), 0, 0);
             }
         }
     }

@@ -77,6 +77,7 @@ def _fwd(lib, **kw):
     (dict(keep=None), INVALID),           # keep_bits required when p > 0
     (dict(S=FAKE + 2), INVALID),          # S 4-byte aligned
     (dict(m=512, k=4096, wsb=0), WORKSPACE),  # needs split-k partials
+    (dict(r=256, n=1 << 22), UNSUPPORTED),    # B of 256 x 2^22 bf16 = 2 GiB
 ])
 def test_fwd_rejects(lib, kw, status):
     assert _fwd(lib, **kw) == status
