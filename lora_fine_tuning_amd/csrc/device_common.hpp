@@ -64,6 +64,16 @@ __device__ __forceinline__ void mfma16x16x32_inplace(f32x4_t &acc, const uint4 &
 // Wait states after the last in-place MFMA before its result is read by any
 // other instruction (a 16x16x32 MFMA needs at most 11; this gives 32).
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
+// Wait states between VALU writes of two source operands and the in-place
+// MFMAs that read them (16; the compiler inserts none before inline asm).
+// The operands pass through the asm so their producers stay above it.
+__device__ __forceinline__ void mfma_src_ready(uint4 &a, uint4 &b) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    i32x4_t x = __builtin_bit_cast(i32x4_t, a), y = __builtin_bit_cast(i32x4_t, b);
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+    a = __builtin_bit_cast(uint4, x);
+    b = __builtin_bit_cast(uint4, y);
+}
 
 // Eight fp32 values -> hi and lo bf16 fragments.
 __device__ __forceinline__ void split_frag(const float v[8], uint4 &hi, uint4 &lo) {

@@ -216,7 +216,10 @@ __device__ __forceinline__ int swz_rows(int r) { return ((r >> 1) & 7) ^ ((r & 1
 // conflict-free.
 __device__ __forceinline__ int swz_w(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
 
-template <bool NN, int EPI, bool MULTI>
+// FAST (single adapter, r <= 32 and a multiple of 8, 16-byte aligned S / dS
+// and rank-side matrix; chosen by the host): the epilogue issues all its loads
+// up front.  Kept as its own instantiation so no kernel merges two epilogues.
+template <bool NN, int EPI, bool MULTI, bool FAST>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     extern __shared__ uint4 gemm_smem[];
     char *smem = (char *)gemm_smem;
@@ -388,10 +391,142 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     const int wrow0 = m0 + wm * 128;  // first row of this wave
     const int wcol0 = n0 + wn * 128;  // first column of this wave
 
-    // ---- F2: alpha * S * B accumulated into acc
     const __amdgpu_buffer_rsrc_t rS = make_rsrc(P.Sx + (size_t)min(wrow0, P.M) * P.RS,
                                                 (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.RS * 4u);
     const bool svec = (P.RS & 7) == 0 && (((uintptr_t)P.Sx) & 15) == 0;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(P.C + (size_t)m0 * P.N, (size_t)(P.M - m0) * N2);
+
+    // ---- single adapter, r <= 32, aligned rank-side operands: every epilogue
+    // load (the column-side fragments, the wave's 128 rows of S / dS and, for
+    // B3, its keep words) is issued before any of them is used, so their
+    // latencies overlap instead of adding up band by band.
+    if constexpr (FAST && EPI != 0 && !MULTI) {
+        ExtItem it;
+        get_item<EPI, MULTI>(P, 0, it);
+        {
+            const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it, wcol0);
+            uint4 cf[NT16];
+            if (EPI == 2) {
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, 0, lane, true);
+            } else {
+                // B[0..32) x [wcol0, wcol0+128) through this wave's 8 KiB of the
+                // (now idle) LDS: 16-byte loads of 256-byte rows (ranks >= r and
+                // columns >= N zero), then transposing reads give each lane 8
+                // consecutive ranks of one column.  Every wave passed the K
+                // loop's last barrier after its last LDS read and DMA.
+                lds_char *bs = (lds_char *)smem + wave * 8192;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int q = lane + 64 * j, rr = q >> 4, c = q & 15;
+                    const uint32_t off = (rr < it.r && wcol0 + 8 * c < P.N) ? ((uint32_t)rr * (uint32_t)P.N + 8u * c) * 2u : kOOB;
+                    const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
+                    *(uint4 *)(bs + rr * 256 + ((c ^ swz_w(rr)) << 4)) = v;
+                }
+                const int kr = 8 * lg + (l16 >> 2);
+                const int swr = swz_w(kr);
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) {
+                    const int ch = 2 * tn + ((l16 & 3) >> 1);
+                    const lds_char *pp = bs + kr * 256 + ((ch ^ swr) << 4) + (l16 & 1) * 8;
+                    const uint2 lo = lds_read_tr4(pp), hi = lds_read_tr4(pp + 1024);
+                    cf[tn] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+#pragma unroll
+                for (int tn = 0; tn < NT16; tn += 2) mfma_src_ready(cf[tn], cf[tn + 1]);
+            }
+            const int rb = 8 * lg;
+            float4 sv[NT16][2];
+#pragma unroll
+            for (int tm = 0; tm < NT16; ++tm) {
+                const int row = wrow0 + tm * 16 + l16;
+                const uint32_t off = (row < P.M && rb < it.r) ? (uint32_t)((tm * 16 + l16) * P.RS + rb) * 4u : kOOB;
+                sv[tm][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off, 0, 0));
+                sv[tm][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off == kOOB ? kOOB : off + 16, 0, 0));
+            }
+            uint32_t kwv[NT16][NT16 / 2];
+            if (EPI == 2) {
+                const bool has_keep = P.keep != nullptr;
+                const __amdgpu_buffer_rsrc_t rK = make_rsrc(has_keep ? P.keep + (size_t)min(wrow0, P.M) * P.KW : P.keep,
+                                                            has_keep ? (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.KW * 4u : 0u);
+#pragma unroll
+                for (int tm = 0; tm < NT16; ++tm)
+#pragma unroll
+                    for (int q = 0; q < NT16 / 2; ++q) {
+                        const int col = wcol0 + q * 32;
+                        const uint32_t off = (has_keep && col < P.N) ? (uint32_t)((tm * 16 + l16) * P.KW + (col >> 5)) * 4u : kOOB;
+                        kwv[tm][q] = has_keep ? __builtin_amdgcn_raw_buffer_load_b32(rK, off, 0, 0) : 0xFFFFFFFFu;
+                    }
+            }
+#pragma unroll
+            for (int tm = 0; tm < NT16; ++tm) {
+                float v[8] = {sv[tm][0].x, sv[tm][0].y, sv[tm][0].z, sv[tm][0].w,
+                              sv[tm][1].x, sv[tm][1].y, sv[tm][1].z, sv[tm][1].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] *= it.scale;
+                uint4 hi, lo;
+                split_frag(v, hi, lo);
+                if (EPI == 1) {
+                    mfma_src_ready(hi, lo);
+#pragma unroll
+                    for (int tn = 0; tn < NT16; ++tn) {
+                        mfma16x16x32_inplace(acc[tm][tn], cf[tn], hi);
+                        mfma16x16x32_inplace(acc[tm][tn], cf[tn], lo);
+                    }
+                } else {
+                    f32x4_t acc2[NT16];
+#pragma unroll
+                    for (int tn = 0; tn < NT16; ++tn) {
+                        acc2[tn] = mfma16x16x32(cf[tn], hi, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                        acc2[tn] = mfma16x16x32(cf[tn], lo, acc2[tn]);
+                    }
+                    const int row = wrow0 + tm * 16 + l16;
+                    if (row < P.M) {
+#pragma unroll
+                        for (int tn = 0; tn < NT16; ++tn) {
+                            const int col = wcol0 + tn * 16 + 4 * lg;
+                            if (col >= P.N) continue;
+                            const uint32_t kw = kwv[tm][tn >> 1] >> (col & 31);
+                            uint32_t h[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float x = acc[tm][tn][e];
+                                if ((kw >> e) & 1u) x += acc2[tn][e];
+                                h[e] = f32_to_bf16_rne(x);
+                            }
+                            __builtin_amdgcn_raw_buffer_store_b64(
+                                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                                   make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]))),
+                                rC, (uint32_t)((size_t)(row - m0) * N2 + (size_t)col * 2), 0, 0);
+                        }
+                    }
+                }
+            }
+            if (EPI == 1) {
+                mfma_drain();
+#pragma unroll
+                for (int tm = 0; tm < NT16; ++tm) {
+                    const int row = wrow0 + tm * 16 + l16;
+                    if (row >= P.M) continue;
+#pragma unroll
+                    for (int tn = 0; tn < NT16; ++tn) {
+                        const int col = wcol0 + tn * 16 + 4 * lg;
+                        if (col >= P.N) continue;
+                        uint32_t h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16_rne(acc[tm][tn][e]);
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                               make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]))),
+                            rC, (uint32_t)((size_t)(row - m0) * N2 + (size_t)col * 2), 0, 0);
+                    }
+                }
+            }
+        }
+        return;
+    } else {
+
+    // ---- F2 (general path): alpha * S * B accumulated into acc
     if (EPI == 1) {
         int s_begin = 0, s_end = 1;
         if (MULTI) {
@@ -410,17 +545,21 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, rr0, lane, false);
 #pragma unroll
+                for (int tn = 0; tn < NT16; tn += 2) mfma_src_ready(cf[tn], cf[tn + 1]);
+#pragma unroll
                 for (int tm = 0; tm < NT16; ++tm) {
                     uint4 hi, lo;
                     row_ext_frags(P, rS, wrow0, it, wrow0 + tm * 16 + l16, rr0, lane, rvec, hi, lo);
+                    mfma_src_ready(hi, lo);
 #pragma unroll
                     for (int tn = 0; tn < NT16; ++tn) {
-                        acc[tm][tn] = mfma16x16x32(cf[tn], hi, acc[tm][tn]);
-                        acc[tm][tn] = mfma16x16x32(cf[tn], lo, acc[tm][tn]);
+                        mfma16x16x32_inplace(acc[tm][tn], cf[tn], hi);
+                        mfma16x16x32_inplace(acc[tm][tn], cf[tn], lo);
                     }
                 }
             }
         }
+        mfma_drain();
     }
 
     // ---- B3, single adapter with r <= 32: the column-side A fragments are
@@ -442,7 +581,6 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     }
 
     // ---- output (B3 adds the masked rank-deep term one 16-row band at a time)
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(P.C + (size_t)m0 * P.N, (size_t)(P.M - m0) * N2);
 #pragma unroll
     for (int tm = 0; tm < NT16; ++tm) {
         const int row = wrow0 + tm * 16 + l16;
@@ -509,24 +647,25 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             }
         }
     }
+    }  // general epilogue
 }
 
 size_t gemm_lds_bytes() { return (size_t)NST * STAGE_BYTES; }
 
-template <bool NN, int EPI, bool MULTI>
+template <bool NN, int EPI, bool MULTI, bool FAST>
 static hipError_t launch_gemm_t(const GemmParams &P, hipStream_t stream, const char *name) {
     const size_t lds = gemm_lds_bytes();
     const int G = P.tiles_m * P.tiles_n;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<NN, EPI, MULTI>,
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<NN, EPI, MULTI, FAST>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     (void)hipGetLastError();
     const int slot = prof_begin(name, stream);
-    hipLaunchKernelGGL((gemm_kernel<NN, EPI, MULTI>), dim3(G), dim3(256), lds, stream, P);
+    hipLaunchKernelGGL((gemm_kernel<NN, EPI, MULTI, FAST>), dim3(G), dim3(256), lds, stream, P);
     hipError_t e = hipGetLastError();
     prof_end(slot, stream);
     return e;
@@ -559,14 +698,19 @@ hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, voi
     P.nseg = src.num_segments;
     if (P.tiles_m == 0 || P.tiles_n == 0) return hipSuccess;
     const bool multi = src.table != nullptr;
+    auto al16 = [](const void *q) { return ((uintptr_t)q & 15) == 0; };
+    const bool fast = !multi && epi != 0 && P.ext_r <= 32 && (P.ext_r & 7) == 0 && (RS & 7) == 0 &&
+                      al16(Sx) && al16(P.ext);
     if (nn) {
-        if (epi == 0) return launch_gemm_t<true, 0, false>(P, stream, "gemm_frozen_fwd");
-        if (epi == 1) return multi ? launch_gemm_t<true, 1, true>(P, stream, "gemm_f2_fwd_lora")
-                                   : launch_gemm_t<true, 1, false>(P, stream, "gemm_f2_fwd_lora");
+        if (epi == 0) return launch_gemm_t<true, 0, false, false>(P, stream, "gemm_frozen_fwd");
+        if (epi == 1) return multi ? launch_gemm_t<true, 1, true, false>(P, stream, "gemm_f2_fwd_lora")
+                             : fast ? launch_gemm_t<true, 1, false, true>(P, stream, "gemm_f2_fwd_lora")
+                                    : launch_gemm_t<true, 1, false, false>(P, stream, "gemm_f2_fwd_lora");
     } else {
-        if (epi == 0) return launch_gemm_t<false, 0, false>(P, stream, "gemm_frozen_bwd");
-        if (epi == 2) return multi ? launch_gemm_t<false, 2, true>(P, stream, "gemm_b3_bwd_dx")
-                                   : launch_gemm_t<false, 2, false>(P, stream, "gemm_b3_bwd_dx");
+        if (epi == 0) return launch_gemm_t<false, 0, false, false>(P, stream, "gemm_frozen_bwd");
+        if (epi == 2) return multi ? launch_gemm_t<false, 2, true, false>(P, stream, "gemm_b3_bwd_dx")
+                             : fast ? launch_gemm_t<false, 2, false, true>(P, stream, "gemm_b3_bwd_dx")
+                                    : launch_gemm_t<false, 2, false, false>(P, stream, "gemm_b3_bwd_dx");
     }
     return hipErrorInvalidValue;
 }

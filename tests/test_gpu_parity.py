@@ -51,6 +51,9 @@ SINGLE_CASES = [
     (130, 1024, 256, 128, 2.0, 0.2),
     (96, 256, 264, 256, 2.0, 0.1),     # largest rank
     (8, 8, 8, 3, 1.0, 0.25),           # tiny
+    (300, 264, 136, 8, 2.0, 0.1),      # all-loads-first epilogue, ragged m and n
+    (257, 512, 520, 24, 1.5, 0.3),     # same epilogue, rank 24
+    (1000, 1024, 776, 32, 2.0, 0.0),   # same epilogue, rank 32, no dropout
 ]
 
 
