@@ -209,8 +209,10 @@ struct FwdPlan {
     size_t bytes;
 };
 
-// F1 splits k into KS slices (multiples of its 128-column staging slice) so
-// the grid has about 1024 work-groups; partials are summed by a second pass.
+// For ranks up to 32 F1 covers all of k inside each work-group (KS = 1).
+// Larger ranks split k into KS slices (multiples of its 128-column staging
+// slice) so the grid has about 1024 work-groups; partials are summed by a
+// second pass.
 FwdPlan plan_fwd(int64_t m, int64_t k, int32_t RS, bool multi, int32_t nseg) {
     FwdPlan p{};
     p.RS = RS;
@@ -218,6 +220,7 @@ FwdPlan plan_fwd(int64_t m, int64_t k, int32_t RS, bool multi, int32_t nseg) {
     p.chunk_cap_bwd = cdiv(m, kBwdRows) + (multi ? nseg : 0);
     const int kslices = cdiv(k, kF1KSub);
     int KS = std::max(1, std::min(kslices, cdiv(1024, std::max(1, p.chunk_cap_f1))));
+    if (f1_streaming(((RS + 15) / 16) * 16, k)) KS = 1;
     const int per = cdiv(kslices, KS);
     p.ksl = per * kF1KSub;
     p.KS = cdiv(k, p.ksl);

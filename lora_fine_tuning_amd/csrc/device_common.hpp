@@ -114,22 +114,47 @@ struct PhiloxOut {
     uint32_t w[4];
 };
 
+// a ^ b ^ k in one instruction (gfx950 three-input bit operation, truth
+// table 0x96); k is wave-uniform.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+    uint32_t d;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(d) : "v"(a), "v"(b), "s"(k));
+    return d;
+}
+
 __device__ __forceinline__ PhiloxOut philox10(uint64_t block, uint64_t seed) {
-    uint32_t c0 = (uint32_t)block, c1 = (uint32_t)(block >> 32), c2 = 0u, c3 = 0u;
+    constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
     uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-#pragma unroll
-    for (int rnd = 0; rnd < 10; ++rnd) {
-        // one 32x32->64 multiply gives both halves of each product
-        const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
-        const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
-        c0 = n0;
+    // round 1 on (b_lo, b_hi, 0, 0): the word-2 product is zero
+    const uint64_t q0 = (uint64_t)(uint32_t)block * M0;
+    uint32_t c0 = (uint32_t)(block >> 32) ^ k0;
+    uint32_t c1 = 0u;
+    uint32_t c2 = (uint32_t)(q0 >> 32) ^ k1;
+    uint32_t c3 = (uint32_t)q0;
+    k0 += W0;
+    k1 += W1;
+    // round 2: word 1 is zero
+    {
+        const uint64_t p0 = (uint64_t)c0 * M0;
+        const uint64_t p1 = (uint64_t)c2 * M1;
+        c0 = (uint32_t)(p1 >> 32) ^ k0;
+        c2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c1 = (uint32_t)p1;
-        c2 = n2;
         c3 = (uint32_t)p0;
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
+        k0 += W0;
+        k1 += W1;
+    }
+#pragma unroll
+    for (int rnd = 2; rnd < 10; ++rnd) {
+        // one 32x32->64 multiply gives both halves of each product
+        const uint64_t p0 = (uint64_t)c0 * M0;
+        const uint64_t p1 = (uint64_t)c2 * M1;
+        c0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+        c2 = xor3((uint32_t)(p0 >> 32), c3, k1);
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        k0 += W0;
+        k1 += W1;
     }
     PhiloxOut o;
     o.w[0] = c0; o.w[1] = c1; o.w[2] = c2; o.w[3] = c3;
@@ -158,12 +183,53 @@ __device__ __forceinline__ uint4 apply_keep(uint4 v, uint32_t byte) {
     return make_uint4(v.x & m[0], v.y & m[1], v.z & m[2], v.w & m[3]);
 }
 
+// Keep test and masking of 8 bf16 elements in packed 16-bit arithmetic.
+// tm1x2 holds T - 1 in both halves (T >= 1).  For each 16-bit uniform u,
+// saturating u - (T - 1) is nonzero iff u >= T; its minimum with 1 is the
+// keep bit, and multiplying the bf16 bit pattern by it keeps or zeroes the
+// element.  Returns the keep byte (bit e for element e) and the masked x.
+__device__ __forceinline__ uint32_t pk_sub_sat_u16(uint32_t a, uint32_t b) {
+    uint32_t d;
+    asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(d) : "v"(a), "s"(b));
+    return d;
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+    uint32_t d;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ uint32_t pk_mul_lo_u16(uint32_t a, uint32_t b) {
+    uint32_t d;
+    asm("v_pk_mul_lo_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ uint32_t keep_and_mask(const PhiloxOut &o, uint32_t tm1x2, const uint4 &x,
+                                                  uint4 &xm) {
+    const uint32_t one2 = 0x00010001u;
+    uint32_t kq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kq[q] = pk_min_u16(pk_sub_sat_u16(o.w[q], tm1x2), one2);
+    xm = make_uint4(pk_mul_lo_u16(x.x, kq[0]), pk_mul_lo_u16(x.y, kq[1]), pk_mul_lo_u16(x.z, kq[2]),
+                    pk_mul_lo_u16(x.w, kq[3]));
+    // low-half bits land on 0,2,4,6 and high-half bits on 16,18,20,22
+    const uint32_t t = kq[0] | (kq[1] << 2) | (kq[2] << 4) | (kq[3] << 6);
+    return (t & 0x55u) | ((t >> 15) & 0xAAu);
+}
+
 // Dropout threshold and inverted-dropout scale from p (identical arithmetic on
 // every device and the host: T in double, exact for float p in [0, 1)).
 __host__ __device__ __forceinline__ uint32_t drop_threshold(float p) {
     return (uint32_t)((double)p * 65536.0 + 0.5);
 }
 __host__ __device__ __forceinline__ float drop_scale(float p) { return 1.0f / (1.0f - p); }
+
+// Buffer resource over `bytes` bytes from `base`; loads past the end return 0
+// and stores past the end are dropped, so edge tiles need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+    const uint32_t nrec = (uint32_t)(bytes < 0x7FFFFFF0ull ? bytes : 0x7FFFFFF0ull);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nrec, 0x00020000);
+}
+constexpr uint32_t kOOB = 0x80000000u;  // an offset beyond every resource
 
 // ---------------------------------------------------------------------------
 // Direct-to-LDS loads and LDS transposing reads (gfx950)

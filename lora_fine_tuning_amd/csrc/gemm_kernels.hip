@@ -80,13 +80,6 @@ __device__ __forceinline__ void tile_coords(int wg, int G, int tiles_m, int tile
     tn = in / gsz;
 }
 
-// Buffer resource over `bytes` bytes from `base`; loads past the end return 0
-// and stores past the end are dropped, so edge tiles need no branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes) {
-    const uint32_t nrec = (uint32_t)(bytes < 0x7FFFFFF0ull ? bytes : 0x7FFFFFF0ull);
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nrec, 0x00020000);
-}
-constexpr uint32_t kOOB = 0x80000000u;  // an offset beyond every resource
 
 // One item of the LoRA epilogue: rows [lo, hi) with one adapter.
 struct ExtItem {

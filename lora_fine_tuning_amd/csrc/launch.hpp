@@ -16,6 +16,10 @@ constexpr int kF1Rows = 64;    // mask + down-projection
 constexpr int kBwdRows = 256;  // dS/dB and dA kernels
 constexpr int kF1KSub = 128;   // k columns per staged slice of A in F1
 
+// F1's streaming form (each work-group covers all of k, no partial sums)
+// serves ranks up to 32; its 32-bit buffer offsets need 64*k < 2^31.
+inline bool f1_streaming(int r_lds, int64_t k) { return r_lds <= 32 && k * 64 < (int64_t(1) << 31); }
+
 // Kernel timing hooks (api.cpp).  prof_begin returns a slot or -1.
 int prof_begin(const char *name, hipStream_t stream);
 void prof_end(int slot, hipStream_t stream);

@@ -113,10 +113,6 @@ static RowWork make_work(const AdapterSource &src, bool f1) {
 // ===========================================================================
 // F1: dropout mask + down-projection (juhe.plus blog, section 4.1, forward
 // item 1: dropout and X -> S in one kernel so X is read once).
-// Work-group = 4 waves x 16 rows of one chunk, over one k-slice.  Lane l of a
-// wave owns row (l % 16) and the 8 columns 8*(l/16).. of each 32-wide K step:
-// exactly one Philox block and one MFMA A-fragment.  A is staged transposed
-// in LDS (At[rr][kk]) per 128-column slice so its fragments are 16-B reads.
 // ===========================================================================
 struct F1Params {
     const uint16_t *X;
@@ -258,6 +254,176 @@ __global__ __launch_bounds__(256) void f1_kernel(F1Params P) {
             const int orow = row_lo + wave * 16 + 4 * g + v;
             if (orow < row_hi) out[(size_t)orow * P.RS + col] = 0.f;
         }
+    }
+}
+
+// ----- F1 streaming form (ranks <= 32).  Work-group = 16 rows of a chunk
+// over all of k, so S leaves the kernel finished (no split-k partials, no
+// second launch).  Its 8 waves take 8 consecutive ranges of k in 128-column
+// units.  Lane l owns row (l % 16) and columns 8*(l/16) .. +7 of each
+// 32-column step: one Philox block, one keep byte, one MFMA row-side
+// fragment.  Per unit, each wave copies the 128 rows of A it needs (stored
+// k-major, rl bf16 per row) into one of two private LDS slabs and reads its
+// rank-side fragments back with transposing LDS reads; the next unit's A and
+// X loads are in flight while the current unit is hashed, masked and
+// multiplied.  The waves' partial S meet in LDS and are summed in wave order.
+constexpr int F1S_WAVES = 8;
+constexpr int F1S_UNIT = 128;  // k columns per unit (4 MFMA steps)
+
+template <int MAXT>  // rank blocks of 16: rl = 16 * MAXT
+__global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
+    constexpr int RL = 16 * MAXT;
+    constexpr int SLAB = F1S_UNIT * RL * 2;  // bytes of A per unit
+    constexpr int NAV = SLAB / (16 * 64);    // 16-byte A loads per lane per unit
+    extern __shared__ uint4 f1s_smem[];
+    lds_char *smem = (lds_char *)f1s_smem;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+
+    int row_lo, row_hi;
+    AdapterView ad;
+    if (!resolve_chunk(P.work, blockIdx.x >> 2, P.m, row_lo, row_hi, ad)) return;
+    row_lo += 16 * (blockIdx.x & 3);
+    if (row_lo >= row_hi) return;
+    row_hi = min(row_hi, row_lo + 16);
+    const int r = ad.r;
+    const uint32_t T = drop_threshold(ad.p);
+    const uint32_t tm1x2 = ((T - 1u) & 0xFFFFu) * 0x00010001u;  // used only when T >= 1
+    const float s = drop_scale(ad.p);
+
+    // X rows row_lo .. row_hi-1 as one buffer: lanes of missing rows and
+    // columns past the wave's range read zeros (host guarantees 16*k*2 < 2^31)
+    const int nrows = row_hi - row_lo;
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(P.X + (size_t)row_lo * P.k, (size_t)nrows * P.k * 2);
+    const uint32_t xrow_off = (uint32_t)l16 * (uint32_t)P.k * 2u;
+    const int row = row_lo + l16;
+    const bool rvalid = l16 < nrows;
+    // Philox block of the lane's first element in a step starting at column c:
+    // (offset + row*k + c + 8g) / 8, all terms multiples of 8
+    const uint64_t blk0 = (P.offset >> 3) + (uint64_t)(rvalid ? row : row_lo) * (uint64_t)(P.k >> 3) + (uint64_t)g;
+
+    const int kq = ((P.k + F1S_WAVES * F1S_UNIT - 1) / (F1S_WAVES * F1S_UNIT)) * F1S_UNIT;
+    const int kb = wave * kq, ke = min(P.k, kb + kq);
+    const int nu = ke > kb ? (ke - kb + F1S_UNIT - 1) / F1S_UNIT : 0;
+    lds_char *slab0 = smem + wave * 2 * SLAB;
+    const bool avec = r == RL && (((uintptr_t)ad.A) & 15) == 0;
+    // A rows below ke (rows at or past ke read as zero)
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(ad.A, (size_t)max(ke, 0) * RL * 2);
+
+    f32x4_t acc[MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto load_x = [&](int c, uint4 (&xv)[4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c0 = c + 32 * t + 8 * g;
+            const uint32_t off = c0 < ke ? xrow_off + (uint32_t)c0 * 2u : kOOB;
+            xv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
+        }
+    };
+    auto load_a = [&](int c, uint4 (&av)[NAV]) {
+#pragma unroll
+        for (int j = 0; j < NAV; ++j) {
+            const uint32_t off = (uint32_t)c * (RL * 2) + (uint32_t)(lane + 64 * j) * 16u;
+            av[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0));
+        }
+    };
+    auto store_a = [&](lds_char *dst, const uint4 (&av)[NAV]) {
+#pragma unroll
+        for (int j = 0; j < NAV; ++j) *(uint4 *)(dst + (lane + 64 * j) * 16) = av[j];
+    };
+    auto copy_a_generic = [&](int c, lds_char *dst) {
+        for (int q = lane; q < F1S_UNIT * RL; q += 64) {
+            const int kk = q / RL, rr = q % RL;
+            uint16_t v = 0;
+            if (c + kk < ke && rr < r) v = ad.A[(size_t)(c + kk) * r + rr];
+            *(uint16_t *)(dst + q * 2) = v;
+        }
+    };
+
+    // The loads of unit u+1 (A first, then X) are issued at the top of unit
+    // u; storing A(u+1) to LDS at the end of the unit waits for A only, so
+    // X(u+1) can still be in flight.  Units go in pairs so the two X register
+    // sets alternate roles without copies (a copy would wait for its loads);
+    // an odd count gets one extra unit, which reads and adds zeros.
+    uint4 xr0[4], xr1[4], an[NAV];
+    if (nu > 0) {
+        load_x(kb, xr0);
+        if (avec) {
+            load_a(kb, an);
+            store_a(slab0, an);
+        } else {
+            copy_a_generic(kb, slab0);
+        }
+    }
+    auto unit = [&](int u, const uint4 (&xc)[4], uint4 (&xf)[4]) {
+        const int c = kb + u * F1S_UNIT;
+        // next unit's loads (past the range they read zeros)
+        if (avec) load_a(c + F1S_UNIT, an);
+        load_x(c + F1S_UNIT, xf);
+        const lds_char *sl = slab0 + (u & 1) * SLAB;
+        uint32_t kw = 0;  // byte t: this lane's keep bits of step t
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c0 = c + 32 * t + 8 * g;
+            uint4 xm = xc[t];
+            uint32_t byte = 0xFFu;
+            if (T != 0) {
+                const PhiloxOut o = philox10(blk0 + (uint64_t)((c + 32 * t) >> 3), P.seed);
+                byte = keep_and_mask(o, tm1x2, xc[t], xm);
+            }
+            kw |= (c0 < ke ? byte : 0u) << (8 * t);  // bits past k stay zero
+            // rank-side fragment: k rows 32t + 8g + (0..7), rank 16 bt + l16
+            const int kr = 32 * t + 8 * g + (l16 >> 2);
+#pragma unroll
+            for (int bt = 0; bt < MAXT; ++bt) {
+                const lds_char *pa = sl + kr * (2 * RL) + (16 * bt + 4 * (l16 & 3)) * 2;
+                const uint2 lo = lds_read_tr4(pa), hi = lds_read_tr4(pa + 4 * (2 * RL));
+                acc[bt] = mfma16x16x32(xm, make_uint4(lo.x, lo.y, hi.x, hi.y), acc[bt]);
+            }
+        }
+        if (P.keep_bits != nullptr) {
+            // 4x4 byte transpose across the lanes of a row (groups g): byte t of
+            // lane g holds group g's bits of step t; afterwards lane g holds the
+            // word of step g, byte j from group j.
+            const uint32_t p1 = (uint32_t)__shfl_xor((int)kw, 16);
+            kw = (g & 1) ? ((kw & 0xFF00FF00u) | ((p1 & 0xFF00FF00u) >> 8))
+                         : ((kw & 0x00FF00FFu) | ((p1 & 0x00FF00FFu) << 8));
+            const uint32_t p2 = (uint32_t)__shfl_xor((int)kw, 32);
+            kw = (g & 2) ? ((kw & 0xFFFF0000u) | (p2 >> 16)) : ((kw & 0x0000FFFFu) | (p2 << 16));
+            if (rvalid && c + 32 * g < ke) P.keep_bits[(size_t)row * P.KW + ((c >> 5) + g)] = kw;
+        }
+        lds_char *nx = slab0 + ((u + 1) & 1) * SLAB;
+        if (avec) store_a(nx, an);
+        else copy_a_generic(c + F1S_UNIT, nx);
+    };
+    for (int u = 0; u < nu; u += 2) {
+        unit(u, xr0, xr1);
+        unit(u + 1, xr1, xr0);
+    }
+
+    // fixed-order sum of the waves' partial S (rows 4g+v, rank 16bt + l16);
+    // the reduction buffer reuses the slabs once every wave is done with them
+    __syncthreads();
+    float *red = (float *)smem;  // [wave][16 rows][RL]
+#pragma unroll
+    for (int bt = 0; bt < MAXT; ++bt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * g + v) * RL + 16 * bt + l16] = acc[bt][v];
+    __syncthreads();
+    for (int i = tid; i < 16 * P.RS; i += 64 * F1S_WAVES) {
+        const int rr = i / P.RS, cc = i % P.RS;
+        const int orow = row_lo + rr;
+        if (orow >= row_hi) continue;
+        float v = 0.f;
+        if (cc < r) {
+#pragma unroll
+            for (int w = 0; w < F1S_WAVES; ++w) v += red[(w * 16 + rr) * RL + cc];
+            v *= s;
+        }
+        P.out[(size_t)orow * P.RS + cc] = v;
     }
 }
 
@@ -1049,9 +1215,10 @@ static int rank_blocks(int r_lds) {
 }
 
 template <typename Kernel, typename Params>
-static void launch_with_lds(Kernel kernel, dim3 grid, size_t lds, hipStream_t stream, const Params &P) {
+static void launch_with_lds(Kernel kernel, dim3 grid, size_t lds, hipStream_t stream, const Params &P,
+                            int threads = 256) {
     if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(kernel, grid, dim3(256), lds, stream, P);
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), lds, stream, P);
 }
 
 static int r_lds_of(const AdapterSource &src) {
@@ -1079,9 +1246,18 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
     const int slab_cols = std::max(kF1KSub, (20480 / (P.r_lds * 2)) / kF1KSub * kF1KSub);
     P.slab = std::min(ksl, slab_cols);
     const size_t lds = (size_t)P.r_lds * (P.slab + 8) * sizeof(uint16_t);
-    const dim3 grid(chunk_cap, KS);
     (void)hipGetLastError();
     const int slot = prof_begin("f1_mask_down", stream);
+    if (f1_streaming(P.r_lds, k)) {
+        // streaming form: 4 work-groups of 16 rows per chunk, all of k each
+        const dim3 g4(4 * chunk_cap);
+        if (P.r_lds <= 16)
+            launch_with_lds(f1s_kernel<1>, g4, (size_t)F1S_WAVES * 2 * F1S_UNIT * 16 * 2, stream, P, 64 * F1S_WAVES);
+        else
+            launch_with_lds(f1s_kernel<2>, g4, (size_t)F1S_WAVES * 2 * F1S_UNIT * 32 * 2, stream, P, 64 * F1S_WAVES);
+        return finish_launch(slot, stream);
+    }
+    const dim3 grid(chunk_cap, KS);
     switch (rank_blocks(P.r_lds)) {
     case 1: launch_with_lds(f1_kernel<1>, grid, lds, stream, P); break;
     case 2: launch_with_lds(f1_kernel<2>, grid, lds, stream, P); break;
