@@ -240,9 +240,11 @@ struct BwdPlan {
     int RS;
     int chunk_cap_bwd;
     int chunk_cap_f1;
-    int C1, C2, CT;
-    int ds_parts;  // dS partials written by B1 (two per column tile for ranks <= 32)
+    B1Shape b1;
+    int C2;
+    int ds_parts;  // dS partials written by B1 (one per column tile)
     size_t off_ds, off_dspart, off_dbpart, off_dapart, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
+    size_t off_t_b1, off_c_b1;
     size_t bytes;
 };
 
@@ -252,20 +254,21 @@ BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_
     p.chunk_cap_bwd = cdiv(m, kBwdRows) + (multi ? nseg : 0);
     p.chunk_cap_f1 = cdiv(m, kF1Rows) + (multi ? nseg : 0);
     const int rl = ((RS + 15) / 16) * 16;
-    p.C1 = rl <= 128 ? 256 : 128;
+    p.b1 = b1_shape(m, n, rl, multi, nseg);
     p.C2 = rl <= 128 ? 256 : 128;
-    p.CT = cdiv(n, p.C1);
-    p.ds_parts = rl <= 32 ? 2 * p.CT : p.CT;
+    p.ds_parts = p.b1.CT;
     Carve c;
     p.off_ds = c.take((size_t)m * RS * sizeof(float));
     p.off_dspart = c.take(p.ds_parts > 1 ? (size_t)p.ds_parts * m * RS * sizeof(float) : 0);
-    p.off_dbpart = c.take((size_t)p.chunk_cap_bwd * RS * n * sizeof(float));
+    p.off_dbpart = c.take((size_t)p.b1.slots * RS * n * sizeof(float));
     p.off_dapart = c.take((size_t)p.chunk_cap_bwd * k * RS * sizeof(float));
     if (multi) {
         p.off_t_f1 = c.take((size_t)p.chunk_cap_f1 * sizeof(ChunkEntry));
         p.off_c_f1 = c.take(sizeof(int32_t));
         p.off_t_bwd = c.take((size_t)p.chunk_cap_bwd * sizeof(ChunkEntry));
         p.off_c_bwd = c.take(sizeof(int32_t));
+        p.off_t_b1 = c.take((size_t)p.b1.slots * sizeof(ChunkEntry));
+        p.off_c_b1 = c.take(sizeof(int32_t));
     }
     p.bytes = c.off;
     return p;
@@ -375,17 +378,15 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
     float *dBpart = (float *)ws_at(workspace, pl.off_dbpart);
     float *dApart = (float *)ws_at(workspace, pl.off_dapart);
     const int chunks = pl.chunk_cap_bwd;
-    if (m > 0) {
-        HIPCHK(launch_b1(dY, S, (int)m, (int)n, r, src, chunks, pl.C1, dSpart, dBpart, stream), "B1 launch");
-        if (pl.ds_parts > 1)
-            HIPCHK(launch_sum_partials(dSpart, pl.ds_parts, (size_t)m * r, (size_t)m * r, dS, "sum_ds_partials", stream),
-                   "dS reduction launch");
-    }
-    HIPCHK(launch_grad_reduce(0, dBpart, (int)m, (int)k, (int)n, r, src, chunks, stream), "dB reduction launch");
+    if (m > 0) HIPCHK(launch_b1(dY, S, (int)m, (int)n, r, src, pl.b1, dSpart, dBpart, stream), "B1 launch");
+    HIPCHK(launch_b1_reduce(dSpart, m > 0 ? pl.ds_parts : 1, dS, dBpart, (int)m, (int)n, r, src, pl.b1.rows,
+                            pl.b1.slots, stream),
+           "dS/dB reduction launch");
     if (m > 0)
         HIPCHK(launch_b2(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, src, chunks, pl.C2, dApart,
                          stream), "B2 launch");
-    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r, src, chunks, stream), "dA reduction launch");
+    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r, src, kBwdRows, chunks, stream),
+           "dA reduction launch");
     if (m > 0)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r, p == 0.0f ? nullptr : keep_bits,
                            (int)((k + 31) / 32), src, stream), "B3 launch");
@@ -462,7 +463,8 @@ extern "C" lora_status multi_lora_linear_fwd(const void *X, const void *W, const
     src.count_bwd = (const int32_t *)ws_at(workspace, pl.off_c_bwd);
     HIPCHK(launch_router(seg_off, seg_adapter, num_segments, (int)m, adapters, num_adapters, r_max,
                          (ChunkEntry *)src.chunks_f1, (int32_t *)src.count_f1, pl.chunk_cap_f1,
-                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd, stream),
+                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd, nullptr,
+                         nullptr, 0, 0, stream),
            "router launch");
     float *sout = pl.KS > 1 ? (float *)ws_at(workspace, pl.off_spart) : S;
     HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r_max, pl.KS,
@@ -500,25 +502,26 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
     src.count_f1 = (const int32_t *)ws_at(workspace, pl.off_c_f1);
     src.chunks_bwd = (const ChunkEntry *)ws_at(workspace, pl.off_t_bwd);
     src.count_bwd = (const int32_t *)ws_at(workspace, pl.off_c_bwd);
+    src.chunks_b1 = (const ChunkEntry *)ws_at(workspace, pl.off_t_b1);
+    src.count_b1 = (const int32_t *)ws_at(workspace, pl.off_c_b1);
     HIPCHK(launch_router(seg_off, seg_adapter, num_segments, (int)m, adapters, num_adapters, r_max,
                          (ChunkEntry *)src.chunks_f1, (int32_t *)src.count_f1, pl.chunk_cap_f1,
-                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd, stream),
+                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd,
+                         (ChunkEntry *)src.chunks_b1, (int32_t *)src.count_b1, pl.b1.rows, pl.b1.slots, stream),
            "router launch");
     float *dS = (float *)ws_at(workspace, pl.off_ds);
     float *dSpart = pl.ds_parts > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
     float *dBpart = (float *)ws_at(workspace, pl.off_dbpart);
     float *dApart = (float *)ws_at(workspace, pl.off_dapart);
     const int chunks = pl.chunk_cap_bwd;
-    if (m > 0) {
-        HIPCHK(launch_b1(dY, S, (int)m, (int)n, r_max, src, chunks, pl.C1, dSpart, dBpart, stream), "B1 launch");
-        if (pl.ds_parts > 1)
-            HIPCHK(launch_sum_partials(dSpart, pl.ds_parts, (size_t)m * r_max, (size_t)m * r_max, dS, "sum_ds_partials",
-                                       stream), "dS reduction launch");
-    }
-    HIPCHK(launch_grad_reduce(0, dBpart, (int)m, (int)k, (int)n, r_max, src, chunks, stream), "dB reduction launch");
+    if (m > 0) HIPCHK(launch_b1(dY, S, (int)m, (int)n, r_max, src, pl.b1, dSpart, dBpart, stream), "B1 launch");
+    HIPCHK(launch_b1_reduce(dSpart, m > 0 ? pl.ds_parts : 1, dS, dBpart, (int)m, (int)n, r_max, src, pl.b1.rows,
+                            pl.b1.slots, stream),
+           "dS/dB reduction launch");
     if (m > 0)
         HIPCHK(launch_b2(X, keep_bits, dS, (int)m, (int)k, r_max, src, chunks, pl.C2, dApart, stream), "B2 launch");
-    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r_max, src, chunks, stream), "dA reduction launch");
+    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r_max, src, kBwdRows, chunks, stream),
+           "dA reduction launch");
     if (m > 0)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r_max, keep_bits, (int)((k + 31) / 32),
                            src, stream), "B3 launch");

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -47,12 +48,17 @@ struct AdapterSource {
     const int32_t *count_f1;
     const ChunkEntry *chunks_bwd;
     const int32_t *count_bwd;
+    const ChunkEntry *chunks_b1;
+    const int32_t *count_b1;
 };
+
+// Which router table a kernel's work items come from.
+enum WorkTable { kTabF1 = 0, kTabBwd = 1, kTabB1 = 2 };
 
 hipError_t launch_router(const int64_t *seg_off, const int32_t *seg_adapter, int nseg, int m,
                          const lora_adapter *adapters, int nad, int r_cap, ChunkEntry *t_f1,
                          int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int cap_bwd,
-                         hipStream_t stream);
+                         ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream);
 
 hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int chunk_cap,
                      uint64_t seed, uint64_t offset, uint32_t *keep_bits, float *out, int RS,
@@ -61,16 +67,60 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
 hipError_t launch_sum_partials(const float *part, int nparts, size_t part_stride, size_t count,
                                float *out, const char *name, hipStream_t stream);
 
+// Launch shape of B1 (dS and dB partials).  Work-groups cover C1 columns of
+// a row group: `rows` rows of the single adapter, or one router chunk of the
+// mixed-adapter form.  dS gets one partial per column tile (CT), dB one per
+// row group (slots).  The streaming kernel serves ranks up to 32; its 32-bit
+// direct-to-LDS offsets need rows * n * 2 < 2^31.
+struct B1Shape {
+    bool streaming;
+    int cw;  // streaming: C1 = 256 * cw
+    int C1, CT, rows, slots;
+};
+inline B1Shape b1_shape(int64_t m, int64_t n, int r_lds, bool multi, int nseg) {
+    B1Shape s{};
+    const int64_t maxrows = ((int64_t(1) << 31) - 1) / (2 * n) / 32 * 32;
+    s.streaming = r_lds <= 32 && maxrows >= 32;
+    if (!s.streaming) {
+        s.cw = 1;
+        s.C1 = r_lds <= 128 ? 256 : 128;
+        s.CT = (int)((n + s.C1 - 1) / s.C1);
+        s.rows = kBwdRows;
+    } else {
+        // 256-column tiles: two work-groups share a CU (measured faster than
+        // 512-column tiles at one per CU, despite twice the dS partials)
+        s.cw = 1;
+        s.C1 = 256 * s.cw;
+        s.CT = (int)((n + s.C1 - 1) / s.C1);
+        // about 512 work-groups; fewer, taller row groups mean fewer dB partials
+        int64_t nrg = std::max<int64_t>(1, 512 / s.CT);
+        nrg = std::min<int64_t>(nrg, std::max<int64_t>(1, (m + 31) / 32));
+        int64_t rows = std::max<int64_t>(32, 32 * (((m + nrg - 1) / nrg + 31) / 32));
+        s.rows = (int)std::min(rows, maxrows);
+    }
+    // mixed adapters: the router cuts each segment into runs of `rows`
+    s.slots = (int)((m + s.rows - 1) / s.rows) + (multi ? nseg : 0);
+    return s;
+}
+
 hipError_t launch_b1(const void *dY, const float *S, int m, int n, int RS, const AdapterSource &src,
-                     int chunk_cap, int C1, float *dSpart, float *dBpart, hipStream_t stream);
+                     const B1Shape &sh, float *dSpart, float *dBpart, hipStream_t stream);
 
 hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS,
                      const AdapterSource &src, int chunk_cap, int C2, float *dApart,
                      hipStream_t stream);
 
 // which = 0: dB (r x n per adapter from [chunk][RS][n]); 1: dA (k x r from [chunk][k][RS]).
+// dS = fixed-order sum of B1's nparts column-tile partials (skipped when
+// nparts == 1) and dB = per-adapter sum of its row-group partials, one launch.
+hipError_t launch_b1_reduce(const float *dSpart, int nparts, float *dS, const float *dBpart, int m, int n,
+                            int RS, const AdapterSource &src, int rows, int slots, hipStream_t stream);
+
+// rows: rows per partial of the single-adapter form; slots: partials
+// written (an upper bound in the mixed-adapter form, where the router's chunk
+// count decides).
 hipError_t launch_grad_reduce(int which, const float *part, int m, int k, int n, int RS,
-                              const AdapterSource &src, int chunk_cap, hipStream_t stream);
+                              const AdapterSource &src, int rows, int slots, hipStream_t stream);
 
 hipError_t launch_mask(uint64_t seed, uint64_t offset, int m, int k, float p, uint32_t *bits,
                        hipStream_t stream);

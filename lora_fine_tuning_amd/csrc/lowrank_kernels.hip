@@ -21,19 +21,28 @@ namespace lora {
 // Router: chunk tables for the low-rank kernels (papers.chlience.com notes,
 // section 5 "FusedMultiLoRA": tile-level routing by adapter id).  Each
 // non-empty segment with a valid adapter is cut into runs of at most
-// rows_f1 (resp. rows_bwd) rows; a single work-group scans the segments.
+// `rows` rows for each of up to three tables; one work-group scans the
+// segments.  A table with rows == 0 is skipped.
 // ===========================================================================
+struct RouterTable {
+    ChunkEntry *t;
+    int32_t *c;
+    int rows;
+    int cap;
+};
+struct RouterTables {
+    RouterTable tab[3];
+};
+
 __global__ __launch_bounds__(1024) void router_kernel(const int64_t *seg_off, const int32_t *seg_ad,
                                                      int nseg, int m, const lora_adapter *adapters,
-                                                     int nad, int r_cap, ChunkEntry *t0, int32_t *c0,
-                                                     int rows0, int cap0, ChunkEntry *t1,
-                                                     int32_t *c1, int rows1, int cap1) {
-    __shared__ int sc0[1024], sc1[1024];
+                                                     int nad, int r_cap, RouterTables T) {
+    __shared__ int sc[3][1024];
     const int tid = threadIdx.x;
-    int carry0 = 0, carry1 = 0;
+    int carry[3] = {0, 0, 0};
     for (int base = 0; base < nseg; base += 1024) {
         const int s = base + tid;
-        int lo = 0, hi = 0, a = -1, n0 = 0, n1 = 0;
+        int lo = 0, hi = 0, a = -1, nq[3] = {0, 0, 0};
         if (s < nseg) {
             const int64_t o0 = seg_off[s], o1 = seg_off[s + 1];
             lo = (int)max((int64_t)0, min(o0, (int64_t)m));
@@ -44,61 +53,56 @@ __global__ __launch_bounds__(1024) void router_kernel(const int64_t *seg_off, co
                 const int r = adapters[a].r;
                 ok = r >= 1 && r <= r_cap;
             }
-            if (ok) {
-                n0 = (hi - lo + rows0 - 1) / rows0;
-                n1 = (hi - lo + rows1 - 1) / rows1;
-            }
+            if (ok)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    nq[j] = T.tab[j].rows > 0 ? (hi - lo + T.tab[j].rows - 1) / T.tab[j].rows : 0;
         }
-        sc0[tid] = n0;
-        sc1[tid] = n1;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) sc[j][tid] = nq[j];
         __syncthreads();
         for (int d = 1; d < 1024; d <<= 1) {
-            const int v0 = tid >= d ? sc0[tid - d] : 0;
-            const int v1 = tid >= d ? sc1[tid - d] : 0;
+            int v[3];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) v[j] = tid >= d ? sc[j][tid - d] : 0;
             __syncthreads();
-            sc0[tid] += v0;
-            sc1[tid] += v1;
+#pragma unroll
+            for (int j = 0; j < 3; ++j) sc[j][tid] += v[j];
             __syncthreads();
         }
-        const int p0 = carry0 + sc0[tid] - n0;
-        const int p1 = carry1 + sc1[tid] - n1;
-        for (int q = 0; q < n0; ++q) {
-            if (p0 + q < cap0) {
-                ChunkEntry e;
-                e.row_lo = lo + q * rows0;
-                e.row_hi = min(hi, lo + (q + 1) * rows0);
-                e.adapter = a;
-                e.pad = 0;
-                t0[p0 + q] = e;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int pos = carry[j] + sc[j][tid] - nq[j];
+            const int rows = T.tab[j].rows;
+            for (int q = 0; q < nq[j]; ++q) {
+                if (pos + q < T.tab[j].cap) {
+                    ChunkEntry e;
+                    e.row_lo = lo + q * rows;
+                    e.row_hi = min(hi, lo + (q + 1) * rows);
+                    e.adapter = a;
+                    e.pad = 0;
+                    T.tab[j].t[pos + q] = e;
+                }
             }
+            carry[j] += sc[j][1023];
         }
-        for (int q = 0; q < n1; ++q) {
-            if (p1 + q < cap1) {
-                ChunkEntry e;
-                e.row_lo = lo + q * rows1;
-                e.row_hi = min(hi, lo + (q + 1) * rows1);
-                e.adapter = a;
-                e.pad = 0;
-                t1[p1 + q] = e;
-            }
-        }
-        carry0 += sc0[1023];
-        carry1 += sc1[1023];
         __syncthreads();
     }
-    if (tid == 0) {
-        c0[0] = min(carry0, cap0);
-        c1[0] = min(carry1, cap1);
-    }
+    if (tid == 0)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (T.tab[j].rows > 0) T.tab[j].c[0] = min(carry[j], T.tab[j].cap);
 }
 
-static RowWork make_work(const AdapterSource &src, bool f1) {
+static RowWork make_work(const AdapterSource &src, WorkTable tab) {
     RowWork w;
-    w.chunks = src.table ? (f1 ? src.chunks_f1 : src.chunks_bwd) : nullptr;
-    w.chunk_count = src.table ? (f1 ? src.count_f1 : src.count_bwd) : nullptr;
+    const ChunkEntry *const tabs[3] = {src.chunks_f1, src.chunks_bwd, src.chunks_b1};
+    const int32_t *const counts[3] = {src.count_f1, src.count_bwd, src.count_b1};
+    w.chunks = src.table ? tabs[tab] : nullptr;
+    w.chunk_count = src.table ? counts[tab] : nullptr;
     w.adapters = src.table;
     w.num_adapters = src.num_adapters;
-    w.rows_per_chunk = f1 ? kF1Rows : kBwdRows;
+    w.rows_per_chunk = tab == kTabF1 ? kF1Rows : kBwdRows;
     w.r_cap = src.table ? src.r_cap : src.r;
     w.single.A = (const uint16_t *)src.A;
     w.single.B = (const uint16_t *)src.B;
@@ -433,11 +437,11 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
 // part, and the four partial sums are added in a fixed order (bitwise
 // reproducible).
 // ===========================================================================
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float *part, int nparts,
-                                                           size_t stride, size_t count, float *out) {
+__device__ __forceinline__ void sum_partials_block(const float *part, int nparts, size_t stride, size_t count,
+                                                   float *out, int block) {
     __shared__ float4 red[4][64];
     const int t = threadIdx.x, pg = t >> 6, c = t & 63;
-    const size_t i4 = ((size_t)blockIdx.x * 64 + c) * 4;
+    const size_t i4 = ((size_t)block * 64 + c) * 4;
     const bool vec = (stride & 3) == 0 && (((uintptr_t)part) & 15) == 0;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i4 < count) {
@@ -468,6 +472,11 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float *part, in
         for (int e = 0; e < 4; ++e)
             if (i4 + e < count) out[i4 + e] = rv[e];
     }
+}
+
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float *part, int nparts, size_t stride,
+                                                           size_t count, float *out) {
+    sum_partials_block(part, nparts, stride, count, out, blockIdx.x);
 }
 
 // ===========================================================================
@@ -952,158 +961,186 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
     }
 }
 
-// ----- B1 streaming: sub-blocks of 32 rows; stage = dY 16 KiB + 4 KiB S (ranks <= 32).
-// Waves (w & 1) own 16 rows for dS and split the 256 columns in halves
-// (w >> 1), each half writing its own dS partial: partial index 2*ct + half.
-constexpr int B1S_ROWS = 32, B1S_Y = 32 * 512, B1S_STAGE = B1S_Y + 4 * 1024, B1S_NST = 3;
-constexpr int B1S_LDB = 256 + 8;  // row stride of the staged B chunk (elements)
+// ----- B1 streaming (ranks <= 32).  Work-group = one row group (rows of one
+// adapter) x C1 = 256*CW columns; rows go in sub-blocks of 32 through a
+// 3-stage ring of direct-to-LDS loads (dY as CW swizzled 256-column sub-tiles,
+// plus the 32 rows of S).  Wave w owns the 16-column blocks 4*CW*w .. +4*CW-1:
+// it accumulates dB = alpha S^T dY for them over all the group's rows, and
+// its share of dS = alpha dY B^T for each sub-block; the four shares meet in
+// LDS and are summed in wave order into one dS partial per column tile.  The
+// B fragments of the wave's columns stay in registers.
+constexpr int B1V_SUB = 32 * 512;  // one 32-row x 256-column sub-tile
 
-template <int MAXT>
-__global__ __launch_bounds__(256) void b1s_kernel(B1Params P) {
-    extern __shared__ uint4 b1s_smem[];
-    lds_char *smem = (lds_char *)b1s_smem;
+template <int CW, int MAXT, int NST>
+__global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
+    constexpr int RL = 16 * MAXT;
+    constexpr int SY = CW * B1V_SUB;        // dY bytes per stage
+    constexpr int STAGE = SY + 32 * 32 * 4;  // + 32 rows of S (up to 32 fp32 each)
+    constexpr int NB = 4 * CW;               // 16-column blocks per wave
+    constexpr int NQ = 2 * CW;               // 32-column k-steps per wave (dS)
+    constexpr int NDMA = 4 * CW + 1;         // direct-to-LDS loads per wave per stage
+    extern __shared__ uint4 b1v_smem[];
+    lds_char *smem = (lds_char *)b1v_smem;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    uint16_t *Bs = (uint16_t *)(smem + B1S_NST * B1S_STAGE);  // [r_lds][B1S_LDB]
+    float *red = (float *)(smem + NST * STAGE);  // [2][4 waves][32 rows][RL]
 
     int row_lo, row_hi;
     AdapterView ad;
     if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
     const int r = ad.r;
-    const int nbt = (r + 15) >> 4;
-    const int rpad = nbt * 16;
     const float alpha = ad.alpha;
-    const int ct = blockIdx.y, n0 = ct * 256;
+    const int ct = blockIdx.y, n0 = ct * 256 * CW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
-    const int rb = wave & 1, half = wave >> 1;
     const int nrows = row_hi - row_lo;
-    const int nsb = (nrows + B1S_ROWS - 1) / B1S_ROWS;
-    auto clampb = [](uint64_t v) { return (uint32_t)(v < 0x7FFFFFF0ull ? v : 0x7FFFFFF0ull); };
-    const sgpr4_t dYd = make_desc(P.dY + (size_t)row_lo * P.n, clampb((uint64_t)nrows * P.n * 2));
-    const sgpr4_t dS = make_desc(P.S + (size_t)row_lo * P.RS, clampb((uint64_t)nrows * P.RS * 4));
+    const int nsb = (nrows + 31) / 32;
+    // host guarantees nrows * n * 2 < 2^31
+    const sgpr4_t dYd = make_desc(P.dY + (size_t)row_lo * P.n, (uint32_t)((uint64_t)nrows * P.n * 2));
+    const sgpr4_t dSd = make_desc(P.S + (size_t)row_lo * P.RS, (uint32_t)((uint64_t)nrows * P.RS * 4));
 
-    // B chunk (rank x 256 columns), zero-padded, staged once
-    for (int idx = tid; idx < rpad * 256; idx += 256) {
-        const int rr = idx >> 8, j = idx & 255;
-        uint16_t v = 0;
-        if (rr < r && n0 + j < P.n) v = ad.B[(size_t)rr * P.n + n0 + j];
-        Bs[rr * B1S_LDB + j] = v;
-    }
-
-    uint32_t offY[4];
+    // dY: instruction j of a sub-tile writes LDS rows 2(4w+j), +1 (512 B each);
+    // LDS chunk (lane & 31) of row rr holds global chunk (lane & 31) ^ swz512(rr)
+    uint32_t offY[CW][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int rr = 2 * (4 * wave + j) + (lane >> 5);
-        const int col = n0 + 8 * ((lane & 31) ^ swz512(rr));
-        offY[j] = col < P.n ? (uint32_t)(((size_t)rr * P.n + col) * 2) : kOOBL;
-    }
-    const uint32_t sbb = (uint32_t)(B1S_ROWS * P.RS * 4);  // S bytes per sub-block
-    auto issue = [&](int sb, int stage) {
-        const uint32_t base = lds0 + stage * B1S_STAGE;
-        const uint32_t yo = (uint32_t)((size_t)sb * B1S_ROWS * P.n * 2);
+    for (int t = 0; t < CW; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(dYd, offY[j] == kOOBL ? kOOBL : offY[j] + yo, base + (4 * wave + j) * 1024);
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 2 * (4 * wave + j) + (lane >> 5);
+            const int col = n0 + 256 * t + 8 * ((lane & 31) ^ swz512(rr));
+            offY[t][j] = col < P.n ? (uint32_t)(rr * P.n + col) * 2u : kOOBL;
+        }
+    const uint32_t sbb = (uint32_t)(32 * P.RS * 4);  // S bytes per sub-block
+    auto issue = [&](int sb, int stage) {  // sub-blocks past the last read zeros
+        const uint32_t base = lds0 + stage * STAGE;
+        const bool live = sb < nsb;
+        const uint32_t yo = live ? (uint32_t)sb * 32u * (uint32_t)P.n * 2u : 0u;
+#pragma unroll
+        for (int t = 0; t < CW; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dma16(dYd, (!live || offY[t][j] == kOOBL) ? kOOBL : offY[t][j] + yo,
+                      base + t * B1V_SUB + (4 * wave + j) * 1024);
         const uint32_t b = (uint32_t)wave * 1024 + lane * 16;
-        dma16(dS, b < sbb ? (uint32_t)sb * sbb + b : kOOBL, base + B1S_Y + wave * 1024);
+        dma16(dSd, (live && b < sbb) ? (uint32_t)sb * sbb + b : kOOBL, base + SY + wave * 1024);
     };
 
-    f32x4_t accB[MAXT][4];
+    // B fragments for dS: rank 16bt + li, columns n0 + 64CW w + 32q + 8g .. +7
+    uint4 bfr[NQ][MAXT];
+    {
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(ad.B, (size_t)r * P.n * 2);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int bt = 0; bt < MAXT; ++bt) {
+                const int rank = 16 * bt + li;
+                const int col = n0 + 64 * CW * wave + 32 * q + 8 * g;
+                const uint32_t off = (rank < r && col < P.n) ? (uint32_t)(rank * P.n + col) * 2u : kOOB;
+                bfr[q][bt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0));
+            }
+    }
+
+    f32x4_t accB[MAXT][NB];
 #pragma unroll
     for (int a = 0; a < MAXT; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) accB[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NB; ++b) accB[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    issue(0, 0);
-    issue(1, 1);
-    wait_vmcnt<5>();
+#pragma unroll
+    for (int q = 0; q < NST - 1; ++q) issue(q, q);
+    wait_vmcnt<NDMA * (NST - 2)>();
     __syncthreads();
-    int stage = 0, lstage = 2;
-    float *dsp = P.dSpart + (size_t)(2 * ct + half) * P.m * P.RS;
+    float *dsp = P.dSpart + (size_t)ct * P.m * P.RS;
+    // sum of the four waves' dS shares of sub-block sb (after the barrier)
+    auto flush_ds = [&](int sb) {
+        const float *rd = red + (sb & 1) * (4 * 32 * RL);
+        const int rs = row_lo + sb * 32;
+        for (int i = tid; i < 32 * P.RS; i += 256) {
+            const int rr = i / P.RS, cc = i - rr * P.RS;
+            if (rs + rr >= row_hi) continue;
+            float v = 0.f;
+            if (cc < r) {
+                v = rd[(0 * 32 + rr) * RL + cc];
+                v += rd[(1 * 32 + rr) * RL + cc];
+                v += rd[(2 * 32 + rr) * RL + cc];
+                v += rd[(3 * 32 + rr) * RL + cc];
+                v *= alpha;
+            }
+            dsp[(size_t)(rs + rr) * P.RS + cc] = v;
+        }
+    };
+    int stage = 0, lstage = NST - 1;
     for (int sb = 0; sb < nsb; ++sb) {
-        issue(sb + 2, lstage);
-        const lds_char *yt = smem + stage * B1S_STAGE;
-        const float *st = (const float *)(yt + B1S_Y);
-        const int rs = row_lo + sb * B1S_ROWS;
+        issue(sb + NST - 1, lstage);
+        const lds_char *yt = smem + stage * STAGE;
+        const float *st = (const float *)(yt + SY);
 
-        // ---- dS partial: 16 rows x rank over this wave's 128 columns
-        f32x4_t accS[MAXT];
+        // ---- dS share: 32 rows x rank over the wave's 64*CW columns
+        f32x4_t accS[2][MAXT];
 #pragma unroll
-        for (int t = 0; t < MAXT; ++t) accS[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int arow = 16 * rb + li;
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int t = 4 * half + tt;
-            const uint4 af = *(const uint4 *)(yt + swz512_off(arow, 4 * t + g));
+            for (int b = 0; b < MAXT; ++b) accS[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int blk = NB * wave + 2 * q;  // first 16-column block of the step
+            const lds_char *sub = yt + (blk >> 4) * B1V_SUB;
+            const int chunk = 2 * (blk & 15) + g;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const uint4 af = *(const uint4 *)(sub + swz512_off(16 * rb + li, chunk));
+#pragma unroll
+                for (int bt = 0; bt < MAXT; ++bt) accS[rb][bt] = mfma16x16x32(af, bfr[q][bt], accS[rb][bt]);
+            }
+        }
+        float *rw = red + (sb & 1) * (4 * 32 * RL) + wave * 32 * RL;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int bt = 0; bt < MAXT; ++bt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) rw[(16 * rb + 4 * g + v) * RL + 16 * bt + li] = accS[rb][bt][v];
+
+        // ---- dB: rank x the wave's columns, K = the 32 rows
+        uint4 ahi[MAXT], alo[MAXT];
+#pragma unroll
+        for (int bt = 0; bt < MAXT; ++bt) {
+            float v[8];
+            const int rr = 16 * bt + li;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = rr < r ? alpha * st[(8 * g + e) * P.RS + rr] : 0.f;
+            split_frag(v, ahi[bt], alo[bt]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int blk = NB * wave + b;
+            const uint4 yf = tile_rows8(yt + (blk >> 4) * B1V_SUB, 8 * g, blk & 15, lane);
 #pragma unroll
             for (int bt = 0; bt < MAXT; ++bt) {
-                if (bt < nbt) {
-                    const uint4 bf = *(const uint4 *)&Bs[(bt * 16 + li) * B1S_LDB + 32 * t + 8 * g];
-                    accS[bt] = mfma16x16x32(af, bf, accS[bt]);
-                }
+                accB[bt][b] = mfma16x16x32(ahi[bt], yf, accB[bt][b]);
+                accB[bt][b] = mfma16x16x32(alo[bt], yf, accB[bt][b]);
             }
         }
-#pragma unroll
-        for (int bt = 0; bt < MAXT; ++bt) {
-            if (bt < nbt) {
-                const int col = bt * 16 + li;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int orow = rs + rb * 16 + 4 * g + v;
-                    if (orow < row_hi && col < P.RS) dsp[(size_t)orow * P.RS + col] = col < r ? alpha * accS[bt][v] : 0.f;
-                }
-            }
-        }
-        for (int col = rpad + li; col < P.RS; col += 16) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int orow = rs + rb * 16 + 4 * g + v;
-                if (orow < row_hi) dsp[(size_t)orow * P.RS + col] = 0.f;
-            }
-        }
-
-        // ---- dB partial: rank x wave's 64 columns, K = the 32 rows
-        uint4 bfr[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) bfr[nb] = tile_rows8(yt, 8 * g, 4 * wave + nb, lane);
-#pragma unroll
-        for (int bt = 0; bt < MAXT; ++bt) {
-            if (bt < nbt) {
-                float v[8];
-                const int rr = 16 * bt + li;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = rr < r ? alpha * st[(8 * g + e) * P.RS + rr] : 0.f;
-                uint4 ahi, alo;
-                split_frag(v, ahi, alo);
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    accB[bt][nb] = mfma16x16x32(ahi, bfr[nb], accB[bt][nb]);
-                    accB[bt][nb] = mfma16x16x32(alo, bfr[nb], accB[bt][nb]);
-                }
-            }
-        }
-        wait_vmcnt<5>();
+        wait_vmcnt<NDMA * (NST - 2)>();
         __syncthreads();
-        stage = stage == B1S_NST - 1 ? 0 : stage + 1;
-        lstage = lstage == B1S_NST - 1 ? 0 : lstage + 1;
+        flush_ds(sb);
+        stage = stage == NST - 1 ? 0 : stage + 1;
+        lstage = lstage == NST - 1 ? 0 : lstage + 1;
     }
     wait_vmcnt<0>();
 
     float *dbp = P.dBpart + (size_t)blockIdx.x * P.RS * P.n;
 #pragma unroll
-    for (int bt = 0; bt < MAXT; ++bt) {
-        if (bt < nbt) {
+    for (int bt = 0; bt < MAXT; ++bt)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const int col = n0 + (wave * 4 + nb) * 16 + li;
+        for (int b = 0; b < NB; ++b) {
+            const int col = n0 + 16 * (NB * wave + b) + li;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int rr = bt * 16 + 4 * g + v;
-                    if (rr < r && col < P.n) dbp[(size_t)rr * P.n + col] = accB[bt][nb][v];
-                }
+            for (int v = 0; v < 4; ++v) {
+                const int rr = 16 * bt + 4 * g + v;
+                if (rr < r && col < P.n) dbp[(size_t)rr * P.n + col] = accB[bt][b][v];
             }
         }
-    }
 }
 
 // ===========================================================================
@@ -1118,9 +1155,8 @@ struct GradReduceParams {
     int chunk_cap;
 };
 
-__global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceParams P) {
+__device__ __forceinline__ void grad_reduce_block(const GradReduceParams &P, int a, int bx, int gx) {
     __shared__ float red[4][64];
-    const int a = blockIdx.y;
     AdapterView ad;
     if (P.work.chunks == nullptr) {
         ad = P.work.single;
@@ -1142,7 +1178,7 @@ __global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceParams P) {
 
     // 64 outputs per work-group pass; wave pg sums chunks pg, pg+4, ...
     const int t = threadIdx.x, pg = t >> 6, c = t & 63;
-    for (size_t base = (size_t)blockIdx.x * 64; base < total; base += (size_t)gridDim.x * 64) {
+    for (size_t base = (size_t)bx * 64; base < total; base += (size_t)gx * 64) {
         const size_t e = base + c;
         float acc = 0.f;
         if (e < total) {
@@ -1161,6 +1197,32 @@ __global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceParams P) {
             const float v = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
             outp[e] = (uint16_t)f32_to_bf16_rne(v);
         }
+    }
+}
+
+__global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceParams P) {
+    grad_reduce_block(P, blockIdx.y, blockIdx.x, gridDim.x);
+}
+
+// dS (fixed-order sum of B1's column-tile partials) and dB (per-adapter sum of
+// its row-group partials) in one launch: work-groups [0, ds_blocks) do the
+// former, the rest the latter (db_gx per adapter).
+struct B1ReduceParams {
+    const float *dspart;
+    int nparts;
+    size_t stride, count;
+    float *ds;
+    int ds_blocks, db_gx;
+    GradReduceParams db;
+};
+
+__global__ __launch_bounds__(256) void b1_reduce_kernel(B1ReduceParams P) {
+    const int b = blockIdx.x;
+    if (b < P.ds_blocks) {
+        sum_partials_block(P.dspart, P.nparts, P.stride, P.count, P.ds, b);
+    } else {
+        const int q = b - P.ds_blocks;
+        grad_reduce_block(P.db, q / P.db_gx, q % P.db_gx, P.db_gx);
     }
 }
 
@@ -1197,12 +1259,15 @@ static hipError_t finish_launch(int slot, hipStream_t stream) {
 hipError_t launch_router(const int64_t *seg_off, const int32_t *seg_adapter, int nseg, int m,
                          const lora_adapter *adapters, int nad, int r_cap, ChunkEntry *t_f1,
                          int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int cap_bwd,
-                         hipStream_t stream) {
+                         ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream) {
+    RouterTables T;
+    T.tab[0] = RouterTable{t_f1, c_f1, kF1Rows, cap_f1};
+    T.tab[1] = RouterTable{t_bwd, c_bwd, kBwdRows, cap_bwd};
+    T.tab[2] = RouterTable{t_b1, c_b1, t_b1 != nullptr ? rows_b1 : 0, cap_b1};
     (void)hipGetLastError();
     const int slot = prof_begin("router", stream);
     hipLaunchKernelGGL(router_kernel, dim3(1), dim3(1024), 0, stream, seg_off, seg_adapter, nseg, m,
-                       adapters, nad, r_cap, t_f1, c_f1, kF1Rows, cap_f1, t_bwd, c_bwd, kBwdRows,
-                       cap_bwd);
+                       adapters, nad, r_cap, T);
     return finish_launch(slot, stream);
 }
 
@@ -1233,7 +1298,7 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
     P.X = (const uint16_t *)X;
     P.m = m;
     P.k = k;
-    P.work = make_work(src, true);
+    P.work = make_work(src, kTabF1);
     P.seed = seed;
     P.offset = offset;
     P.keep_bits = keep_bits;
@@ -1285,34 +1350,42 @@ size_t b1_lds_bytes(int C1, int r_lds) {
 size_t b2_lds_bytes(int C2, int r_lds) { return (size_t)C2 * 72 * 2 + (size_t)r_lds * 68 * 4; }
 
 hipError_t launch_b1(const void *dY, const float *S, int m, int n, int RS, const AdapterSource &src,
-                     int chunk_cap, int C1, float *dSpart, float *dBpart, hipStream_t stream) {
+                     const B1Shape &sh, float *dSpart, float *dBpart, hipStream_t stream) {
     B1Params P;
     P.dY = (const uint16_t *)dY;
     P.S = S;
     P.m = m;
     P.n = n;
     P.RS = RS;
-    P.work = make_work(src, false);
+    P.work = make_work(src, kTabB1);
+    P.work.rows_per_chunk = sh.rows;
     P.dSpart = dSpart;
     P.dBpart = dBpart;
     P.r_lds = r_lds_of(src);
-    const size_t lds = b1_lds_bytes(C1, P.r_lds);
     (void)hipGetLastError();
     const int slot = prof_begin("b1_ds_db", stream);
-    const dim3 grid(chunk_cap, cdiv(n, C1));
-    if (C1 == 256 && P.r_lds <= 32) {
-        const size_t slds = (size_t)B1S_NST * B1S_STAGE + (size_t)P.r_lds * B1S_LDB * 2;
-        if (P.r_lds <= 16) launch_with_lds(b1s_kernel<1>, grid, slds, stream, P);
-        else launch_with_lds(b1s_kernel<2>, grid, slds, stream, P);
-    } else if (C1 == 256) {
-        switch (rank_blocks(P.r_lds)) {
-        case 1: launch_with_lds(b1_kernel<256, 1>, grid, lds, stream, P); break;
-        case 2: launch_with_lds(b1_kernel<256, 2>, grid, lds, stream, P); break;
-        case 4: launch_with_lds(b1_kernel<256, 4>, grid, lds, stream, P); break;
-        default: launch_with_lds(b1_kernel<256, 8>, grid, lds, stream, P); break;
-        }
+    const dim3 grid(sh.slots, sh.CT);
+    if (sh.streaming) {
+        if (sh.cw != 1) return hipErrorInvalidValue;  // the streaming kernel is built for 256-column tiles
+        const int rl = P.r_lds <= 16 ? 16 : 32;
+        // ring depth 3: two stages in flight, two work-groups per CU
+        auto lds_of = [&](int nst) {
+            return (size_t)nst * (sh.cw * B1V_SUB + 32 * 32 * 4) + (size_t)2 * 4 * 32 * rl * 4;
+        };
+        if (rl == 16) launch_with_lds(b1v_kernel<1, 1, 3>, grid, lds_of(3), stream, P);
+        else launch_with_lds(b1v_kernel<1, 2, 3>, grid, lds_of(3), stream, P);
     } else {
-        launch_with_lds(b1_kernel<128, 16>, grid, lds, stream, P);
+        const size_t lds = b1_lds_bytes(sh.C1, P.r_lds);
+        if (sh.C1 == 256) {
+            switch (rank_blocks(P.r_lds)) {
+            case 1: launch_with_lds(b1_kernel<256, 1>, grid, lds, stream, P); break;
+            case 2: launch_with_lds(b1_kernel<256, 2>, grid, lds, stream, P); break;
+            case 4: launch_with_lds(b1_kernel<256, 4>, grid, lds, stream, P); break;
+            default: launch_with_lds(b1_kernel<256, 8>, grid, lds, stream, P); break;
+            }
+        } else {
+            launch_with_lds(b1_kernel<128, 16>, grid, lds, stream, P);
+        }
     }
     return finish_launch(slot, stream);
 }
@@ -1328,7 +1401,7 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
     P.k = k;
     P.RS = RS;
     P.KW = (k + 31) / 32;
-    P.work = make_work(src, false);
+    P.work = make_work(src, kTabBwd);
     P.dApart = dApart;
     P.r_lds = r_lds_of(src);
     const size_t lds = b2_lds_bytes(C2, P.r_lds);
@@ -1352,8 +1425,8 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
     return finish_launch(slot, stream);
 }
 
-hipError_t launch_grad_reduce(int which, const float *part, int m, int k, int n, int RS,
-                              const AdapterSource &src, int chunk_cap, hipStream_t stream) {
+static GradReduceParams grad_params(int which, const float *part, int m, int k, int n, int RS,
+                                    const AdapterSource &src, int rows, int slots) {
     GradReduceParams P;
     P.part = part;
     P.which = which;
@@ -1361,14 +1434,45 @@ hipError_t launch_grad_reduce(int which, const float *part, int m, int k, int n,
     P.k = k;
     P.n = n;
     P.RS = RS;
-    P.work = make_work(src, false);
-    P.chunk_cap = chunk_cap;
-    const int nad = src.table ? src.num_adapters : 1;
+    P.work = make_work(src, which == 0 ? kTabB1 : kTabBwd);
+    P.work.rows_per_chunk = rows;
+    P.chunk_cap = slots;
+    return P;
+}
+
+static int grad_gx(int which, int k, int n, int RS) {
     const size_t per = (size_t)(which == 0 ? n : k) * (size_t)RS;
-    const int gx = (int)std::min<size_t>((per + 63) / 64, 8192);
+    return (int)std::min<size_t>((per + 63) / 64, 8192);
+}
+
+hipError_t launch_grad_reduce(int which, const float *part, int m, int k, int n, int RS,
+                              const AdapterSource &src, int rows, int slots, hipStream_t stream) {
+    const GradReduceParams P = grad_params(which, part, m, k, n, RS, src, rows, slots);
+    const int nad = src.table ? src.num_adapters : 1;
+    const int gx = grad_gx(which, k, n, RS);
     (void)hipGetLastError();
     const int slot = prof_begin(which == 0 ? "reduce_db" : "reduce_da", stream);
     hipLaunchKernelGGL(grad_reduce_kernel, dim3(gx, nad), dim3(256), 0, stream, P);
+    return finish_launch(slot, stream);
+}
+
+hipError_t launch_b1_reduce(const float *dSpart, int nparts, float *dS, const float *dBpart, int m, int n,
+                            int RS, const AdapterSource &src, int rows, int slots, hipStream_t stream) {
+    B1ReduceParams P;
+    P.dspart = dSpart;
+    P.nparts = nparts;
+    P.stride = (size_t)m * RS;
+    P.count = (size_t)m * RS;
+    P.ds = dS;
+    P.ds_blocks = nparts > 1 ? (int)((P.count + 255) / 256) : 0;  // one partial: B1 wrote dS itself
+    P.db = grad_params(0, dBpart, m, 0, n, RS, src, rows, slots);
+    P.db_gx = grad_gx(0, 0, n, RS);
+    const int nad = src.table ? src.num_adapters : 1;
+    const size_t blocks = (size_t)P.ds_blocks + (size_t)P.db_gx * nad;
+    if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    const int slot = prof_begin("reduce_ds_db", stream);
+    hipLaunchKernelGGL(b1_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P);
     return finish_launch(slot, stream);
 }
 
