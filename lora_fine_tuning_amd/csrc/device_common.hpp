@@ -34,6 +34,14 @@ __device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo) 
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
 
+// Two fp32 values -> packed bf16 pair, round to nearest even (one gfx950
+// v_cvt_pk_bf16_f32; agrees with f32_to_bf16_rne on finite inputs).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, bf16x2_t));
+}
+
 // ---------------------------------------------------------------------------
 // MFMA: D = A*B + C with 8 bf16 per lane for each operand.
 // 32x32x16: operand lane l holds row/column (l % 32) and K slots 8*(l/32)..+7;

@@ -389,6 +389,33 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     const bool svec = (P.RS & 7) == 0 && (((uintptr_t)P.Sx) & 15) == 0;
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(P.C + (size_t)m0 * P.N, (size_t)(P.M - m0) * N2);
 
+    // ---- output staging.  Each lane holds 4 consecutive columns of a row per
+    // 16 x 16 tile, so direct stores would write 32-byte pieces of 16 rows
+    // per instruction.  Instead the wave's 128 x 128 bf16 block goes to its
+    // 32 KiB of the (now idle) stage ring -- every wave passed the K loop's
+    // last barrier after its last ring read -- with the 16-byte chunks of each
+    // 256-byte row XOR-swizzled by the row, and is written out as 1 KiB
+    // stores of 4 whole rows (full cache lines).
+    lds_char *cw = (lds_char *)smem + wave * 32768;
+    auto c_put = [&](int tm, int tn, float x0, float x1, float x2, float x3) {
+        const int r = tm * 16 + l16;
+        const int ch = (2 * tn + (lg >> 1)) ^ (r & 15);
+        *(uint2 *)(cw + r * 256 + ch * 16 + (lg & 1) * 8) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+    };
+    auto c_flush = [&]() {
+        const int cc = lane & 15;
+        const int col = wcol0 + cc * 8;
+#pragma unroll 4
+        for (int it = 0; it < 32; ++it) {
+            const int r = it * 4 + (lane >> 4);
+            const uint4 v = *(const uint4 *)(cw + r * 256 + ((cc ^ (r & 15)) << 4));
+            // rows past M fall outside rC; columns past N are dropped here
+            const uint32_t off = col < P.N ? (uint32_t)((size_t)(wrow0 + r - m0) * N2 + (size_t)col * 2) : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                                   rC, off, 0, 0);
+        }
+    };
+
     // ---- single adapter, r <= 32, aligned rank-side operands: every epilogue
     // load (the column-side fragments, the wave's 128 rows of S / dS and, for
     // B3, its keep words) is issued before any of them is used, so their
@@ -403,12 +430,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, 0, lane, true);
             } else {
-                // B[0..32) x [wcol0, wcol0+128) through this wave's 8 KiB of the
-                // (now idle) LDS: 16-byte loads of 256-byte rows (ranks >= r and
-                // columns >= N zero), then transposing reads give each lane 8
-                // consecutive ranks of one column.  Every wave passed the K
-                // loop's last barrier after its last LDS read and DMA.
-                lds_char *bs = (lds_char *)smem + wave * 8192;
+                // B[0..32) x [wcol0, wcol0+128) through this wave's 8 KiB of LDS
+                // past the stage ring (the ring holds the output staging):
+                // 16-byte loads of 256-byte rows (ranks >= r and columns >= N
+                // zero), then transposing reads give each lane 8 consecutive
+                // ranks of one column.
+                lds_char *bs = (lds_char *)smem + NST * STAGE_BYTES + wave * 8192;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int q = lane + 64 * j, rr = q >> 4, c = q & 15;
@@ -480,17 +507,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                             const int col = wcol0 + tn * 16 + 4 * lg;
                             if (col >= P.N) continue;
                             const uint32_t kw = kwv[tm][tn >> 1] >> (col & 31);
-                            uint32_t h[4];
+                            float x[4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                float x = acc[tm][tn][e];
-                                if ((kw >> e) & 1u) x += acc2[tn][e];
-                                h[e] = f32_to_bf16_rne(x);
+                                x[e] = acc[tm][tn][e];
+                                if ((kw >> e) & 1u) x[e] += acc2[tn][e];
                             }
-                            __builtin_amdgcn_raw_buffer_store_b64(
-                                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                                                   make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]))),
-                                rC, (uint32_t)((size_t)(row - m0) * N2 + (size_t)col * 2), 0, 0);
+                            c_put(tm, tn, x[0], x[1], x[2], x[3]);
                         }
                     }
                 }
@@ -505,17 +528,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                     for (int tn = 0; tn < NT16; ++tn) {
                         const int col = wcol0 + tn * 16 + 4 * lg;
                         if (col >= P.N) continue;
-                        uint32_t h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16_rne(acc[tm][tn][e]);
-                        __builtin_amdgcn_raw_buffer_store_b64(
-                            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                                               make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]))),
-                            rC, (uint32_t)((size_t)(row - m0) * N2 + (size_t)col * 2), 0, 0);
+                        const f32x4_t a4 = acc[tm][tn];
+                        c_put(tm, tn, a4[0], a4[1], a4[2], a4[3]);
                     }
                 }
             }
         }
+        c_flush();
         return;
     } else {
 
@@ -624,26 +643,24 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 if (col >= P.N) continue;
                 uint32_t kw = 0xFFFFFFFFu;
                 if (EPI == 2 && P.keep != nullptr) kw = P.keep[(size_t)row * P.KW + (col >> 5)] >> (col & 31);
-                uint32_t h[4];
+                float x[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float v = acc[tm][tn][e];
+                    x[e] = acc[tm][tn][e];
                     if (EPI == 2) {
-                        if ((kw >> e) & 1u) v += acc2[tn][e];
+                        if ((kw >> e) & 1u) x[e] += acc2[tn][e];
                     }
-                    h[e] = f32_to_bf16_rne(v);
                 }
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                                       make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]))),
-                    rC, (uint32_t)((size_t)(row - m0) * N2 + (size_t)col * 2), 0, 0);
+                c_put(tm, tn, x[0], x[1], x[2], x[3]);
             }
         }
     }
+    c_flush();
     }  // general epilogue
 }
 
-size_t gemm_lds_bytes() { return (size_t)NST * STAGE_BYTES; }
+// the stage ring plus 8 KiB per wave for the forward epilogue's B staging
+size_t gemm_lds_bytes() { return (size_t)NST * STAGE_BYTES + 4 * 8192; }
 
 template <bool NN, int EPI, bool MULTI, bool FAST>
 static hipError_t launch_gemm_t(const GemmParams &P, hipStream_t stream, const char *name) {
