@@ -157,8 +157,8 @@ def main():
     lf.lora_profiling_reset()
     ms_prof = timed(step, args.steps, 0)
     kernels = {}
-    for name in ("f1_mask_down", "sum_s_partials", "gemm_f2_fwd_lora", "b1_ds_db",
-                 "reduce_ds_db", "b2_da", "reduce_da", "gemm_b3_bwd_dx"):
+    for name in ("f1_mask_down", "sum_s_partials", "gemm_f2_fwd_lora", "b1_ds_db", "sum_ds_partials",
+                 "reduce_db", "reduce_ds_db", "b2_da", "reduce_da", "gemm_b3_bwd_dx"):
         cnt, tot = lf.lora_profiling_query(name)
         kernels[name] = {"launches": cnt, "total_ms": tot,
                          "avg_us": (tot / cnt * 1e3) if cnt else None}
