@@ -82,6 +82,12 @@ __device__ __forceinline__ void mfma_src_ready(uint4 &a, uint4 &b) {
     a = __builtin_bit_cast(uint4, x);
     b = __builtin_bit_cast(uint4, y);
 }
+__device__ __forceinline__ void mfma_src_ready(uint4 &a) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    i32x4_t x = __builtin_bit_cast(i32x4_t, a);
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x));
+    a = __builtin_bit_cast(uint4, x);
+}
 
 // Eight fp32 values -> hi and lo bf16 fragments.
 __device__ __forceinline__ void split_frag(const float v[8], uint4 &hi, uint4 &lo) {
@@ -90,6 +96,16 @@ __device__ __forceinline__ void split_frag(const float v[8], uint4 &hi, uint4 &l
     for (int e = 0; e < 8; ++e) split_bf16(v[e], h[e], l[e]);
     hi = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
     lo = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+}
+
+// One half of split_frag chosen per lane: the hi parts, or (want_lo) the lo
+// parts, of the same 8 values (bit-identical to split_frag's output).
+__device__ __forceinline__ uint4 split_frag_half(const float v[8], bool want_lo) {
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = v[e] - (want_lo ? bf16_to_f32(f32_to_bf16_rne(v[e])) : 0.f);
+    return make_uint4(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]),
+                      pack_bf16x2(d[6], d[7]));
 }
 
 // 8x8 bf16 transpose held in one thread: in[e] is row e (8 elements, 16 B);

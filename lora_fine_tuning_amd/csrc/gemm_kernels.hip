@@ -209,10 +209,12 @@ __device__ __forceinline__ int swz_rows(int r) { return ((r >> 1) & 7) ^ ((r & 1
 // conflict-free.
 __device__ __forceinline__ int swz_w(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
 
-// FAST (single adapter, r <= 32 and a multiple of 8, 16-byte aligned S / dS
-// and rank-side matrix; chosen by the host): the epilogue issues all its loads
-// up front.  Kept as its own instantiation so no kernel merges two epilogues.
-template <bool NN, int EPI, bool MULTI, bool FAST>
+// FAST != 0 (single adapter, r <= 32 and a multiple of 8, 16-byte aligned S /
+// dS, rank-side matrix and mask rows; chosen by the host): the epilogue issues
+// all its loads up front.  FAST == 2 is the r <= 16 form that folds the two
+// halves of the split row side into one MFMA.  Each is its own instantiation
+// so no kernel merges two epilogues.
+template <bool NN, int EPI, bool MULTI, int FAST>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     extern __shared__ uint4 gemm_smem[];
     char *smem = (char *)gemm_smem;
@@ -424,11 +426,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         ExtItem it;
         get_item<EPI, MULTI>(P, 0, it);
         {
+            // FAST == 2 (r <= 16): one 32-deep MFMA per output tile carries both
+            // halves of the fp32 row side -- K slots 0-15 hold the hi parts of
+            // ranks 0-15, slots 16-31 the lo parts -- against the column side's
+            // ranks 0-15 repeated in both halves.  Lanes of K groups 2, 3 then
+            // address the ranks of groups 0, 1.
+            constexpr bool pack = FAST == 2;
+            const int lgr = pack ? (lg & 1) : lg;
             const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it, wcol0);
             uint4 cf[NT16];
             if (EPI == 2) {
 #pragma unroll
-                for (int tn = 0; tn < NT16; ++tn) cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, 0, lane, true);
+                for (int tn = 0; tn < NT16; ++tn)
+                    cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, 0, 16 * lgr + l16, true);
             } else {
                 // B[0..32) x [wcol0, wcol0+128) through this wave's 8 KiB of LDS
                 // past the stage ring (the ring holds the output staging):
@@ -443,7 +453,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                     const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
                     *(uint4 *)(bs + rr * 256 + ((c ^ swz_w(rr)) << 4)) = v;
                 }
-                const int kr = 8 * lg + (l16 >> 2);
+                const int kr = 8 * lgr + (l16 >> 2);
                 const int swr = swz_w(kr);
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) {
@@ -455,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
                 for (int tn = 0; tn < NT16; tn += 2) mfma_src_ready(cf[tn], cf[tn + 1]);
             }
-            const int rb = 8 * lg;
+            const int rb = 8 * lgr;
             float4 sv[NT16][2];
 #pragma unroll
             for (int tm = 0; tm < NT16; ++tm) {
@@ -469,14 +479,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 const bool has_keep = P.keep != nullptr;
                 const __amdgpu_buffer_rsrc_t rK = make_rsrc(has_keep ? P.keep + (size_t)min(wrow0, P.M) * P.KW : P.keep,
                                                             has_keep ? (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.KW * 4u : 0u);
+                // the wave's 128 columns are 4 consecutive mask words of each row:
+                // one 16-byte load per row (the host picks this path only when
+                // rows of words are 16-byte aligned; words past the row's end
+                // only govern columns that are never stored)
 #pragma unroll
-                for (int tm = 0; tm < NT16; ++tm)
-#pragma unroll
-                    for (int q = 0; q < NT16 / 2; ++q) {
-                        const int col = wcol0 + q * 32;
-                        const uint32_t off = (has_keep && col < P.N) ? (uint32_t)((tm * 16 + l16) * P.KW + (col >> 5)) * 4u : kOOB;
-                        kwv[tm][q] = has_keep ? __builtin_amdgcn_raw_buffer_load_b32(rK, off, 0, 0) : 0xFFFFFFFFu;
-                    }
+                for (int tm = 0; tm < NT16; ++tm) {
+                    const uint32_t off = has_keep ? (uint32_t)((tm * 16 + l16) * P.KW + (wcol0 >> 5)) * 4u : kOOB;
+                    const uint4 w4 = has_keep ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0))
+                                              : make_uint4(~0u, ~0u, ~0u, ~0u);
+                    kwv[tm][0] = w4.x;
+                    kwv[tm][1] = w4.y;
+                    kwv[tm][2] = w4.z;
+                    kwv[tm][3] = w4.w;
+                }
             }
 #pragma unroll
             for (int tm = 0; tm < NT16; ++tm) {
@@ -485,20 +501,29 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] *= it.scale;
                 uint4 hi, lo;
-                split_frag(v, hi, lo);
+                if constexpr (pack)
+                    hi = split_frag_half(v, lg >= 2);
+                else
+                    split_frag(v, hi, lo);
                 if (EPI == 1) {
-                    mfma_src_ready(hi, lo);
+                    if constexpr (pack) {
+                        mfma_src_ready(hi);
 #pragma unroll
-                    for (int tn = 0; tn < NT16; ++tn) {
-                        mfma16x16x32_inplace(acc[tm][tn], cf[tn], hi);
-                        mfma16x16x32_inplace(acc[tm][tn], cf[tn], lo);
+                        for (int tn = 0; tn < NT16; ++tn) mfma16x16x32_inplace(acc[tm][tn], cf[tn], hi);
+                    } else {
+                        mfma_src_ready(hi, lo);
+#pragma unroll
+                        for (int tn = 0; tn < NT16; ++tn) {
+                            mfma16x16x32_inplace(acc[tm][tn], cf[tn], hi);
+                            mfma16x16x32_inplace(acc[tm][tn], cf[tn], lo);
+                        }
                     }
                 } else {
                     f32x4_t acc2[NT16];
 #pragma unroll
                     for (int tn = 0; tn < NT16; ++tn) {
                         acc2[tn] = mfma16x16x32(cf[tn], hi, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                        acc2[tn] = mfma16x16x32(cf[tn], lo, acc2[tn]);
+                        if constexpr (!pack) acc2[tn] = mfma16x16x32(cf[tn], lo, acc2[tn]);
                     }
                     const int row = wrow0 + tm * 16 + l16;
                     if (row < P.M) {
@@ -662,7 +687,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 // the stage ring plus 8 KiB per wave for the forward epilogue's B staging
 size_t gemm_lds_bytes() { return (size_t)NST * STAGE_BYTES + 4 * 8192; }
 
-template <bool NN, int EPI, bool MULTI, bool FAST>
+template <bool NN, int EPI, bool MULTI, int FAST>
 static hipError_t launch_gemm_t(const GemmParams &P, hipStream_t stream, const char *name) {
     const size_t lds = gemm_lds_bytes();
     const int G = P.tiles_m * P.tiles_n;
@@ -710,17 +735,20 @@ hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, voi
     const bool multi = src.table != nullptr;
     auto al16 = [](const void *q) { return ((uintptr_t)q & 15) == 0; };
     const bool fast = !multi && epi != 0 && P.ext_r <= 32 && (P.ext_r & 7) == 0 && (RS & 7) == 0 &&
-                      al16(Sx) && al16(P.ext);
+                      al16(Sx) && al16(P.ext) && (epi != 2 || ((KW & 3) == 0 && al16(keep)));
+    const bool pack = fast && P.ext_r <= 16;
     if (nn) {
-        if (epi == 0) return launch_gemm_t<true, 0, false, false>(P, stream, "gemm_frozen_fwd");
-        if (epi == 1) return multi ? launch_gemm_t<true, 1, true, false>(P, stream, "gemm_f2_fwd_lora")
-                             : fast ? launch_gemm_t<true, 1, false, true>(P, stream, "gemm_f2_fwd_lora")
-                                    : launch_gemm_t<true, 1, false, false>(P, stream, "gemm_f2_fwd_lora");
+        if (epi == 0) return launch_gemm_t<true, 0, false, 0>(P, stream, "gemm_frozen_fwd");
+        if (epi == 1) return multi ? launch_gemm_t<true, 1, true, 0>(P, stream, "gemm_f2_fwd_lora")
+                             : pack ? launch_gemm_t<true, 1, false, 2>(P, stream, "gemm_f2_fwd_lora")
+                             : fast ? launch_gemm_t<true, 1, false, 1>(P, stream, "gemm_f2_fwd_lora")
+                                    : launch_gemm_t<true, 1, false, 0>(P, stream, "gemm_f2_fwd_lora");
     } else {
-        if (epi == 0) return launch_gemm_t<false, 0, false, false>(P, stream, "gemm_frozen_bwd");
-        if (epi == 2) return multi ? launch_gemm_t<false, 2, true, false>(P, stream, "gemm_b3_bwd_dx")
-                             : fast ? launch_gemm_t<false, 2, false, true>(P, stream, "gemm_b3_bwd_dx")
-                                    : launch_gemm_t<false, 2, false, false>(P, stream, "gemm_b3_bwd_dx");
+        if (epi == 0) return launch_gemm_t<false, 0, false, 0>(P, stream, "gemm_frozen_bwd");
+        if (epi == 2) return multi ? launch_gemm_t<false, 2, true, 0>(P, stream, "gemm_b3_bwd_dx")
+                             : pack ? launch_gemm_t<false, 2, false, 2>(P, stream, "gemm_b3_bwd_dx")
+                             : fast ? launch_gemm_t<false, 2, false, 1>(P, stream, "gemm_b3_bwd_dx")
+                                    : launch_gemm_t<false, 2, false, 0>(P, stream, "gemm_b3_bwd_dx");
     }
     return hipErrorInvalidValue;
 }
