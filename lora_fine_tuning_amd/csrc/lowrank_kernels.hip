@@ -911,7 +911,11 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
             float v[8];
             const int rr = 16 * bt + li;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (bt < nbt && rr < r) ? s * ds[(8 * g + e) * P.RS + rr] : 0.f;
+            for (int e = 0; e < 8; ++e) {
+                // in-bounds for every lane (rows < 32, RS and rr < 32): read, then select
+                const float dv = ds[(8 * g + e) * P.RS + rr];
+                v[e] = (bt < nbt && rr < r) ? s * dv : 0.f;
+            }
             split_frag(v, bhi[bt], blo[bt]);
         }
 #pragma unroll
@@ -1052,21 +1056,22 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     __syncthreads();
     float *dsp = P.dSpart + (size_t)ct * P.m * P.RS;
     // sum of the four waves' dS shares of sub-block sb (after the barrier)
+    // thread t handles row t / 8 of the sub-block, columns t % 8, +8, ...
     auto flush_ds = [&](int sb) {
         const float *rd = red + (sb & 1) * (4 * 32 * RL);
-        const int rs = row_lo + sb * 32;
-        for (int i = tid; i < 32 * P.RS; i += 256) {
-            const int rr = i / P.RS, cc = i - rr * P.RS;
-            if (rs + rr >= row_hi) continue;
-            float v = 0.f;
-            if (cc < r) {
-                v = rd[(0 * 32 + rr) * RL + cc];
-                v += rd[(1 * 32 + rr) * RL + cc];
-                v += rd[(2 * 32 + rr) * RL + cc];
-                v += rd[(3 * 32 + rr) * RL + cc];
-                v *= alpha;
-            }
-            dsp[(size_t)(rs + rr) * P.RS + cc] = v;
+        const int rr = tid >> 3, rs = row_lo + sb * 32;
+        if (rs + rr >= row_hi) return;
+        float *drow = dsp + (size_t)(rs + rr) * P.RS;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int cc = (tid & 7) + 8 * j;
+            if (cc >= P.RS) break;
+            const int cl = min(cc, RL - 1);
+            float v = rd[(0 * 32 + rr) * RL + cl];
+            v += rd[(1 * 32 + rr) * RL + cl];
+            v += rd[(2 * 32 + rr) * RL + cl];
+            v += rd[(3 * 32 + rr) * RL + cl];
+            drow[cc] = cc < r ? v * alpha : 0.f;
         }
     };
     int stage = 0, lstage = NST - 1;
@@ -1108,7 +1113,11 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
             float v[8];
             const int rr = 16 * bt + li;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = rr < r ? alpha * st[(8 * g + e) * P.RS + rr] : 0.f;
+            for (int e = 0; e < 8; ++e) {
+                // in-bounds for every lane (rows < 32, RS and rr < 32): read, then select
+                const float sv = st[(8 * g + e) * P.RS + rr];
+                v[e] = rr < r ? alpha * sv : 0.f;
+            }
             split_frag(v, ahi[bt], alo[bt]);
         }
 #pragma unroll
