@@ -350,13 +350,70 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     using T_ = std::true_type;
     using F_ = std::false_type;
 
+    // ---- FAST == 2: the epilogue's operands go to the 32 KiB past the stage
+    // ring by direct-to-LDS loads issued right after the prologue, so they
+    // arrive during the K loop (whose first full wait covers them).  Layout
+    // (byte offsets from the region's start):
+    //   0      S / dS rows m0 .. m0+255, 64 bytes each (ranks 0..15; ranks at
+    //          or past RS zero), 16-byte chunk c of row q at c ^ ((q >> 2) & 3)
+    //   16384  F2: B ranks 0..15 x columns n0 .. n0+255, 512-byte rows with
+    //          the W tile's chunk swizzle; B3: A rows n0 .. n0+255 (r bf16
+    //          each) as one contiguous block
+    //   24576  B3: mask words n0/32 .. +7 of rows m0 .. m0+255, 32 bytes each
+    constexpr bool PF = FAST == 2 && EPI != 0 && !MULTI;
+    constexpr int NPF = EPI == 2 ? 8 : 6;  // prefetch loads per wave
+    const uint32_t pf_lds = smem_lds + NST * STAGE_BYTES;
+    auto epi_prefetch = [&]() {
+        {
+            const sgpr4_t d = make_desc(P.Sx + (size_t)m0 * P.RS, clamp_bytes((uint64_t)(P.M - m0) * P.RS * 4u));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = 4 * wave + q, row = 16 * j + (lane >> 2);
+                const int lc = (lane & 3) ^ ((row >> 2) & 3);
+                const uint32_t off = (m0 + row < P.M && 4 * lc < P.RS) ? (uint32_t)(row * P.RS + 4 * lc) * 4u : kOOB;
+                dma16(d, off, pf_lds + j * 1024);
+            }
+        }
+        if (EPI == 1) {
+            const sgpr4_t d = make_desc(P.ext, (uint32_t)P.ext_r * (uint32_t)N2);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int j = 2 * wave + q, kr = 2 * j + (lane >> 5);
+                const int col = n0 + 8 * ((lane & 31) ^ swz_w(kr));
+                const uint32_t off = (kr < P.ext_r && col < P.N) ? (uint32_t)(kr * P.N + col) * 2u : kOOB;
+                dma16(d, off, pf_lds + 16384 + j * 1024);
+            }
+        } else {
+            const uint32_t abytes = (uint32_t)P.N * (uint32_t)P.ext_r * 2u;
+            const uint32_t a0 = (uint32_t)n0 * (uint32_t)P.ext_r * 2u, ablk = 256u * (uint32_t)P.ext_r * 2u;
+            const sgpr4_t d = make_desc(P.ext, abytes);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int j = 2 * wave + q;
+                const uint32_t b = (uint32_t)(j * 64 + lane) * 16u;
+                dma16(d, (b < ablk && a0 + b < abytes) ? a0 + b : kOOB, pf_lds + 16384 + j * 1024);
+            }
+            const bool has_keep = P.keep != nullptr;
+            const sgpr4_t dk = make_desc(has_keep ? P.keep + (size_t)m0 * P.KW : P.keep,
+                                         has_keep ? clamp_bytes((uint64_t)(P.M - m0) * P.KW * 4u) : 0u);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int j = 2 * wave + q, row = 32 * j + (lane >> 1);
+                const int w = (n0 >> 5) + 4 * (lane & 1);
+                const uint32_t off = (has_keep && m0 + row < P.M && w < P.KW) ? (uint32_t)(row * P.KW + w) * 4u : kOOB;
+                dma16(dk, off, pf_lds + 24576 + j * 1024);
+            }
+        }
+    };
+
     const int nk = (P.K + BK - 1) / BK;
     // prologue: stages 0 and 1 in flight, wait for stage 0
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) dma_one(0, 0, j);
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j);
-    wait_vmcnt<NDMA>();
+    if constexpr (PF) epi_prefetch();
+    wait_vmcnt<PF ? NDMA + NPF : NDMA>();
     asm volatile("" ::: "memory");  // keep the LDS reads below the barrier
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -434,8 +491,30 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             constexpr bool pack = FAST == 2;
             const int lgr = pack ? (lg & 1) : lg;
             const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it, wcol0);
+            const lds_char *pf = (const lds_char *)smem + NST * STAGE_BYTES;
+            if constexpr (PF) __syncthreads();  // every wave's prefetch landed (K = 0 never waited)
             uint4 cf[NT16];
-            if (EPI == 2) {
+            if constexpr (PF && EPI == 2) {
+                // A rows of this wave's columns, ranks 8*lgr .. +7 (zero past r)
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) {
+                    const int c = wn * 128 + tn * 16 + l16;
+                    cf[tn] = 8 * lgr < it.r ? *(const uint4 *)(pf + 16384 + c * it.r * 2 + lgr * 16)
+                                            : make_uint4(0u, 0u, 0u, 0u);
+                }
+            } else if constexpr (PF) {
+                const int kr = 8 * lgr + (l16 >> 2);
+                const int swr = swz_w(kr);
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) {
+                    const int ch = wn * 16 + 2 * tn + ((l16 & 3) >> 1);
+                    const lds_char *pp = pf + 16384 + kr * 512 + ((ch ^ swr) << 4) + (l16 & 1) * 8;
+                    const uint2 lo = lds_read_tr4(pp), hi = lds_read_tr4(pp + 2048);
+                    cf[tn] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+#pragma unroll
+                for (int tn = 0; tn < NT16; tn += 2) mfma_src_ready(cf[tn], cf[tn + 1]);
+            } else if (EPI == 2) {
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn)
                     cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, 0, 16 * lgr + l16, true);
@@ -467,15 +546,36 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             }
             const int rb = 8 * lgr;
             float4 sv[NT16][2];
+            if constexpr (PF) {
+                // chunks 2*lgr, 2*lgr+1 of the row; the row's swizzle is (l16 >> 2)
 #pragma unroll
-            for (int tm = 0; tm < NT16; ++tm) {
-                const int row = wrow0 + tm * 16 + l16;
-                const uint32_t off = (row < P.M && rb < it.r) ? (uint32_t)((tm * 16 + l16) * P.RS + rb) * 4u : kOOB;
-                sv[tm][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off, 0, 0));
-                sv[tm][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off == kOOB ? kOOB : off + 16, 0, 0));
+                for (int tm = 0; tm < NT16; ++tm) {
+                    const lds_char *sr = pf + (wm * 128 + tm * 16 + l16) * 64;
+                    sv[tm][0] = *(const float4 *)(sr + (((2 * lgr) ^ (l16 >> 2)) << 4));
+                    sv[tm][1] = *(const float4 *)(sr + (((2 * lgr + 1) ^ (l16 >> 2)) << 4));
+                }
+            } else {
+#pragma unroll
+                for (int tm = 0; tm < NT16; ++tm) {
+                    const int row = wrow0 + tm * 16 + l16;
+                    const uint32_t off = (row < P.M && rb < it.r) ? (uint32_t)((tm * 16 + l16) * P.RS + rb) * 4u : kOOB;
+                    sv[tm][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off, 0, 0));
+                    sv[tm][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off == kOOB ? kOOB : off + 16, 0, 0));
+                }
             }
             uint32_t kwv[NT16][NT16 / 2];
-            if (EPI == 2) {
+            if (PF && EPI == 2) {
+                const bool has_keep = P.keep != nullptr;
+#pragma unroll
+                for (int tm = 0; tm < NT16; ++tm) {
+                    const uint4 w4 = has_keep ? *(const uint4 *)(pf + 24576 + (wm * 128 + tm * 16 + l16) * 32 + wn * 16)
+                                              : make_uint4(~0u, ~0u, ~0u, ~0u);
+                    kwv[tm][0] = w4.x;
+                    kwv[tm][1] = w4.y;
+                    kwv[tm][2] = w4.z;
+                    kwv[tm][3] = w4.w;
+                }
+            } else if (EPI == 2) {
                 const bool has_keep = P.keep != nullptr;
                 const __amdgpu_buffer_rsrc_t rK = make_rsrc(has_keep ? P.keep + (size_t)min(wrow0, P.M) * P.KW : P.keep,
                                                             has_keep ? (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.KW * 4u : 0u);
@@ -736,7 +836,7 @@ hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, voi
     auto al16 = [](const void *q) { return ((uintptr_t)q & 15) == 0; };
     const bool fast = !multi && epi != 0 && P.ext_r <= 32 && (P.ext_r & 7) == 0 && (RS & 7) == 0 &&
                       al16(Sx) && al16(P.ext) && (epi != 2 || ((KW & 3) == 0 && al16(keep)));
-    const bool pack = fast && P.ext_r <= 16;
+    const bool pack = fast && P.ext_r <= 16 && RS <= 16;
     if (nn) {
         if (epi == 0) return launch_gemm_t<true, 0, false, 0>(P, stream, "gemm_frozen_fwd");
         if (epi == 1) return multi ? launch_gemm_t<true, 1, true, 0>(P, stream, "gemm_f2_fwd_lora")
