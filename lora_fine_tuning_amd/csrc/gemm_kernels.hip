@@ -625,21 +625,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                         acc2[tn] = mfma16x16x32(cf[tn], hi, f32x4_t{0.f, 0.f, 0.f, 0.f});
                         if constexpr (!pack) acc2[tn] = mfma16x16x32(cf[tn], lo, acc2[tn]);
                     }
-                    const int row = wrow0 + tm * 16 + l16;
-                    if (row < P.M) {
+                    // Rows past M and columns past N are staged too; the flush
+                    // drops them.  A clear keep bit turns the LoRA term into +0
+                    // (AND with a sign-extended bit: no compare or select).
 #pragma unroll
-                        for (int tn = 0; tn < NT16; ++tn) {
-                            const int col = wcol0 + tn * 16 + 4 * lg;
-                            if (col >= P.N) continue;
-                            const uint32_t kw = kwv[tm][tn >> 1] >> (col & 31);
-                            float x[4];
+                    for (int tn = 0; tn < NT16; ++tn) {
+                        const uint32_t kw = kwv[tm][tn >> 1] >> (((tn & 1) << 4) + 4 * lg);
+                        float x[4];
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                x[e] = acc[tm][tn][e];
-                                if ((kw >> e) & 1u) x[e] += acc2[tn][e];
-                            }
-                            c_put(tm, tn, x[0], x[1], x[2], x[3]);
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t keep = (uint32_t)((int32_t)(kw << (31 - e)) >> 31);
+                            x[e] = acc[tm][tn][e] + __uint_as_float(__float_as_uint(acc2[tn][e]) & keep);
                         }
+                        c_put(tm, tn, x[0], x[1], x[2], x[3]);
                     }
                 }
             }
@@ -647,12 +645,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 mfma_drain();
 #pragma unroll
                 for (int tm = 0; tm < NT16; ++tm) {
-                    const int row = wrow0 + tm * 16 + l16;
-                    if (row >= P.M) continue;
 #pragma unroll
                     for (int tn = 0; tn < NT16; ++tn) {
-                        const int col = wcol0 + tn * 16 + 4 * lg;
-                        if (col >= P.N) continue;
                         const f32x4_t a4 = acc[tm][tn];
                         c_put(tm, tn, a4[0], a4[1], a4[2], a4[3]);
                     }
