@@ -66,6 +66,11 @@ struct GemmParams {
     const int64_t *seg_off;
     const int32_t *seg_adapter;
     int nseg;
+    // multi adapter: S / dS rows and mask rows meet the fast epilogue's
+    // alignment (RS % 8 == 0, 16-byte aligned; KW % 4 == 0, 16-byte aligned)
+    int multi_fast;
+    // mask rows 16-byte aligned with KW % 4 == 0 (one 16-byte load per row)
+    int keep16;
 };
 
 __device__ __forceinline__ void tile_coords(int wg, int G, int tiles_m, int tiles_n, int &tm, int &tn) {
@@ -479,9 +484,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     // load (the column-side fragments, the wave's 128 rows of S / dS and, for
     // B3, its keep words) is issued before any of them is used, so their
     // latencies overlap instead of adding up band by band.
-    if constexpr (FAST && EPI != 0 && !MULTI) {
-        ExtItem it;
-        get_item<EPI, MULTI>(P, 0, it);
+    // The fast epilogue for one adapter item `it` covering all of the wave's
+    // rows (r <= 32, a multiple of 8, 16-byte aligned rank-side matrix).
+    auto fast_epilogue = [&](const ExtItem &it) {
         {
             // FAST == 2 (r <= 16): one 32-deep MFMA per output tile carries both
             // halves of the fp32 row side -- K slots 0-15 hold the hi parts of
@@ -654,14 +659,33 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             }
         }
         c_flush();
+    };
+    if constexpr (FAST && EPI != 0 && !MULTI) {
+        ExtItem it;
+        get_item<EPI, MULTI>(P, 0, it);
+        fast_epilogue(it);
         return;
     } else {
+    // mixed adapters: the wave's first segment, found once
+    const int wseg = MULTI ? first_segment(P, wrow0) : 0;
+    if constexpr (MULTI && EPI == 2) {
+        // a wave whose rows all lie in one segment whose adapter meets the
+        // fast conditions takes the fast epilogue (wave-uniform decision; no
+        // barrier follows in either path)
+        ExtItem it;
+        if (P.multi_fast && wrow0 < P.M && wseg < P.nseg && get_item<EPI, MULTI>(P, wseg, it) &&
+            it.lo <= wrow0 && it.hi >= min(wrow0 + 128, P.M) && it.r <= 32 && (it.r & 7) == 0 &&
+            (((uintptr_t)it.w) & 15) == 0) {
+            fast_epilogue(it);
+            return;
+        }
+    }
 
     // ---- F2 (general path): alpha * S * B accumulated into acc
     if (EPI == 1) {
         int s_begin = 0, s_end = 1;
         if (MULTI) {
-            s_begin = first_segment(P, wrow0);
+            s_begin = wseg;
             s_end = P.nseg;
         }
         for (int s = s_begin; s < s_end; ++s) {
@@ -671,10 +695,35 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             if (it.hi <= wrow0 || it.lo >= wrow0 + 128) continue;
             const bool rvec = svec && (it.r & 7) == 0;
             const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it, wcol0);
+            // B rows 16-byte aligned: stage ranks rr0 .. rr0+31 of the wave's
+            // 128 columns through its 8 KiB past the stage ring and read them
+            // back transposed (as the fast epilogue does); else 2-byte loads
+            const bool bstage = (P.N & 7) == 0 && (((uintptr_t)it.w) & 15) == 0;
             for (int rr0 = 0; rr0 < it.r; rr0 += 32) {
                 uint4 cf[NT16];
+                if (bstage) {
+                    lds_char *bs = (lds_char *)smem + NST * STAGE_BYTES + wave * 8192;
 #pragma unroll
-                for (int tn = 0; tn < NT16; ++tn) cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, rr0, lane, false);
+                    for (int j = 0; j < 8; ++j) {
+                        const int q = lane + 64 * j, rr = q >> 4, c = q & 15;
+                        const uint32_t off = (rr0 + rr < it.r && wcol0 + 8 * c < P.N)
+                            ? ((uint32_t)(rr0 + rr) * (uint32_t)P.N + 8u * c) * 2u : kOOB;
+                        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
+                        *(uint4 *)(bs + rr * 256 + ((c ^ swz_w(rr)) << 4)) = v;
+                    }
+                    const int kr = 8 * lg + (l16 >> 2);
+                    const int swr = swz_w(kr);
+#pragma unroll
+                    for (int tn = 0; tn < NT16; ++tn) {
+                        const int ch = 2 * tn + ((l16 & 3) >> 1);
+                        const lds_char *pp = bs + kr * 256 + ((ch ^ swr) << 4) + (l16 & 1) * 8;
+                        const uint2 lo = lds_read_tr4(pp), hi = lds_read_tr4(pp + 1024);
+                        cf[tn] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    }
+                } else {
+#pragma unroll
+                    for (int tn = 0; tn < NT16; ++tn) cf[tn] = col_ext_frag<EPI>(P, rW, wcol0, it, wcol0 + tn * 16 + l16, rr0, lane, false);
+                }
 #pragma unroll
                 for (int tn = 0; tn < NT16; tn += 2) mfma_src_ready(cf[tn], cf[tn + 1]);
 #pragma unroll
@@ -712,11 +761,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     }
 
     // ---- output (B3 adds the masked rank-deep term one 16-row band at a time)
+    const bool has_keep = EPI == 2 && P.keep != nullptr;
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(has_keep ? P.keep + (size_t)min(wrow0, P.M) * P.KW : P.keep,
+                                                has_keep ? (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.KW * 4u : 0u);
 #pragma unroll
     for (int tm = 0; tm < NT16; ++tm) {
         const int row = wrow0 + tm * 16 + l16;
         f32x4_t acc2[NT16];
+        uint4 kw4 = make_uint4(~0u, ~0u, ~0u, ~0u);
         if (EPI == 2) {
+            // the band's mask words (the wave's 128 columns are 4 words of each
+            // row), issued ahead of its rank-deep loads
+            if (has_keep && P.keep16)
+                kw4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rK, (uint32_t)((tm * 16 + l16) * P.KW + (wcol0 >> 5)) * 4u, 0, 0));
 #pragma unroll
             for (int tn = 0; tn < NT16; ++tn) acc2[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (!MULTI && one_chunk) {
@@ -731,7 +789,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 const int band0 = wrow0 + tm * 16;
                 int s_begin = 0, s_end = 1;
                 if (MULTI) {
-                    s_begin = first_segment(P, band0);
+                    // first segment ending past the band, stepping on from the wave's
+                    s_begin = wseg;
+                    while (s_begin < P.nseg && P.seg_off[s_begin + 1] <= (int64_t)band0) ++s_begin;
                     s_end = P.nseg;
                 }
                 for (int s = s_begin; s < s_end; ++s) {
@@ -755,23 +815,43 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 }
             }
         }
-        if (row < P.M) {
+        if constexpr (EPI != 2) {
+            if (row < P.M) {
 #pragma unroll
-            for (int tn = 0; tn < NT16; ++tn) {
-                const int col = wcol0 + tn * 16 + 4 * lg;
-                if (col >= P.N) continue;
-                uint32_t kw = 0xFFFFFFFFu;
-                if (EPI == 2 && P.keep != nullptr) kw = P.keep[(size_t)row * P.KW + (col >> 5)] >> (col & 31);
-                float x[4];
+                for (int tn = 0; tn < NT16; ++tn) {
+                    const int col = wcol0 + tn * 16 + 4 * lg;
+                    if (col >= P.N) continue;
+                    const f32x4_t a4 = acc[tm][tn];
+                    c_put(tm, tn, a4[0], a4[1], a4[2], a4[3]);
+                }
+            }
+            continue;
+        }
+        // rows past M and columns past N are staged too; the flush drops them
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = acc[tm][tn][e];
-                    if (EPI == 2) {
-                        if ((kw >> e) & 1u) x[e] += acc2[tn][e];
+        for (int tn = 0; tn < NT16; ++tn) {
+            float x[4];
+            if (EPI == 2) {
+                uint32_t kw = ~0u;
+                if (has_keep) {
+                    if (P.keep16) {
+                        const uint32_t w = (tn >> 1) == 0 ? kw4.x : (tn >> 1) == 1 ? kw4.y : (tn >> 1) == 2 ? kw4.z : kw4.w;
+                        kw = w >> (((tn & 1) << 4) + 4 * lg);
+                    } else {
+                        const int col = wcol0 + tn * 16 + 4 * lg;
+                        kw = (row < P.M && col < P.N) ? P.keep[(size_t)row * P.KW + (col >> 5)] >> (col & 31) : 0u;
                     }
                 }
-                c_put(tm, tn, x[0], x[1], x[2], x[3]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t keep = (uint32_t)((int32_t)(kw << (31 - e)) >> 31);
+                    x[e] = acc[tm][tn][e] + __uint_as_float(__float_as_uint(acc2[tn][e]) & keep);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = acc[tm][tn][e];
             }
+            c_put(tm, tn, x[0], x[1], x[2], x[3]);
         }
     }
     c_flush();
@@ -831,6 +911,8 @@ hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, voi
     const bool fast = !multi && epi != 0 && P.ext_r <= 32 && (P.ext_r & 7) == 0 && (RS & 7) == 0 &&
                       al16(Sx) && al16(P.ext) && (epi != 2 || ((KW & 3) == 0 && al16(keep)));
     const bool pack = fast && P.ext_r <= 16 && RS <= 16;
+    P.keep16 = (KW & 3) == 0 && al16(keep);
+    P.multi_fast = multi && epi != 0 && (RS & 7) == 0 && al16(Sx) && (epi != 2 || ((KW & 3) == 0 && al16(keep)));
     if (nn) {
         if (epi == 0) return launch_gemm_t<true, 0, false, 0>(P, stream, "gemm_frozen_fwd");
         if (epi == 1) return multi ? launch_gemm_t<true, 1, true, 0>(P, stream, "gemm_f2_fwd_lora")
