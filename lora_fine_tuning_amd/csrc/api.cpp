@@ -254,7 +254,7 @@ BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_
     p.chunk_cap_bwd = cdiv(m, kBwdRows) + (multi ? nseg : 0);
     p.chunk_cap_f1 = cdiv(m, kF1Rows) + (multi ? nseg : 0);
     const int rl = ((RS + 15) / 16) * 16;
-    p.b1 = b1_shape(m, n, rl, multi, nseg);
+    p.b1 = b1_shape(m, n, rl, RS, multi, nseg);
     p.C2 = rl <= 128 ? 256 : 128;
     p.ds_parts = p.b1.CT;
     Carve c;

@@ -17,9 +17,17 @@ constexpr int kF1Rows = 64;    // mask + down-projection
 constexpr int kBwdRows = 256;  // dS/dB and dA kernels
 constexpr int kF1KSub = 128;   // k columns per staged slice of A in F1
 
+// The streaming low-rank kernels work on ranks in tiles of up to 32; ranks
+// above 32 take ceil(r/32) tiles of 32 (one launch, one tile per grid slice).
+inline int rank_tiles(int r_lds) { return r_lds > 32 ? (r_lds + 31) / 32 : 1; }
+
 // F1's streaming form (each work-group covers all of k, no partial sums)
-// serves ranks up to 32; its 32-bit buffer offsets need 64*k < 2^31.
-inline bool f1_streaming(int r_lds, int64_t k) { return r_lds <= 32 && k * 64 < (int64_t(1) << 31); }
+// serves ranks up to 128; its 32-bit buffer offsets need 64*k < 2^31.
+inline bool f1_streaming(int r_lds, int64_t k) { return r_lds <= 128 && k * 64 < (int64_t(1) << 31); }
+
+// B1 / B2 streaming forms: ranks up to 32, or up to 128 in rank tiles when
+// the S / dS row stride is a multiple of 4 floats (16-byte row pieces).
+inline bool bwd_streaming(int r_lds, int RS) { return r_lds <= 32 || (r_lds <= 128 && RS % 4 == 0); }
 
 // Kernel timing hooks (api.cpp).  prof_begin returns a slot or -1.
 int prof_begin(const char *name, hipStream_t stream);
@@ -77,10 +85,10 @@ struct B1Shape {
     int cw;  // streaming: C1 = 256 * cw
     int C1, CT, rows, slots;
 };
-inline B1Shape b1_shape(int64_t m, int64_t n, int r_lds, bool multi, int nseg) {
+inline B1Shape b1_shape(int64_t m, int64_t n, int r_lds, int RS, bool multi, int nseg) {
     B1Shape s{};
     const int64_t maxrows = ((int64_t(1) << 31) - 1) / (2 * n) / 32 * 32;
-    s.streaming = r_lds <= 32 && maxrows >= 32;
+    s.streaming = bwd_streaming(r_lds, RS) && maxrows >= 32;
     if (!s.streaming) {
         s.cw = 1;
         s.C1 = r_lds <= 128 ? 256 : 128;

@@ -292,6 +292,18 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
     if (row_lo >= row_hi) return;
     row_hi = min(row_hi, row_lo + 16);
     const int r = ad.r;
+    // rank tile blockIdx.y: ranks r0 .. r0+RL-1 of S (ranks above 32 take
+    // several tiles; each reads X again and only the first writes the mask)
+    const int r0 = blockIdx.y * RL;
+    const int ncol = min(RL, P.RS - r0);  // S columns this tile writes
+    if (r0 >= r) {
+        // no ranks of this adapter here: the tile's S columns are zero
+        for (int i = tid; i < 16 * RL; i += 64 * F1S_WAVES) {
+            const int rr = i / RL, cl = i % RL;
+            if (cl < ncol && row_lo + rr < row_hi) P.out[(size_t)(row_lo + rr) * P.RS + r0 + cl] = 0.f;
+        }
+        return;
+    }
     const uint32_t T = drop_threshold(ad.p);
     const uint32_t tm1x2 = ((T - 1u) & 0xFFFFu) * 0x00010001u;  // used only when T >= 1
     const float s = drop_scale(ad.p);
@@ -311,9 +323,9 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
     const int kb = wave * kq, ke = min(P.k, kb + kq);
     const int nu = ke > kb ? (ke - kb + F1S_UNIT - 1) / F1S_UNIT : 0;
     lds_char *slab0 = smem + wave * 2 * SLAB;
-    const bool avec = r == RL && (((uintptr_t)ad.A) & 15) == 0;
+    const bool avec = (r & 7) == 0 && (((uintptr_t)ad.A) & 15) == 0;
     // A rows below ke (rows at or past ke read as zero)
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(ad.A, (size_t)max(ke, 0) * RL * 2);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(ad.A, (size_t)max(ke, 0) * r * 2);
 
     f32x4_t acc[MAXT];
 #pragma unroll
@@ -327,10 +339,12 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
             xv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
         }
     };
+    // 16-byte vector q of the slab: k row q / (RL/8), ranks r0 + 8 (q % (RL/8)) .. +7
     auto load_a = [&](int c, uint4 (&av)[NAV]) {
 #pragma unroll
         for (int j = 0; j < NAV; ++j) {
-            const uint32_t off = (uint32_t)c * (RL * 2) + (uint32_t)(lane + 64 * j) * 16u;
+            const int q = lane + 64 * j, kk = q / (RL / 8), v = q % (RL / 8);
+            const uint32_t off = r0 + 8 * v < r ? ((uint32_t)(c + kk) * (uint32_t)r + (uint32_t)(r0 + 8 * v)) * 2u : kOOB;
             av[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0));
         }
     };
@@ -342,7 +356,7 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
         for (int q = lane; q < F1S_UNIT * RL; q += 64) {
             const int kk = q / RL, rr = q % RL;
             uint16_t v = 0;
-            if (c + kk < ke && rr < r) v = ad.A[(size_t)(c + kk) * r + rr];
+            if (c + kk < ke && r0 + rr < r) v = ad.A[(size_t)(c + kk) * r + r0 + rr];
             *(uint16_t *)(dst + q * 2) = v;
         }
     };
@@ -388,7 +402,7 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
                 acc[bt] = mfma16x16x32(xm, make_uint4(lo.x, lo.y, hi.x, hi.y), acc[bt]);
             }
         }
-        if (P.keep_bits != nullptr) {
+        if (P.keep_bits != nullptr && r0 == 0) {
             // 4x4 byte transpose across the lanes of a row (groups g): byte t of
             // lane g holds group g's bits of step t; afterwards lane g holds the
             // word of step g, byte j from group j.
@@ -417,17 +431,17 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * g + v) * RL + 16 * bt + l16] = acc[bt][v];
     __syncthreads();
-    for (int i = tid; i < 16 * P.RS; i += 64 * F1S_WAVES) {
-        const int rr = i / P.RS, cc = i % P.RS;
+    for (int i = tid; i < 16 * RL; i += 64 * F1S_WAVES) {
+        const int rr = i / RL, cl = i % RL;
         const int orow = row_lo + rr;
-        if (orow >= row_hi) continue;
+        if (orow >= row_hi || cl >= ncol) continue;
         float v = 0.f;
-        if (cc < r) {
+        if (r0 + cl < r) {
 #pragma unroll
-            for (int w = 0; w < F1S_WAVES; ++w) v += red[(w * 16 + rr) * RL + cc];
+            for (int w = 0; w < F1S_WAVES; ++w) v += red[(w * 16 + rr) * RL + cl];
             v *= s;
         }
-        P.out[(size_t)orow * P.RS + cc] = v;
+        P.out[(size_t)orow * P.RS + r0 + cl] = v;
     }
 }
 
@@ -496,6 +510,7 @@ struct B1Params {
     float *dSpart;  // [CT][m][RS]
     float *dBpart;  // [chunk][RS][n]
     int r_lds;
+    int tiled;  // rank tiles of 32 (blockIdx.z); S staged 32 columns per row (RS % 4 == 0)
 };
 
 template <int C1, int MAXT>
@@ -676,6 +691,7 @@ struct B2Params {
     RowWork work;
     float *dApart;  // [chunk][k][RS]
     int r_lds;
+    int tiled;  // rank tiles of 32 (blockIdx.z); dS staged 32 columns per row (RS % 4 == 0)
 };
 
 template <int C2, int MAXT>
@@ -843,7 +859,14 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
     AdapterView ad;
     if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
     const int r = ad.r;
-    const int nbt = (r + 15) >> 4;
+    constexpr int RL = 16 * MAXT;
+    // rank tile (tiled launches): ranks r0 .. r0+RL-1; dS rows staged as RL
+    // floats (else the whole RS-float rows, r0 = 0)
+    const int r0 = P.tiled ? (int)blockIdx.z * RL : 0;
+    if (r0 >= r) return;  // partial columns past r are never read
+    const int rt = min(r - r0, RL);
+    const int nbt = (rt + 15) >> 4;
+    const int sst = P.tiled ? 32 : P.RS;  // LDS row stride of the staged dS (tiled: RL = 32)
     const float s = drop_scale(ad.p);
     const int k0 = blockIdx.y * 256;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -881,6 +904,12 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
                 const uint32_t off = (has_mask && w0 < P.KW)
                     ? (uint32_t)((((size_t)sb * B2S_ROWS + (lane >> 1)) * P.KW + w0) * 4) : kOOBL;
                 dma16(dK, off, dst);
+            } else if (P.tiled) {
+                // slot q: rows 8(q-1) + lane/8, 16-byte chunk lane % 8 of the tile's columns
+                const int row = 8 * (slot - 1) + (lane >> 3), cc = r0 + 4 * (lane & 7);
+                const uint32_t off = (slot <= 4 && cc < P.RS)
+                    ? (uint32_t)((((size_t)sb * B2S_ROWS + row) * P.RS + cc) * 4) : kOOBL;
+                dma16(dD, off, dst);
             } else {
                 const uint32_t b = (uint32_t)(slot - 1) * 1024 + lane * 16;
                 dma16(dD, b < dsb ? (uint32_t)sb * dsb + b : kOOBL, dst);
@@ -913,8 +942,8 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 // in-bounds for every lane (rows < 32, RS and rr < 32): read, then select
-                const float dv = ds[(8 * g + e) * P.RS + rr];
-                v[e] = (bt < nbt && rr < r) ? s * dv : 0.f;
+                const float dv = ds[(8 * g + e) * sst + rr];
+                v[e] = (bt < nbt && rr < rt) ? s * dv : 0.f;
             }
             split_frag(v, bhi[bt], blo[bt]);
         }
@@ -958,7 +987,7 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int kk = k0 + (4 * wave + mb) * 16 + 4 * g + v;
-                    if (kk < P.k && rr < r) dap[(size_t)kk * P.RS + rr] = acc[mb][bt][v];
+                    if (kk < P.k && rr < rt) dap[(size_t)kk * P.RS + r0 + rr] = acc[mb][bt][v];
                 }
             }
         }
@@ -995,6 +1024,19 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     const float alpha = ad.alpha;
     const int ct = blockIdx.y, n0 = ct * 256 * CW;
     const int tid = threadIdx.x, lane = tid & 63;
+    // rank tile (tiled launches, RL = 32): ranks r0 .. r0+31; S rows staged as
+    // 32 floats (else whole RS-float rows, r0 = 0)
+    const int r0 = P.tiled ? (int)blockIdx.z * RL : 0;
+    const int sst = P.tiled ? 32 : P.RS;
+    float *dsp = P.dSpart + (size_t)ct * P.m * P.RS;
+    if (r0 >= r) {
+        // no ranks here: this tile's columns of the dS partial are zero
+        for (int i = tid; i < (row_hi - row_lo) * RL; i += 256) {
+            const int rr = i / RL, cc = r0 + i % RL;
+            if (cc < P.RS) dsp[(size_t)(row_lo + rr) * P.RS + cc] = 0.f;
+        }
+        return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
     const int nrows = row_hi - row_lo;
@@ -1025,8 +1067,15 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
             for (int j = 0; j < 4; ++j)
                 dma16(dYd, (!live || offY[t][j] == kOOBL) ? kOOBL : offY[t][j] + yo,
                       base + t * B1V_SUB + (4 * wave + j) * 1024);
-        const uint32_t b = (uint32_t)wave * 1024 + lane * 16;
-        dma16(dSd, (live && b < sbb) ? (uint32_t)sb * sbb + b : kOOBL, base + SY + wave * 1024);
+        if (P.tiled) {
+            // wave w: rows 8w + lane/8, 16-byte chunk lane % 8 of the tile's 32 columns
+            const int row = 8 * wave + (lane >> 3), cc = r0 + 4 * (lane & 7);
+            dma16(dSd, (live && cc < P.RS) ? (uint32_t)(((size_t)sb * 32 + row) * P.RS + cc) * 4u : kOOBL,
+                  base + SY + wave * 1024);
+        } else {
+            const uint32_t b = (uint32_t)wave * 1024 + lane * 16;
+            dma16(dSd, (live && b < sbb) ? (uint32_t)sb * sbb + b : kOOBL, base + SY + wave * 1024);
+        }
     };
 
     // B fragments for dS: rank 16bt + li, columns n0 + 64CW w + 32q + 8g .. +7
@@ -1037,7 +1086,7 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int bt = 0; bt < MAXT; ++bt) {
-                const int rank = 16 * bt + li;
+                const int rank = r0 + 16 * bt + li;
                 const int col = n0 + 64 * CW * wave + 32 * q + 8 * g;
                 const uint32_t off = (rank < r && col < P.n) ? (uint32_t)(rank * P.n + col) * 2u : kOOB;
                 bfr[q][bt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0));
@@ -1054,7 +1103,6 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     for (int q = 0; q < NST - 1; ++q) issue(q, q);
     wait_vmcnt<NDMA * (NST - 2)>();
     __syncthreads();
-    float *dsp = P.dSpart + (size_t)ct * P.m * P.RS;
     // sum of the four waves' dS shares of sub-block sb (after the barrier)
     // thread t handles row t / 8 of the sub-block, columns t % 8, +8, ...
     auto flush_ds = [&](int sb) {
@@ -1064,9 +1112,8 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
         float *drow = dsp + (size_t)(rs + rr) * P.RS;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int cc = (tid & 7) + 8 * j;
-            if (cc >= P.RS) break;
-            const int cl = min(cc, RL - 1);
+            const int cl = (tid & 7) + 8 * j, cc = r0 + cl;
+            if (cl >= RL || cc >= P.RS) break;
             float v = rd[(0 * 32 + rr) * RL + cl];
             v += rd[(1 * 32 + rr) * RL + cl];
             v += rd[(2 * 32 + rr) * RL + cl];
@@ -1115,8 +1162,8 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 // in-bounds for every lane (rows < 32, RS and rr < 32): read, then select
-                const float sv = st[(8 * g + e) * P.RS + rr];
-                v[e] = rr < r ? alpha * sv : 0.f;
+                const float sv = st[(8 * g + e) * sst + rr];
+                v[e] = r0 + rr < r ? alpha * sv : 0.f;
             }
             split_frag(v, ahi[bt], alo[bt]);
         }
@@ -1146,7 +1193,7 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
             const int col = n0 + 16 * (NB * wave + b) + li;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int rr = 16 * bt + 4 * g + v;
+                const int rr = r0 + 16 * bt + 4 * g + v;
                 if (rr < r && col < P.n) dbp[(size_t)rr * P.n + col] = accB[bt][b][v];
             }
         }
@@ -1323,8 +1370,9 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
     (void)hipGetLastError();
     const int slot = prof_begin("f1_mask_down", stream);
     if (f1_streaming(P.r_lds, k)) {
-        // streaming form: 4 work-groups of 16 rows per chunk, all of k each
-        const dim3 g4(4 * chunk_cap);
+        // streaming form: 4 work-groups of 16 rows per chunk, all of k each,
+        // times the rank tiles
+        const dim3 g4(4 * chunk_cap, rank_tiles(P.r_lds));
         if (P.r_lds <= 16)
             launch_with_lds(f1s_kernel<1>, g4, (size_t)F1S_WAVES * 2 * F1S_UNIT * 16 * 2, stream, P, 64 * F1S_WAVES);
         else
@@ -1371,11 +1419,13 @@ hipError_t launch_b1(const void *dY, const float *S, int m, int n, int RS, const
     P.dSpart = dSpart;
     P.dBpart = dBpart;
     P.r_lds = r_lds_of(src);
+    P.tiled = P.r_lds > 32;
     (void)hipGetLastError();
     const int slot = prof_begin("b1_ds_db", stream);
-    const dim3 grid(sh.slots, sh.CT);
+    const dim3 grid(sh.slots, sh.CT, sh.streaming ? rank_tiles(P.r_lds) : 1);
     if (sh.streaming) {
         if (sh.cw != 1) return hipErrorInvalidValue;  // the streaming kernel is built for 256-column tiles
+        if (P.tiled && RS % 4 != 0) return hipErrorInvalidValue;  // tiles stage 16-byte row pieces
         const int rl = P.r_lds <= 16 ? 16 : 32;
         // ring depth 3: two stages in flight, two work-groups per CU
         auto lds_of = [&](int nst) {
@@ -1413,11 +1463,13 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
     P.work = make_work(src, kTabBwd);
     P.dApart = dApart;
     P.r_lds = r_lds_of(src);
+    P.tiled = P.r_lds > 32;
     const size_t lds = b2_lds_bytes(C2, P.r_lds);
     (void)hipGetLastError();
     const int slot = prof_begin("b2_da", stream);
-    const dim3 grid(chunk_cap, cdiv(k, C2));
-    if (C2 == 256 && P.r_lds <= 32) {
+    const bool streaming = C2 == 256 && bwd_streaming(P.r_lds, RS);
+    const dim3 grid(chunk_cap, cdiv(k, C2), streaming ? rank_tiles(P.r_lds) : 1);
+    if (streaming) {
         const size_t slds = (size_t)B2S_NST * B2S_STAGE;
         if (P.r_lds <= 16) launch_with_lds(b2s_kernel<1>, grid, slds, stream, P);
         else launch_with_lds(b2s_kernel<2>, grid, slds, stream, P);

@@ -76,7 +76,7 @@ def _fwd(lib, **kw):
     (dict(offset=4), INVALID),            # offset % 8
     (dict(keep=None), INVALID),           # keep_bits required when p > 0
     (dict(S=FAKE + 2), INVALID),          # S 4-byte aligned
-    (dict(m=512, k=4096, r=64, wsb=0), WORKSPACE),  # rank 64 needs split-k partials
+    (dict(m=512, k=4096, r=256, wsb=0), WORKSPACE),  # rank 256 needs split-k partials
     (dict(r=256, n=1 << 22), UNSUPPORTED),    # B of 256 x 2^22 bf16 = 2 GiB
 ])
 def test_fwd_rejects(lib, kw, status):
@@ -165,10 +165,12 @@ def test_workspace_sizes():
     s1 = lf.lora_linear_bwd_workspace_size(8192, 4096, 4096, 16)
     s2 = lf.lora_linear_bwd_workspace_size(16384, 4096, 4096, 16)
     assert 0 < s1 < s2
-    # ranks up to 32: F1 finishes S inside each work-group, no partials
+    # ranks up to 128: F1 finishes S inside each work-group (rank tiles of
+    # 32 above 32), no partials; larger ranks split k
     assert lf.lora_linear_fwd_workspace_size(512, 1024, 1024, 16) == 0
     assert lf.lora_linear_fwd_workspace_size(8192, 4096, 4096, 32) == 0
-    assert lf.lora_linear_fwd_workspace_size(512, 1024, 1024, 64) > 0
+    assert lf.lora_linear_fwd_workspace_size(8192, 4096, 4096, 128) == 0
+    assert lf.lora_linear_fwd_workspace_size(512, 1024, 1024, 256) > 0
     assert lf.multi_lora_bwd_workspace_size(8192, 28672, 8192, 128, 8, 8) > \
         lf.lora_linear_bwd_workspace_size(8192, 28672, 8192, 128)
 

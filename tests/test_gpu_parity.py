@@ -54,6 +54,9 @@ SINGLE_CASES = [
     (300, 264, 136, 8, 2.0, 0.1),      # all-loads-first epilogue, ragged m and n
     (257, 512, 520, 24, 1.5, 0.3),     # same epilogue, rank 24
     (1000, 1024, 776, 32, 2.0, 0.0),   # same epilogue, rank 32, no dropout
+    (700, 512, 520, 64, 2.0, 0.1),     # two rank tiles of 32
+    (333, 264, 264, 36, 1.0, 0.2),     # rank tiles, second one ragged (rank not a multiple of 8)
+    (520, 1024, 264, 96, 0.5, 0.1),    # three rank tiles
 ]
 
 
