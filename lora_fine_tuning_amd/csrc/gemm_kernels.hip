@@ -742,21 +742,24 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         mfma_drain();
     }
 
-    // ---- B3, single adapter with r <= 32: the column-side A fragments are
-    // the same for every 16-row band, loaded once
-    uint4 cf1[NT16];
-    bool one_chunk = false;
+    // ---- B3, single adapter with r <= 64: the column-side A fragments (one
+    // or two rank chunks of 32) are the same for every 16-row band, loaded once
+    uint4 cf1[2][NT16];
+    bool one_chunk = false;  // r <= 64 (the name predates the second chunk)
     ExtItem it1;
     bool rvec1 = false;
     if (EPI == 2 && !MULTI) {
         get_item<EPI, MULTI>(P, 0, it1);
-        one_chunk = it1.r <= 32;
+        one_chunk = it1.r <= 64;
         rvec1 = svec && (it1.r & 7) == 0;
         if (one_chunk) {
             const bool avec = (it1.r & 7) == 0 && (((uintptr_t)it1.w) & 15) == 0;
             const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it1, wcol0);
 #pragma unroll
-            for (int tn = 0; tn < NT16; ++tn) cf1[tn] = col_ext_frag<EPI>(P, rW, wcol0, it1, wcol0 + tn * 16 + l16, 0, lane, avec);
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn)
+                    cf1[c][tn] = col_ext_frag<EPI>(P, rW, wcol0, it1, wcol0 + tn * 16 + l16, 32 * c, lane, avec);
         }
     }
 
@@ -778,12 +781,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
             for (int tn = 0; tn < NT16; ++tn) acc2[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (!MULTI && one_chunk) {
-                uint4 hi, lo;
-                row_ext_frags(P, rS, wrow0, it1, row, 0, lane, rvec1, hi, lo);
+                // both chunks' row-side loads first; the second is all zeros
+                // (out-of-range offsets) when r <= 32
+                uint4 hi0, lo0, hi1, lo1;
+                row_ext_frags(P, rS, wrow0, it1, row, 0, lane, rvec1, hi0, lo0);
+                row_ext_frags(P, rS, wrow0, it1, row, 32, lane, rvec1, hi1, lo1);
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) {
-                    acc2[tn] = mfma16x16x32(cf1[tn], hi, acc2[tn]);
-                    acc2[tn] = mfma16x16x32(cf1[tn], lo, acc2[tn]);
+                    acc2[tn] = mfma16x16x32(cf1[0][tn], hi0, acc2[tn]);
+                    acc2[tn] = mfma16x16x32(cf1[0][tn], lo0, acc2[tn]);
+                }
+                if (it1.r > 32) {
+#pragma unroll
+                    for (int tn = 0; tn < NT16; ++tn) {
+                        acc2[tn] = mfma16x16x32(cf1[1][tn], hi1, acc2[tn]);
+                        acc2[tn] = mfma16x16x32(cf1[1][tn], lo1, acc2[tn]);
+                    }
                 }
             } else {
                 const int band0 = wrow0 + tm * 16;
