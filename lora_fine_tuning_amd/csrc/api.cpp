@@ -205,7 +205,8 @@ struct FwdPlan {
     int chunk_cap_f1;  // grid size of F1 (upper bound on chunks)
     int chunk_cap_bwd;
     int KS, ksl;
-    size_t off_spart, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
+    int s2_rp;  // > 0: F1 writes alpha*S as bf16 hi | lo rows of 2*s2_rp for the GEMM's extra K
+    size_t off_spart, off_s2, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
     size_t bytes;
 };
 
@@ -224,8 +225,13 @@ FwdPlan plan_fwd(int64_t m, int64_t k, int32_t RS, bool multi, int32_t nseg) {
     const int per = cdiv(kslices, KS);
     p.ksl = per * kF1KSub;
     p.KS = cdiv(k, p.ksl);
+    // single adapter, ranks 33..128 (streaming F1): the up-projection runs as
+    // extra K columns of the forward GEMM, fed by F1's split of alpha*S
+    const int rl = ((RS + 15) / 16) * 16;
+    p.s2_rp = (!multi && rl > 32 && p.KS == 1) ? rank_tiles(rl) * 32 : 0;
     Carve c;
     p.off_spart = c.take(p.KS > 1 ? (size_t)p.KS * m * RS * sizeof(float) : 0);
+    p.off_s2 = c.take((size_t)m * 2 * p.s2_rp * sizeof(uint16_t));
     if (multi) {
         p.off_t_f1 = c.take((size_t)p.chunk_cap_f1 * sizeof(ChunkEntry));
         p.off_c_f1 = c.take(sizeof(int32_t));
@@ -337,12 +343,17 @@ extern "C" lora_status lora_linear_fwd(const void *X, const void *W, const void 
 
     AdapterSource src = single_source(A, B, nullptr, nullptr, r, alpha, p);
     float *sout = pl.KS > 1 ? (float *)ws_at(workspace, pl.off_spart) : S;
+    // the extra-K form needs B's rows 16-byte aligned (n % 8 == 0 is checked above)
+    uint16_t *s2 = (pl.s2_rp > 0 && aligned(B, 16)) ? (uint16_t *)ws_at(workspace, pl.off_s2) : nullptr;
     HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r, pl.KS,
-                     pl.ksl, stream), "F1 launch");
+                     pl.ksl, stream, s2, pl.s2_rp), "F1 launch");
     if (pl.KS > 1)
         HIPCHK(launch_sum_partials(sout, pl.KS, (size_t)m * r, (size_t)m * r, S, "sum_s_partials", stream),
                "S reduction launch");
-    HIPCHK(launch_gemm(true, 1, X, W, Y, (int)m, (int)n, (int)k, S, r, nullptr, 0, src, stream), "F2 launch");
+    if (s2)
+        HIPCHK(launch_gemm_kext(X, W, Y, (int)m, (int)n, (int)k, s2, 2 * pl.s2_rp, B, r, stream), "F2 launch");
+    else
+        HIPCHK(launch_gemm(true, 1, X, W, Y, (int)m, (int)n, (int)k, S, r, nullptr, 0, src, stream), "F2 launch");
     return LORA_OK;
 }
 

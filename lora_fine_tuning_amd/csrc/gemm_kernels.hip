@@ -71,6 +71,11 @@ struct GemmParams {
     int multi_fast;
     // mask rows 16-byte aligned with KW % 4 == 0 (one 16-byte load per row)
     int keep16;
+    // epi 3 (forward, ranks 33..128): the LoRA term as kx = 2*RP extra K
+    // columns -- S2 (M x kx bf16: alpha*S split, [hi | lo] of RP ranks each)
+    // against B's rows (rank j for extra column j and RP + j; past r zero)
+    const uint16_t *S2;
+    int kx;
 };
 
 __device__ __forceinline__ void tile_coords(int wg, int G, int tiles_m, int tiles_n, int &tm, int &tn) {
@@ -268,9 +273,45 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         }
     }
 
-    // DMA load j (0..NDMA-1) of the stage starting at k0 into LDS stage `stage`
-    auto dma_one = [&](int k0, int stage, int j) {
+    // epi 3: geometry of the extra K stages (S2 rows stride kx; B rows by
+    // extra column, the W tile's chunk swizzle)
+    constexpr bool KEXT = EPI == 3;
+    const int nkx = (P.K + BK - 1) / BK;  // stages of X / W before the extra ones
+    uint32_t offX2[LPW];
+    if (KEXT) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int r = (wave * LPW + j) * RPI + lane / CPR;
+            const int c = (lane % CPR) ^ swz_rows(r);
+            offX2[j] = (uint32_t)(r * P.kx * 2 + c * 16);
+        }
+    }
+    const sgpr4_t dX2 = make_desc(KEXT ? P.S2 + (size_t)m0 * P.kx : P.Arow,
+                                  KEXT ? clamp_bytes((uint64_t)(P.M - m0) * P.kx * 2u) : 0u);
+    const sgpr4_t dBx = make_desc(P.ext, KEXT ? clamp_bytes((uint64_t)P.ext_r * N2) : 0u);
+
+    // DMA load j (0..NDMA-1) of the stage starting at k0 into LDS stage
+    // `stage`; extra_c (compile-time) selects an extra-K stage of epi 3
+    auto dma_one = [&](int k0, int stage, int j, auto extra_c) {
+        constexpr bool EXTRA = decltype(extra_c)::value;
         const uint32_t sa = smem_lds + stage * STAGE_BYTES + wave * LPW * 1024;
+        if constexpr (EXTRA) {
+            const int kx0 = k0 - nkx * BK;  // first extra column of the stage
+            if (j < LPW) {
+                const uint32_t off = (kx0 + colK[j] < P.kx) ? offX2[j] + (uint32_t)(kx0 * 2) : kOOB;
+                dma16(dX2, off, sa + j * 1024);
+            } else {
+                const int jj = j - LPW;
+                const int kr = (wave * LPW + jj) * 2 + lane / 32;
+                const int c = (lane % 32) ^ swz_w(kr);
+                const int kp = kx0 + kr, rp = P.kx >> 1;
+                const int brow = kp < rp ? kp : kp - rp;
+                const uint32_t off = (kp < P.kx && brow < P.ext_r)
+                    ? (uint32_t)(brow * N2 + (size_t)(n0 + c * 8) * 2) : kOOB;
+                dma16(dBx, off, sa + TILE_BYTES + jj * 1024);
+            }
+            return;
+        }
         if (j < LPW) {
             const uint32_t off = (k0 + colK[j] < P.K) ? offK[j] + (uint32_t)(k0 * 2) : kOOB;
             dma16(dA, off, sa + j * 1024);
@@ -335,9 +376,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 
     // 64 MFMAs of fragment slot `sl`; MFMA i is followed by side work: for
     // i % 4 == 0 the fragment read i/4 of (rstage, rks) into slot rsl, and for
-    // i % 4 == 2 the DMA load i/4 of the stage at dk0 into dstage.  READ and
-    // DMA are compile-time flags so the MFMA stream carries no branches.
-    auto mfma_step = [&](int sl, auto read_c, int rstage, int rks, int rsl, auto dma_c, int dk0, int dstage) {
+    // i % 4 == 2 the DMA load i/4 of the stage at dk0 into dstage.  READ, DMA
+    // and EXTRA (the DMA is of an extra-K stage) are compile-time flags so the
+    // MFMA stream carries no branches.
+    auto mfma_step = [&](int sl, auto read_c, int rstage, int rks, int rsl, auto dma_c, int dk0, int dstage,
+                         auto extra_c) {
         constexpr bool READ = decltype(read_c)::value, DMA = decltype(dma_c)::value;
 #pragma unroll
         for (int i = 0; i < NT16 * NT16; ++i) {
@@ -347,7 +390,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 if ((i & 3) == 0) read_frag(rstage, rks, rsl, (i >> 2) & 1, i >> 3);
             }
             if constexpr (DMA) {
-                if ((i & 3) == 2) dma_one(dk0, dstage, i >> 2);
+                if ((i & 3) == 2) dma_one(dk0, dstage, i >> 2, extra_c);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -411,12 +454,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         }
     };
 
-    const int nk = (P.K + BK - 1) / BK;
+    const int nk = nkx + (KEXT ? (P.kx + BK - 1) / BK : 0);
     // prologue: stages 0 and 1 in flight, wait for stage 0
+    if (KEXT && nkx < 1) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_one(0, 0, j);
+        for (int j = 0; j < NDMA; ++j) dma_one(0, 0, j, std::true_type{});
+    } else {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j);
+        for (int j = 0; j < NDMA; ++j) dma_one(0, 0, j, std::false_type{});
+    }
+    if (KEXT && nkx < 2) {
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j, std::true_type{});
+    } else {
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j, std::false_type{});
+    }
     if constexpr (PF) epi_prefetch();
     wait_vmcnt<PF ? NDMA + NPF : NDMA>();
     asm volatile("" ::: "memory");  // keep the LDS reads below the barrier
@@ -431,17 +484,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     // landed everywhere and stage kt's buffer is no longer read -- step 1 with
     // the reads of step 0 of stage kt+1 and the loads of stage kt+2 into the
     // buffer stage kt released.  The last two stages drop the loads / reads.
-    auto stage_body = [&](int kt, auto read_next, auto load_next2) {
+    auto stage_body = [&](int kt, auto read_next, auto load_next2, auto extra_c) {
         const int stage = kt & 1;
-        mfma_step(0, T_{}, stage, 1, 1, F_{}, 0, 0);
+        mfma_step(0, T_{}, stage, 1, 1, F_{}, 0, 0, F_{});
         wait_vmcnt<0>();
         __syncthreads();
-        mfma_step(1, read_next, stage ^ 1, 0, 0, load_next2, (kt + 2) * BK, stage);
+        mfma_step(1, read_next, stage ^ 1, 0, 0, load_next2, (kt + 2) * BK, stage, extra_c);
     };
     int kt = 0;
-    for (; kt + 2 < nk; ++kt) stage_body(kt, T_{}, T_{});
-    if (kt + 1 < nk) stage_body(kt++, T_{}, F_{});
-    if (kt < nk) stage_body(kt, F_{}, F_{});
+    // epi 3: stages whose loads (two ahead) are extra-K ones take their own
+    // unrolled copy of the stage
+    for (; kt + 2 < (KEXT ? min(nk, nkx) : nk); ++kt) stage_body(kt, T_{}, T_{}, F_{});
+    if constexpr (KEXT) {
+        for (; kt + 2 < nk; ++kt) stage_body(kt, T_{}, T_{}, T_{});
+    }
+    if (kt + 1 < nk) stage_body(kt++, T_{}, F_{}, F_{});
+    if (kt < nk) stage_body(kt, F_{}, F_{}, F_{});
     mfma_drain();
     wait_vmcnt<0>();
 
@@ -896,7 +954,7 @@ static hipError_t launch_gemm_t(const GemmParams &P, hipStream_t stream, const c
 hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, void *C, int M, int N,
                        int K, const float *Sx, int RS, const uint32_t *keep, int KW,
                        const AdapterSource &src, hipStream_t stream) {
-    GemmParams P;
+    GemmParams P{};
     P.Arow = (const uint16_t *)Arow;
     P.Bcol = (const uint16_t *)Bcol;
     P.C = (uint16_t *)C;
@@ -940,6 +998,25 @@ hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, voi
                                     : launch_gemm_t<false, 2, false, 0>(P, stream, "gemm_b3_bwd_dx");
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_kext(const void *X, const void *W, void *Y, int M, int N, int K, const uint16_t *S2,
+                            int kx, const void *B, int r, hipStream_t stream) {
+    GemmParams P{};
+    P.Arow = (const uint16_t *)X;
+    P.Bcol = (const uint16_t *)W;
+    P.C = (uint16_t *)Y;
+    P.M = M;
+    P.N = N;
+    P.K = K;
+    P.tiles_m = (M + GBM - 1) / GBM;
+    P.tiles_n = (N + GBN - 1) / GBN;
+    P.ext = (const uint16_t *)B;
+    P.ext_r = r;
+    P.S2 = S2;
+    P.kx = kx;
+    if (P.tiles_m == 0 || P.tiles_n == 0) return hipSuccess;
+    return launch_gemm_t<true, 3, false, 0>(P, stream, "gemm_f2_fwd_lora");
 }
 
 }  // namespace lora

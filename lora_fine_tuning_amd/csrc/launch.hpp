@@ -68,9 +68,11 @@ hipError_t launch_router(const int64_t *seg_off, const int32_t *seg_adapter, int
                          int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int cap_bwd,
                          ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream);
 
+// s2 (streaming form only; may be NULL): also write alpha*S split into bf16
+// [hi | lo] rows of 2*s2_rp columns for the forward GEMM's extra K columns.
 hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int chunk_cap,
                      uint64_t seed, uint64_t offset, uint32_t *keep_bits, float *out, int RS,
-                     int KS, int ksl, hipStream_t stream);
+                     int KS, int ksl, hipStream_t stream, uint16_t *s2 = nullptr, int s2_rp = 0);
 
 hipError_t launch_sum_partials(const float *part, int nparts, size_t part_stride, size_t count,
                                float *out, const char *name, hipStream_t stream);
@@ -139,6 +141,13 @@ hipError_t launch_mask(uint64_t seed, uint64_t offset, int m, int k, float p, ui
 hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, void *C, int M, int N,
                        int K, const float *Sx, int RS, const uint32_t *keep, int KW,
                        const AdapterSource &src, hipStream_t stream);
+
+// Forward GEMM with the LoRA term as kx extra K columns: Y = [X | S2] [W ; B' ]
+// where S2 holds alpha*S split into bf16 hi and lo parts of kx/2 ranks each and
+// B' repeats B's rows for both halves (rows past r zero).  B must be 16-byte
+// aligned (N is a multiple of 8).
+hipError_t launch_gemm_kext(const void *X, const void *W, void *Y, int M, int N, int K, const uint16_t *S2,
+                            int kx, const void *B, int r, hipStream_t stream);
 
 size_t gemm_lds_bytes();
 

@@ -130,6 +130,11 @@ struct F1Params {
     int KW;
     int r_lds;  // rows of the staged At buffer (>= every rank, multiple of 16)
     int slab;   // columns of A staged at once (multiple of kF1KSub)
+    // streaming form, single adapter: also write alpha*S split into bf16 hi
+    // and lo parts, row i = [hi of ranks 0..RP) | lo of ranks 0..RP), RP = s2_rp
+    // (zeros past r) -- the extra K columns of the forward GEMM
+    uint16_t *s2;
+    int s2_rp;
 };
 
 // F1: dropout mask + down-projection (juhe.plus blog, section 4.1, forward
@@ -297,10 +302,16 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
     const int r0 = blockIdx.y * RL;
     const int ncol = min(RL, P.RS - r0);  // S columns this tile writes
     if (r0 >= r) {
-        // no ranks of this adapter here: the tile's S columns are zero
+        // no ranks of this adapter here: the tile's S (and hi / lo) columns are zero
         for (int i = tid; i < 16 * RL; i += 64 * F1S_WAVES) {
             const int rr = i / RL, cl = i % RL;
-            if (cl < ncol && row_lo + rr < row_hi) P.out[(size_t)(row_lo + rr) * P.RS + r0 + cl] = 0.f;
+            if (row_lo + rr >= row_hi) continue;
+            if (cl < ncol) P.out[(size_t)(row_lo + rr) * P.RS + r0 + cl] = 0.f;
+            if (P.s2 != nullptr && r0 + cl < P.s2_rp) {
+                uint16_t *q = P.s2 + (size_t)(row_lo + rr) * (2 * P.s2_rp) + r0 + cl;
+                q[0] = 0;
+                q[P.s2_rp] = 0;
+            }
         }
         return;
     }
@@ -442,6 +453,14 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
             v *= s;
         }
         P.out[(size_t)orow * P.RS + r0 + cl] = v;
+        if (P.s2 != nullptr && r0 + cl < P.s2_rp) {
+            // the forward epilogue's split of alpha*S, same arithmetic
+            uint32_t hi, lo;
+            split_bf16(ad.alpha * v, hi, lo);
+            uint16_t *q = P.s2 + (size_t)orow * (2 * P.s2_rp) + r0 + cl;
+            q[0] = (uint16_t)hi;
+            q[P.s2_rp] = (uint16_t)lo;
+        }
     }
 }
 
@@ -1349,8 +1368,10 @@ static int r_lds_of(const AdapterSource &src) {
 
 hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int chunk_cap,
                      uint64_t seed, uint64_t offset, uint32_t *keep_bits, float *out, int RS,
-                     int KS, int ksl, hipStream_t stream) {
+                     int KS, int ksl, hipStream_t stream, uint16_t *s2, int s2_rp) {
     F1Params P;
+    P.s2 = s2;
+    P.s2_rp = s2_rp;
     P.X = (const uint16_t *)X;
     P.m = m;
     P.k = k;
