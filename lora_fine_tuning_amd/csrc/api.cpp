@@ -244,6 +244,7 @@ FwdPlan plan_fwd(int64_t m, int64_t k, int32_t RS, bool multi, int32_t nseg) {
 
 struct BwdPlan {
     int RS;
+    int rows2;  // rows per B2 work item (one dA partial each)
     int chunk_cap_bwd;
     int chunk_cap_f1;
     B1Shape b1;
@@ -257,9 +258,10 @@ struct BwdPlan {
 BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_t nseg) {
     BwdPlan p{};
     p.RS = RS;
-    p.chunk_cap_bwd = cdiv(m, kBwdRows) + (multi ? nseg : 0);
-    p.chunk_cap_f1 = cdiv(m, kF1Rows) + (multi ? nseg : 0);
     const int rl = ((RS + 15) / 16) * 16;
+    p.rows2 = b2_rows(m, k, rl);
+    p.chunk_cap_bwd = cdiv(m, p.rows2) + (multi ? nseg : 0);
+    p.chunk_cap_f1 = cdiv(m, kF1Rows) + (multi ? nseg : 0);
     p.b1 = b1_shape(m, n, rl, RS, multi, nseg);
     p.C2 = rl <= 128 ? 256 : 128;
     p.ds_parts = p.b1.CT;
@@ -394,9 +396,9 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
                             pl.b1.slots, stream),
            "dS/dB reduction launch");
     if (m > 0)
-        HIPCHK(launch_b2(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, src, chunks, pl.C2, dApart,
-                         stream), "B2 launch");
-    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r, src, kBwdRows, chunks, stream),
+        HIPCHK(launch_b2(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, pl.rows2, src, chunks, pl.C2,
+                         dApart, stream), "B2 launch");
+    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r, src, pl.rows2, chunks, stream),
            "dA reduction launch");
     if (m > 0)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r, p == 0.0f ? nullptr : keep_bits,
@@ -474,8 +476,8 @@ extern "C" lora_status multi_lora_linear_fwd(const void *X, const void *W, const
     src.count_bwd = (const int32_t *)ws_at(workspace, pl.off_c_bwd);
     HIPCHK(launch_router(seg_off, seg_adapter, num_segments, (int)m, adapters, num_adapters, r_max,
                          (ChunkEntry *)src.chunks_f1, (int32_t *)src.count_f1, pl.chunk_cap_f1,
-                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd, nullptr,
-                         nullptr, 0, 0, stream),
+                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, kBwdRows, pl.chunk_cap_bwd,
+                         nullptr, nullptr, 0, 0, stream),
            "router launch");
     float *sout = pl.KS > 1 ? (float *)ws_at(workspace, pl.off_spart) : S;
     HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r_max, pl.KS,
@@ -517,7 +519,7 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
     src.count_b1 = (const int32_t *)ws_at(workspace, pl.off_c_b1);
     HIPCHK(launch_router(seg_off, seg_adapter, num_segments, (int)m, adapters, num_adapters, r_max,
                          (ChunkEntry *)src.chunks_f1, (int32_t *)src.count_f1, pl.chunk_cap_f1,
-                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.chunk_cap_bwd,
+                         (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.rows2, pl.chunk_cap_bwd,
                          (ChunkEntry *)src.chunks_b1, (int32_t *)src.count_b1, pl.b1.rows, pl.b1.slots, stream),
            "router launch");
     float *dS = (float *)ws_at(workspace, pl.off_ds);
@@ -530,8 +532,9 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
                             pl.b1.slots, stream),
            "dS/dB reduction launch");
     if (m > 0)
-        HIPCHK(launch_b2(X, keep_bits, dS, (int)m, (int)k, r_max, src, chunks, pl.C2, dApart, stream), "B2 launch");
-    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r_max, src, kBwdRows, chunks, stream),
+        HIPCHK(launch_b2(X, keep_bits, dS, (int)m, (int)k, r_max, pl.rows2, src, chunks, pl.C2, dApart, stream),
+               "B2 launch");
+    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r_max, src, pl.rows2, chunks, stream),
            "dA reduction launch");
     if (m > 0)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r_max, keep_bits, (int)((k + 31) / 32),

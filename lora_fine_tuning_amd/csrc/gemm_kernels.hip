@@ -726,15 +726,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     } else {
     // mixed adapters: the wave's first segment, found once
     const int wseg = MULTI ? first_segment(P, wrow0) : 0;
+    // B3 with mixed adapters: a wave whose rows all lie in one segment (wave-
+    // uniform; no barrier follows in any path) takes the fast epilogue when
+    // that adapter meets its conditions, else the single-adapter band path
+    // below with this segment's item
+    bool wave_one_seg = false;
+    ExtItem wit;
     if constexpr (MULTI && EPI == 2) {
-        // a wave whose rows all lie in one segment whose adapter meets the
-        // fast conditions takes the fast epilogue (wave-uniform decision; no
-        // barrier follows in either path)
-        ExtItem it;
-        if (P.multi_fast && wrow0 < P.M && wseg < P.nseg && get_item<EPI, MULTI>(P, wseg, it) &&
-            it.lo <= wrow0 && it.hi >= min(wrow0 + 128, P.M) && it.r <= 32 && (it.r & 7) == 0 &&
-            (((uintptr_t)it.w) & 15) == 0) {
-            fast_epilogue(it);
+        wave_one_seg = wrow0 < P.M && wseg < P.nseg && get_item<EPI, MULTI>(P, wseg, wit) &&
+                       wit.lo <= wrow0 && wit.hi >= min(wrow0 + 128, P.M);
+        if (wave_one_seg && P.multi_fast && wit.r <= 32 && (wit.r & 7) == 0 && (((uintptr_t)wit.w) & 15) == 0) {
+            fast_epilogue(wit);
             return;
         }
     }
@@ -806,8 +808,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     bool one_chunk = false;  // r <= 64 (the name predates the second chunk)
     ExtItem it1;
     bool rvec1 = false;
-    if (EPI == 2 && !MULTI) {
-        get_item<EPI, MULTI>(P, 0, it1);
+    if (EPI == 2 && (!MULTI || wave_one_seg)) {
+        if (MULTI) it1 = wit;
+        else get_item<EPI, MULTI>(P, 0, it1);
         one_chunk = it1.r <= 64;
         rvec1 = svec && (it1.r & 7) == 0;
         if (one_chunk) {
@@ -838,7 +841,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                                                     rK, (uint32_t)((tm * 16 + l16) * P.KW + (wcol0 >> 5)) * 4u, 0, 0));
 #pragma unroll
             for (int tn = 0; tn < NT16; ++tn) acc2[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (!MULTI && one_chunk) {
+            if (one_chunk) {
                 // both chunks' row-side loads first; the second is all zeros
                 // (out-of-range offsets) when r <= 32
                 uint4 hi0, lo0, hi1, lo1;

@@ -25,6 +25,19 @@ inline int rank_tiles(int r_lds) { return r_lds > 32 ? (r_lds + 31) / 32 : 1; }
 // serves ranks up to 128; its 32-bit buffer offsets need 64*k < 2^31.
 inline bool f1_streaming(int r_lds, int64_t k) { return r_lds <= 128 && k * 64 < (int64_t(1) << 31); }
 
+// Rows per B2 work item (the dA partials are one per item): 256, or taller
+// when the grid (items x 256-column tiles of k x rank tiles) would still have
+// about 1024 work-groups -- fewer partials for wide k or many rank tiles.
+inline int b2_rows(int64_t m, int64_t k, int r_lds) {
+    const int rt = r_lds > 32 ? (r_lds + 31) / 32 : 1;
+    const int64_t want = m * ((k + 255) / 256) * rt / 1024;
+    int64_t rows = std::max<int64_t>(kBwdRows, (want + 31) / 32 * 32);
+    rows = std::min<int64_t>(rows, std::max<int64_t>(kBwdRows, (m + 31) / 32 * 32));
+    // the kernels address an item's rows of X with 32-bit offsets
+    const int64_t cap = ((int64_t(1) << 31) - 1) / (2 * std::max<int64_t>(k, 1)) / 32 * 32;
+    return (int)std::max<int64_t>(std::min<int64_t>(rows, cap), std::min<int64_t>(kBwdRows, cap));
+}
+
 // B1 / B2 streaming forms: ranks up to 32, or up to 128 in rank tiles when
 // the S / dS row stride is a multiple of 4 floats (16-byte row pieces).
 inline bool bwd_streaming(int r_lds, int RS) { return r_lds <= 32 || (r_lds <= 128 && RS % 4 == 0); }
@@ -65,7 +78,7 @@ enum WorkTable { kTabF1 = 0, kTabBwd = 1, kTabB1 = 2 };
 
 hipError_t launch_router(const int64_t *seg_off, const int32_t *seg_adapter, int nseg, int m,
                          const lora_adapter *adapters, int nad, int r_cap, ChunkEntry *t_f1,
-                         int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int cap_bwd,
+                         int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int rows_bwd, int cap_bwd,
                          ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream);
 
 // s2 (streaming form only; may be NULL): also write alpha*S split into bf16
@@ -116,7 +129,7 @@ inline B1Shape b1_shape(int64_t m, int64_t n, int r_lds, int RS, bool multi, int
 hipError_t launch_b1(const void *dY, const float *S, int m, int n, int RS, const AdapterSource &src,
                      const B1Shape &sh, float *dSpart, float *dBpart, hipStream_t stream);
 
-hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS,
+hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS, int rows,
                      const AdapterSource &src, int chunk_cap, int C2, float *dApart,
                      hipStream_t stream);
 

@@ -1333,11 +1333,11 @@ static hipError_t finish_launch(int slot, hipStream_t stream) {
 
 hipError_t launch_router(const int64_t *seg_off, const int32_t *seg_adapter, int nseg, int m,
                          const lora_adapter *adapters, int nad, int r_cap, ChunkEntry *t_f1,
-                         int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int cap_bwd,
+                         int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int rows_bwd, int cap_bwd,
                          ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream) {
     RouterTables T;
     T.tab[0] = RouterTable{t_f1, c_f1, kF1Rows, cap_f1};
-    T.tab[1] = RouterTable{t_bwd, c_bwd, kBwdRows, cap_bwd};
+    T.tab[1] = RouterTable{t_bwd, c_bwd, rows_bwd, cap_bwd};
     T.tab[2] = RouterTable{t_b1, c_b1, t_b1 != nullptr ? rows_b1 : 0, cap_b1};
     (void)hipGetLastError();
     const int slot = prof_begin("router", stream);
@@ -1470,7 +1470,7 @@ hipError_t launch_b1(const void *dY, const float *S, int m, int n, int RS, const
     return finish_launch(slot, stream);
 }
 
-hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS,
+hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS, int rows,
                      const AdapterSource &src, int chunk_cap, int C2, float *dApart,
                      hipStream_t stream) {
     B2Params P;
@@ -1482,6 +1482,7 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
     P.RS = RS;
     P.KW = (k + 31) / 32;
     P.work = make_work(src, kTabBwd);
+    P.work.rows_per_chunk = rows;
     P.dApart = dApart;
     P.r_lds = r_lds_of(src);
     P.tiled = P.r_lds > 32;
