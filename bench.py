@@ -42,7 +42,112 @@ def parse():
     ap.add_argument("--r", type=int, default=16)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB (byte-counter calibration)")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the headline step: the mixed-adapter workloads and the rank/token "
+                         "sweep, fused vs frozen, one JSON line per case")
     return ap.parse_args()
+
+
+KERNELS = ("router", "f1_mask_down", "sum_s_partials", "gemm_f2_fwd_lora", "b1_ds_db", "reduce_ds_db",
+           "b2_da", "reduce_da", "gemm_b3_bwd_dx")
+
+
+def config_report(args):
+    """Fused fwd+bwd against the frozen layer (ours and torch.matmul) for the
+    mixed-adapter workloads (4 adapters r 16, k = n 8192, 16384 packed tokens;
+    8 adapters r 8..128 on k 28672 -> n 8192, 8192 tokens) and the rank/token
+    sweep (k = n 4096, r 8..128, m 2048..32768).  Same synthetic inputs as the
+    parity tests' workloads; per-kernel averages from the library's HIP events."""
+    import torch
+
+    import lora_fine_tuning_amd as lf
+    from synth import make_tensors_device, workload
+
+    lf.load()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps=args.steps, warmup=args.warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def kernels(fn):
+        lf.lora_profiling_enable(True, capacity=8192)
+        lf.lora_profiling_reset()
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        out = {}
+        for nm in KERNELS:
+            c, t = lf.lora_profiling_query(nm)
+            if c:
+                out[nm] = round(t / c * 1e3, 1)
+        lf.lora_profiling_enable(False)
+        return out
+
+    def report(w, fused):
+        t = tensors[w.name]
+        X, W, dY = t["X"], t["W"], t["dY"]
+        Yf = torch.empty(w.m, w.n, device="cuda", dtype=torch.bfloat16)
+        dXf = torch.empty_like(X)
+        Wt = W.t().contiguous()
+
+        def ours():
+            lf.lora_frozen_fwd(X, W, Y=Yf, stream=stream)
+            lf.lora_frozen_bwd(dY, W, dX=dXf, stream=stream)
+
+        def tor():
+            torch.matmul(X, W, out=Yf)
+            torch.matmul(dY, Wt, out=dXf)
+
+        f, o, tt = timed(fused), timed(ours), timed(tor)
+        print(json.dumps({"workload": w.name, "m": w.m, "k": w.k, "n": w.n,
+                          "ranks": [a.r for a in w.adapters],
+                          "segments": 0 if w.seg_off is None else len(w.seg_off) - 1,
+                          "fused_ms": round(f, 4), "frozen_ours_ms": round(o, 4),
+                          "frozen_torch_ms": round(tt, 4), "fused_over_frozen": round(f / min(o, tt), 4),
+                          "kernel_us": kernels(fused)}), flush=True)
+
+    tensors = {}
+    for cid in (2, 4):
+        w = workload(cid)
+        t = tensors[w.name] = make_tensors_device(w, "cuda")
+        As, Bs = t["A"], t["B"]
+        dAs = [torch.empty_like(a) for a in As]
+        dBs = [torch.empty_like(b) for b in Bs]
+        table = lf.adapter_table(As, Bs, [a.alpha for a in w.adapters], [a.p for a in w.adapters], dAs, dBs)
+        so = torch.as_tensor(w.seg_off).cuda()
+        sa = torch.as_tensor(w.seg_adapter).cuda()
+
+        def fused(t=t, table=table, so=so, sa=sa, w=w):
+            Y, S, keep = lf.multi_lora_linear_fwd(t["X"], t["W"], table, len(t["A"]), so, sa, w.r_max, 0, 0,
+                                                  stream=stream)
+            lf.multi_lora_linear_bwd(t["dY"], t["X"], t["W"], table, len(t["A"]), so, sa, S, keep, w.r_max,
+                                     stream=stream)
+        report(w, fused)
+        del tensors[w.name]
+        torch.cuda.empty_cache()
+    for m in (2048, 8192, 32768):
+        for r in (8, 16, 32, 64, 128):
+            w = workload(3, m=m, r=r)
+            t = tensors[w.name] = make_tensors_device(w, "cuda")
+            ad = w.adapters[0]
+
+            def fused(t=t, ad=ad):
+                Y, S, keep = lf.lora_linear_fwd(t["X"], t["W"], t["A"][0], t["B"][0], ad.alpha, ad.p, 0, 0,
+                                                stream=stream)
+                lf.lora_linear_bwd(t["dY"], t["X"], t["W"], t["A"][0], t["B"][0], S, keep, ad.alpha, ad.p,
+                                   stream=stream)
+            report(w, fused)
+            del tensors[w.name]
+            torch.cuda.empty_cache()
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama8b_m8192_hbm_traffic.md")
@@ -92,6 +197,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.configs:
+        config_report(args)
+        return
     lf.load()
     dev = "cuda"
     m, k, r, alpha, p = args.m, 4096, args.r, 2.0, 0.1

@@ -104,11 +104,11 @@ def workload(config_id: int, variant: int = 0, *, m: Optional[int] = None,
        Dirichlet(1) segments, alpha 2, p 0.1.
     """
     if config_id == 0:
-        return Workload("cfg0 m512 k1024 n1024 r16", 0, 0, m or 512, 1024, 1024,
+        return Workload("small m512 k1024 n1024 r16", 0, 0, m or 512, 1024, 1024,
                         [AdapterSpec(r or 16, 2.0, 0.1)])
     if config_id == 1:
         n = 4096 if variant == 0 else 14336
-        return Workload(f"cfg1 m8192 k4096 n{n} r16", 1, variant, m or 8192, 4096, n,
+        return Workload(f"llama8b-proj m8192 k4096 n{n} r16", 1, variant, m or 8192, 4096, n,
                         [AdapterSpec(r or 16, 2.0, 0.1)])
     if config_id == 2:
         rng = np.random.Generator(np.random.PCG64(2000 + config_id))
@@ -116,20 +116,20 @@ def workload(config_id: int, variant: int = 0, *, m: Optional[int] = None,
         seg_off, seg_ad = lognormal_packed_segments(rng, total, 900.0, 0.75, 128, 4096, 4)
         ads = [AdapterSpec(16, 1.0, 0.0), AdapterSpec(16, 2.0, 0.05),
                AdapterSpec(16, 2.0, 0.1), AdapterSpec(16, 4.0, 0.1)]
-        return Workload(f"cfg2 multi4 m{total} k8192 n8192 r16", 2, 0, total, 8192, 8192, ads,
+        return Workload(f"multi4 packed m{total} k8192 n8192 r16", 2, 0, total, 8192, 8192, ads,
                         seg_off, seg_ad)
     if config_id == 3:
         ranks = [8, 16, 32, 64, 128]
         rr = r or ranks[variant]
         mm = m or 8192
-        return Workload(f"cfg3 m{mm} k4096 n4096 r{rr}", 3, variant, mm, 4096, 4096,
+        return Workload(f"sweep m{mm} k4096 n4096 r{rr}", 3, variant, mm, 4096, 4096,
                         [AdapterSpec(rr, 2.0, 0.1)])
     if config_id == 4:
         rng = np.random.Generator(np.random.PCG64(2000 + config_id))
         total = m or 8192
         seg_off, seg_ad = dirichlet_segments(rng, total, 8)
         ads = [AdapterSpec(rk, 2.0, 0.1) for rk in (8, 16, 16, 32, 32, 64, 64, 128)]
-        return Workload(f"cfg4 multi8 m{total} k28672 n8192", 4, 0, total, 28672, 8192, ads,
+        return Workload(f"multi8 down-proj m{total} k28672 n8192 r8..128", 4, 0, total, 28672, 8192, ads,
                         seg_off, seg_ad)
     raise ValueError(f"unknown config {config_id}")
 
