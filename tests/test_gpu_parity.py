@@ -149,6 +149,8 @@ MULTI_CASES = [
      [0, 1, 65, 129, 700, 1100], [2, 0, 1, 0, 2]),             # 1-row segment, ranks up to 128
     (333, 136, 520, [5, 17], [3.0, 0.7], [0.3, 0.1],
      [0, 100, 200, 333], [1, 1, 0]),                           # same adapter twice in a row
+    (600, 256, 264, [64, 16, 24], [2.0, 1.0, 0.5], [0.1, 0.2, 0.0],
+     [0, 520, 600], [0, 2]),                                   # whole 128-row waves inside a rank-64 segment
 ]
 
 
