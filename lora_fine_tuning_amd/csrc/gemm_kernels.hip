@@ -470,8 +470,28 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j, std::false_type{});
     }
+    // B3, one adapter with 64 < r <= 128 (16-byte A rows): A's ranks 64..127 of
+    // the tile's 256 columns go to the 32 KiB past the ring (128-byte rows,
+    // 16-byte chunk q of column c at q ^ (c & 7)), loaded during the K loop
+    bool ahi = false;
+    if constexpr (EPI == 2 && !MULTI && FAST == 0) {
+        ahi = P.ext_r > 64 && P.ext_r <= 128 && (P.ext_r & 7) == 0 && (((uintptr_t)P.ext) & 15) == 0;
+        if (ahi) {
+            const uint32_t abytes = (uint32_t)P.N * (uint32_t)P.ext_r * 2u;
+            const sgpr4_t d = make_desc(P.ext, abytes);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int j = 8 * wave + q, c = 8 * j + (lane >> 3);
+                const int lq = (lane & 7) ^ (c & 7);  // logical 8-rank chunk of the lane's 16 bytes
+                const uint32_t off = (n0 + c < P.N && 64 + 8 * lq < P.ext_r)
+                    ? ((uint32_t)(n0 + c) * (uint32_t)P.ext_r + 64u + 8u * lq) * 2u : kOOB;
+                dma16(d, off, pf_lds + j * 1024);
+            }
+        }
+    }
     if constexpr (PF) epi_prefetch();
-    wait_vmcnt<PF ? NDMA + NPF : NDMA>();
+    if (ahi) wait_vmcnt<NDMA + 8>();
+    else wait_vmcnt<PF ? NDMA + NPF : NDMA>();
     asm volatile("" ::: "memory");  // keep the LDS reads below the barrier
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -811,7 +831,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     if (EPI == 2 && (!MULTI || wave_one_seg)) {
         if (MULTI) it1 = wit;
         else get_item<EPI, MULTI>(P, 0, it1);
-        one_chunk = it1.r <= 64;
+        one_chunk = it1.r <= 64 || (!MULTI && ahi);
         rvec1 = svec && (it1.r & 7) == 0;
         if (one_chunk) {
             const bool avec = (it1.r & 7) == 0 && (((uintptr_t)it1.w) & 15) == 0;
@@ -823,6 +843,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                     cf1[c][tn] = col_ext_frag<EPI>(P, rW, wcol0, it1, wcol0 + tn * 16 + l16, 32 * c, lane, avec);
         }
     }
+
+    if (ahi) __syncthreads();  // every wave's part of the A copy landed (K = 0 never waited)
 
     // ---- output (B3 adds the masked rank-deep term one 16-row band at a time)
     const bool has_keep = EPI == 2 && P.keep != nullptr;
@@ -857,6 +879,23 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                     for (int tn = 0; tn < NT16; ++tn) {
                         acc2[tn] = mfma16x16x32(cf1[1][tn], hi1, acc2[tn]);
                         acc2[tn] = mfma16x16x32(cf1[1][tn], lo1, acc2[tn]);
+                    }
+                }
+                if (!MULTI && ahi) {
+                    // ranks 64..127: column-side fragments from the LDS copy of A
+                    const lds_char *pa = (const lds_char *)smem + NST * STAGE_BYTES;
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        uint4 hi, lo;
+                        row_ext_frags(P, rS, wrow0, it1, row, 64 + 32 * c2, lane, rvec1, hi, lo);
+                        const int lq = 4 * c2 + lg;
+#pragma unroll
+                        for (int tn = 0; tn < NT16; ++tn) {
+                            const int c = wn * 128 + tn * 16 + l16;
+                            const uint4 cf = *(const uint4 *)(pa + c * 128 + ((lq ^ (c & 7)) << 4));
+                            acc2[tn] = mfma16x16x32(cf, hi, acc2[tn]);
+                            acc2[tn] = mfma16x16x32(cf, lo, acc2[tn]);
+                        }
                     }
                 }
             } else {

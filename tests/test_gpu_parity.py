@@ -57,6 +57,7 @@ SINGLE_CASES = [
     (700, 512, 520, 64, 2.0, 0.1),     # two rank tiles of 32
     (333, 264, 264, 36, 1.0, 0.2),     # rank tiles, second one ragged (rank not a multiple of 8)
     (520, 1024, 264, 96, 0.5, 0.1),    # three rank tiles
+    (300, 264, 136, 80, 1.0, 0.1),     # ranks past 64 with a ragged last column tile of dX
 ]
 
 
