@@ -266,13 +266,14 @@ __global__ __launch_bounds__(256) void f1_kernel(F1Params P) {
     }
 }
 
-// ----- F1 streaming form (ranks <= 32).  Work-group = 16 rows of a chunk
-// over all of k, so S leaves the kernel finished (no split-k partials, no
-// second launch).  Its 8 waves take 8 consecutive ranges of k in 128-column
-// units.  Lane l owns row (l % 16) and columns 8*(l/16) .. +7 of each
-// 32-column step: one Philox block, one keep byte, one MFMA row-side
-// fragment.  Per unit, each wave copies the 128 rows of A it needs (stored
-// k-major, rl bf16 per row) into one of two private LDS slabs and reads its
+// ----- F1 streaming form (ranks <= 32 per launch slice; larger ranks in rank
+// tiles of 32).  Work-group = 16 rows of a chunk over all of k, so S leaves
+// the kernel finished (no split-k partials, no second launch).  Its 8 waves
+// take 8 consecutive ranges of k in 128-column units.  Lane l owns row
+// (l % 16) and columns 8*(l/16) .. +7 of each 32-column step: one Philox
+// block, one keep byte, one MFMA row-side fragment.  Per unit, each wave
+// copies the 128 rows of A it needs (k-major, rl bf16 per row) into a
+// private LDS slab and reads its
 // rank-side fragments back with transposing LDS reads; the next unit's A and
 // X loads are in flight while the current unit is hashed, masked and
 // multiplied.  The waves' partial S meet in LDS and are summed in wave order.
@@ -333,7 +334,11 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
     const int kq = ((P.k + F1S_WAVES * F1S_UNIT - 1) / (F1S_WAVES * F1S_UNIT)) * F1S_UNIT;
     const int kb = wave * kq, ke = min(P.k, kb + kq);
     const int nu = ke > kb ? (ke - kb + F1S_UNIT - 1) / F1S_UNIT : 0;
-    lds_char *slab0 = smem + wave * 2 * SLAB;
+    // A slabs per wave: two for RL = 16; one for RL = 32 (the next unit's A is
+    // stored after this unit's last read of it -- LDS accesses of a wave are
+    // performed in order), so two work-groups fit a CU
+    constexpr int NSLAB = MAXT == 1 ? 2 : 1;
+    lds_char *slab0 = smem + wave * NSLAB * SLAB;
     const bool avec = (r & 7) == 0 && (((uintptr_t)ad.A) & 15) == 0;
     // A rows below ke (rows at or past ke read as zero)
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(ad.A, (size_t)max(ke, 0) * r * 2);
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
         // next unit's loads (past the range they read zeros)
         if (avec) load_a(c + F1S_UNIT, an);
         load_x(c + F1S_UNIT, xf);
-        const lds_char *sl = slab0 + (u & 1) * SLAB;
+        const lds_char *sl = slab0 + (u % NSLAB) * SLAB;
         uint32_t kw = 0;  // byte t: this lane's keep bits of step t
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -424,7 +429,7 @@ __global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
             kw = (g & 2) ? ((kw & 0xFFFF0000u) | (p2 >> 16)) : ((kw & 0x0000FFFFu) | (p2 << 16));
             if (rvalid && c + 32 * g < ke) P.keep_bits[(size_t)row * P.KW + ((c >> 5) + g)] = kw;
         }
-        lds_char *nx = slab0 + ((u + 1) & 1) * SLAB;
+        lds_char *nx = slab0 + ((u + 1) % NSLAB) * SLAB;
         if (avec) store_a(nx, an);
         else copy_a_generic(c + F1S_UNIT, nx);
     };
@@ -1034,7 +1039,10 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     extern __shared__ uint4 b1v_smem[];
     lds_char *smem = (lds_char *)b1v_smem;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    float *red = (float *)(smem + NST * STAGE);  // [2][4 waves][32 rows][RL]
+    // [NRED][4 waves][32 rows][RL]: double-buffered for RL = 16; for RL = 32 one
+    // buffer and a second barrier per sub-block, so two work-groups fit a CU
+    constexpr int NRED = MAXT == 1 ? 2 : 1;
+    float *red = (float *)(smem + NST * STAGE);
 
     int row_lo, row_hi;
     AdapterView ad;
@@ -1125,7 +1133,7 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     // sum of the four waves' dS shares of sub-block sb (after the barrier)
     // thread t handles row t / 8 of the sub-block, columns t % 8, +8, ...
     auto flush_ds = [&](int sb) {
-        const float *rd = red + (sb & 1) * (4 * 32 * RL);
+        const float *rd = red + (sb % NRED) * (4 * 32 * RL);
         const int rr = tid >> 3, rs = row_lo + sb * 32;
         if (rs + rr >= row_hi) return;
         float *drow = dsp + (size_t)(rs + rr) * P.RS;
@@ -1164,7 +1172,7 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
                 for (int bt = 0; bt < MAXT; ++bt) accS[rb][bt] = mfma16x16x32(af, bfr[q][bt], accS[rb][bt]);
             }
         }
-        float *rw = red + (sb & 1) * (4 * 32 * RL) + wave * 32 * RL;
+        float *rw = red + (sb % NRED) * (4 * 32 * RL) + wave * 32 * RL;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -1199,6 +1207,7 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
         wait_vmcnt<NDMA * (NST - 2)>();
         __syncthreads();
         flush_ds(sb);
+        if constexpr (NRED == 1) __syncthreads();  // the next sub-block rewrites red
         stage = stage == NST - 1 ? 0 : stage + 1;
         lstage = lstage == NST - 1 ? 0 : lstage + 1;
     }
@@ -1397,7 +1406,7 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
         if (P.r_lds <= 16)
             launch_with_lds(f1s_kernel<1>, g4, (size_t)F1S_WAVES * 2 * F1S_UNIT * 16 * 2, stream, P, 64 * F1S_WAVES);
         else
-            launch_with_lds(f1s_kernel<2>, g4, (size_t)F1S_WAVES * 2 * F1S_UNIT * 32 * 2, stream, P, 64 * F1S_WAVES);
+            launch_with_lds(f1s_kernel<2>, g4, (size_t)F1S_WAVES * 1 * F1S_UNIT * 32 * 2, stream, P, 64 * F1S_WAVES);
         return finish_launch(slot, stream);
     }
     const dim3 grid(chunk_cap, KS);
@@ -1450,7 +1459,7 @@ hipError_t launch_b1(const void *dY, const float *S, int m, int n, int RS, const
         const int rl = P.r_lds <= 16 ? 16 : 32;
         // ring depth 3: two stages in flight, two work-groups per CU
         auto lds_of = [&](int nst) {
-            return (size_t)nst * (sh.cw * B1V_SUB + 32 * 32 * 4) + (size_t)2 * 4 * 32 * rl * 4;
+            return (size_t)nst * (sh.cw * B1V_SUB + 32 * 32 * 4) + (size_t)(rl == 16 ? 2 : 1) * 4 * 32 * rl * 4;
         };
         if (rl == 16) launch_with_lds(b1v_kernel<1, 1, 3>, grid, lds_of(3), stream, P);
         else launch_with_lds(b1v_kernel<1, 2, 3>, grid, lds_of(3), stream, P);
