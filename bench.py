@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--r", type=int, default=16)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB (byte-counter calibration)")
+    ap.add_argument("--unfused-only", action="store_true",
+                    help="time only the eager PyTorch LoRA sequence (for its byte counters)")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the headline step: the mixed-adapter workloads and the rank/token "
                          "sweep, fused vs frozen, one JSON line per case")
@@ -256,6 +258,43 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    # The unfused comparator: the eager PyTorch LoRA layer (dropout, three
+    # matmuls, scale, add; backward by autograd), bf16, same shapes.  Its mask
+    # comes from torch's own generator; only its time and bytes are used.
+    unfused = []
+    for st in shapes:
+        ua = st["A"].detach().clone().requires_grad_(True)
+        ub = st["B"].detach().clone().requires_grad_(True)
+        unfused.append((st, ua, ub))
+
+    def unfused_step():
+        for st, ua, ub in unfused:
+            ua.grad = None
+            ub.grad = None
+            xg = st["X"].detach().requires_grad_(True)
+            xd = torch.nn.functional.dropout(xg, p=p, training=True)
+            y = xg @ st["W"] + alpha * ((xd @ ua) @ ub)
+            y.backward(st["dY"])
+
+    def copy_calibration():
+        # ends a counter run with device copies of known size (byte-counter scale)
+        if not args.copy_calib_mib:
+            return
+        nel = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + written per copy, 3 copies",
+              file=sys.stderr, flush=True)
+
+    if args.unfused_only:
+        ms_u = timed(unfused_step, args.steps, args.warmup)
+        copy_calibration()
+        print(json.dumps({"unfused_torch_ms": round(ms_u, 4), "steps": args.steps, "warmup": args.warmup}))
+        return
+
     print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
     ms = timed(step, args.steps, args.warmup)
     print(f"[bench] fused fwd+bwd {ms:.3f} ms/step", file=sys.stderr, flush=True)
@@ -276,6 +315,8 @@ def main():
     ms_frozen_torch = timed(lambda: frozen_step("torch"), args.steps, args.warmup)
     print(f"[bench] frozen ours {ms_frozen_ours:.3f} ms, torch {ms_frozen_torch:.3f} ms",
           file=sys.stderr, flush=True)
+    ms_unfused = timed(unfused_step, args.steps, args.warmup)
+    print(f"[bench] unfused torch LoRA {ms_unfused:.3f} ms", file=sys.stderr, flush=True)
 
     # algorithmic FLOPs per launch (both shapes): F2 2mkn + 2mrn; B3 2mnk + 2mrk
     flops = {
@@ -322,21 +363,14 @@ def main():
         "roofline": roofline,
         "frozen": {"ours_ms": round(ms_frozen_ours, 4), "torch_matmul_ms": round(ms_frozen_torch, 4),
                    "fused_over_frozen": round(ms / min(ms_frozen_ours, ms_frozen_torch), 4)},
+        "unfused_torch": {"ms": round(ms_unfused, 4), "fused_speedup": round(ms_unfused / ms, 4)},
         "kernels": {nm: {kk: (round(v, 3) if isinstance(v, float) else v) for kk, v in d.items()}
                     for nm, d in kernels.items()},
         "ms_per_step_with_kernel_events": round(ms_prof, 4),
         "hbm_kernels": hbm,
         "gemm_source_digest": source_digest(),
     }
-    if args.copy_calib_mib:
-        nel = args.copy_calib_mib * (1 << 20) // 4
-        src = torch.ones(nel, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + written per copy, 3 copies",
-              file=sys.stderr, flush=True)
+    copy_calibration()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(m, k, ns, r, alpha, p, args.cpu_rows)
     print(json.dumps(result), flush=True)
