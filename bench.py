@@ -57,13 +57,14 @@ KERNELS = ("router", "f1_mask_down", "sum_s_partials", "gemm_f2_fwd_lora", "b1_d
 def config_report(args):
     """Fused fwd+bwd against the frozen layer (ours and torch.matmul) for the
     mixed-adapter workloads (4 adapters r 16, k = n 8192, 16384 packed tokens;
-    8 adapters r 8..128 on k 28672 -> n 8192, 8192 tokens) and the rank/token
-    sweep (k = n 4096, r 8..128, m 2048..32768).  Same synthetic inputs as the
+    8 adapters r 8..128 on k 28672 -> n 8192, 8192 tokens), the seven
+    projections of a LLaMA-8B-shaped decoder layer, and the rank/token sweep
+    (k = n 4096, r 8..128, m 2048..32768).  Same synthetic inputs as the
     parity tests' workloads; per-kernel averages from the library's HIP events."""
     import torch
 
     import lora_fine_tuning_amd as lf
-    from synth import make_tensors_device, workload
+    from synth import AdapterSpec, Workload, make_tensors_device, workload
 
     lf.load()
     stream = torch.cuda.current_stream()
@@ -136,6 +137,42 @@ def config_report(args):
         report(w, fused)
         del tensors[w.name]
         torch.cuda.empty_cache()
+    # the seven LoRA projections of one LLaMA-8B-shaped decoder layer (q, k, v, o,
+    # gate, up, down; m 8192, r 16; synthetic weights, no attention), run back to
+    # back as one step
+    proj = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
+            ("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)]
+    layer = []
+    for vi, (nm, kk, nn) in enumerate(proj):
+        wl = Workload(f"{nm} m8192 k{kk} n{nn} r16", 1, 10 + vi, 8192, kk, nn, [AdapterSpec(16, 2.0, 0.1)])
+        layer.append(make_tensors_device(wl, "cuda"))
+
+    def layer_fused():
+        for t in layer:
+            Y, S, keep = lf.lora_linear_fwd(t["X"], t["W"], t["A"][0], t["B"][0], 2.0, 0.1, 0, 0, stream=stream)
+            lf.lora_linear_bwd(t["dY"], t["X"], t["W"], t["A"][0], t["B"][0], S, keep, 2.0, 0.1, stream=stream)
+
+    outs = [(torch.empty(t["X"].shape[0], t["W"].shape[1], device="cuda", dtype=torch.bfloat16),
+             torch.empty_like(t["X"]), t["W"].t().contiguous()) for t in layer]
+
+    def layer_ours():
+        for t, (yf, dxf, _) in zip(layer, outs):
+            lf.lora_frozen_fwd(t["X"], t["W"], Y=yf, stream=stream)
+            lf.lora_frozen_bwd(t["dY"], t["W"], dX=dxf, stream=stream)
+
+    def layer_torch():
+        for t, (yf, dxf, wt) in zip(layer, outs):
+            torch.matmul(t["X"], t["W"], out=yf)
+            torch.matmul(t["dY"], wt, out=dxf)
+
+    f, o, tt = timed(layer_fused), timed(layer_ours), timed(layer_torch)
+    print(json.dumps({"workload": "llama8b-layer q k v o gate up down, m 8192, r 16", "m": 8192,
+                      "projections": [f"{nm} {kk}->{nn}" for nm, kk, nn in proj],
+                      "fused_ms": round(f, 4), "frozen_ours_ms": round(o, 4), "frozen_torch_ms": round(tt, 4),
+                      "fused_over_frozen": round(f / min(o, tt), 4), "kernel_us": kernels(layer_fused)}),
+          flush=True)
+    del layer, outs
+    torch.cuda.empty_cache()
     for m in (2048, 8192, 32768):
         for r in (8, 16, 32, 64, 128):
             w = workload(3, m=m, r=r)
