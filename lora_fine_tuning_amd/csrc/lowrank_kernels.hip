@@ -842,7 +842,8 @@ __global__ __launch_bounds__(256) void b2_kernel(B2Params P) {
 }
 
 // ===========================================================================
-// Streaming variants of B1 and B2 for ranks <= 32.  The full-size operand
+// Streaming variants of B1 and B2 for ranks <= 32 per launch slice (ranks up to
+// 128 in rank tiles of 32, grid dimension z).  The full-size operand
 // (dY or X) and the small per-row operands (alpha*S or dS, the keep words)
 // flow global -> LDS through a 3-stage ring of direct-to-LDS loads, so two
 // sub-blocks are in flight while a third is consumed and no VGPRs stage data.
@@ -1018,10 +1019,10 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
     }
 }
 
-// ----- B1 streaming (ranks <= 32).  Work-group = one row group (rows of one
-// adapter) x C1 = 256*CW columns; rows go in sub-blocks of 32 through a
-// 3-stage ring of direct-to-LDS loads (dY as CW swizzled 256-column sub-tiles,
-// plus the 32 rows of S).  Wave w owns the 16-column blocks 4*CW*w .. +4*CW-1:
+// ----- B1 streaming (ranks <= 32 per rank tile).  Work-group = one row group
+// (rows of one adapter) x C1 = 256*CW columns; rows go in sub-blocks of 32
+// through a 3-stage ring of direct-to-LDS loads (dY as CW swizzled 256-column
+// sub-tiles, plus the 32 rows of S).  Wave w owns the 16-column blocks 4*CW*w .. +4*CW-1:
 // it accumulates dB = alpha S^T dY for them over all the group's rows, and
 // its share of dS = alpha dY B^T for each sub-block; the four shares meet in
 // LDS and are summed in wave order into one dS partial per column tile.  The
