@@ -114,7 +114,7 @@ def test_full_llama8b_projection(variant):
     run_single(workload(1, variant))
 
 
-@pytest.mark.parametrize("m,r", [(2048, 8), (8192, 32), (8192, 128), (32768, 16)])
+@pytest.mark.parametrize("m,r", [(2048, 8), (2048, 128), (8192, 32), (8192, 128), (32768, 16), (32768, 64)])
 def test_full_rank_token_sweep(m, r):
     run_single(workload(3, m=m, r=r))
 
