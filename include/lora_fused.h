@@ -170,6 +170,53 @@ lora_status multi_lora_check_segments(const int64_t *seg_off_host, const int32_t
                                       const int32_t *adapter_r_host, int32_t num_adapters,
                                       int32_t r_max);
 
+/* ---- mixed-adapter batching (host) ---------------------------------------
+ * The step upstream of the mixed-adapter entry points: a scheduler packs the
+ * samples of several adapters' global batches into microbatches of bounded
+ * token count, and each microbatch's rows, grouped by adapter, become one
+ * segment table (papers.chlience.com notes on LoRAFusion, section 4
+ * "Multi-LoRA scheduler"; juhe.plus blog, section 4.2).  All arrays are host
+ * memory owned by the caller; nothing is retained; no device work. */
+
+/* Greedy packing of num_samples samples (lengths[i] tokens, 1 <= lengths[i]
+ * <= capacity) into microbatches of at most `capacity` tokens: first-fit
+ * decreasing -- samples longest first (equal lengths in index order), each
+ * into the lowest-numbered microbatch with room, else into a new one (the
+ * pages' greedy fallback of their MILP packer).  Writes mb_of_sample[i] (the
+ * microbatch of sample i, numbered in opening order) and *num_microbatches.
+ * LORA_ERR_INVALID_ARG for a length outside [1, capacity], capacity < 1,
+ * num_samples < 0 or a NULL array. */
+lora_status lora_pack_greedy(const int32_t *lengths, int32_t num_samples, int64_t capacity,
+                             int32_t *mb_of_sample, int32_t *num_microbatches);
+
+/* The segment table of microbatch `mb`: its samples ordered by adapter
+ * (increasing id; one adapter's samples in increasing index), one segment per
+ * adapter present.  Writes sample_order[0 .. *num_members) (sample indices in
+ * row order; room for num_samples), seg_off[0 .. *num_segments] (token
+ * offsets; room for num_adapters + 1; seg_off[*num_segments] is the
+ * microbatch's row count m) and seg_adapter[0 .. *num_segments) (room for
+ * num_adapters).  An empty microbatch gives zero segments and seg_off[0] = 0.
+ * LORA_ERR_INVALID_ARG for an adapter id outside [0, num_adapters), a length
+ * below 1 among the members, or a NULL array. */
+lora_status lora_microbatch_segments(const int32_t *lengths, const int32_t *adapter_of_sample,
+                                     const int32_t *mb_of_sample, int32_t num_samples,
+                                     int32_t num_adapters, int32_t mb, int32_t *sample_order,
+                                     int32_t *num_members, int64_t *seg_off,
+                                     int32_t *seg_adapter, int32_t *num_segments);
+
+/* Pipeline dependency check ("bubble lemma", same sections): with `stages`
+ * pipeline stages, sample i sits in microbatch mb_of_sample[i] and belongs to
+ * global batch batch_of_sample[i] of adapter adapter_of_sample[i].  For every
+ * adapter and each of its global batches that has a later one with samples,
+ * the earliest microbatch of that next batch must be at least the latest
+ * microbatch of this batch plus stages - 1.  *violations = the number of
+ * (adapter, batch) pairs that break it (0: the order is valid).
+ * LORA_ERR_INVALID_ARG for stages < 1, an adapter id outside
+ * [0, num_adapters), a negative index or a NULL array. */
+lora_status lora_check_bubble_lemma(const int32_t *mb_of_sample, const int32_t *adapter_of_sample,
+                                    const int32_t *batch_of_sample, int32_t num_samples,
+                                    int32_t num_adapters, int32_t stages, int64_t *violations);
+
 /* ---- pieces exposed for testing and as the frozen-layer baseline -------- */
 
 /* The dropout mask alone (same bits the forward stores). */

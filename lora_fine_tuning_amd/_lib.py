@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import List, Optional, Sequence
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 
@@ -29,7 +29,8 @@ EXPORTS = [
     "multi_lora_bwd_workspace_size", "multi_lora_linear_bwd", "multi_lora_check_segments",
     "lora_dropout_mask", "lora_frozen_fwd", "lora_frozen_bwd", "lora_profiling_enable",
     "lora_profiling_reset", "lora_profiling_query", "lora_status_string",
-    "lora_last_error_message",
+    "lora_last_error_message", "lora_pack_greedy", "lora_microbatch_segments",
+    "lora_check_bubble_lemma",
 ]
 
 
@@ -73,6 +74,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "multi_lora_linear_bwd": (I32, [P, P, P, P, I32, P, P, I32, P, P, I64, I64, I64, I32, P,
                                         P, SZ, P]),
         "multi_lora_check_segments": (I32, [P, P, I32, I64, P, I32, I32]),
+        "lora_pack_greedy": (I32, [P, I32, I64, P, P]),
+        "lora_microbatch_segments": (I32, [P, P, P, I32, I32, I32, P, P, P, P, P]),
+        "lora_check_bubble_lemma": (I32, [P, P, P, I32, I32, I32, P]),
         "lora_dropout_mask": (I32, [U64, U64, I64, I64, F32, P, P]),
         "lora_frozen_fwd": (I32, [P, P, I64, I64, I64, P, P]),
         "lora_frozen_bwd": (I32, [P, P, I64, I64, I64, P, P]),
@@ -255,6 +259,44 @@ def multi_lora_check_segments(seg_off: Sequence[int], seg_adapter: Sequence[int]
     sa = (ctypes.c_int32 * len(seg_adapter))(*[int(v) for v in seg_adapter])
     rk = (ctypes.c_int32 * len(ranks))(*[int(v) for v in ranks])
     _check(load().multi_lora_check_segments(so, sa, len(seg_adapter), m, rk, len(ranks), r_max))
+
+
+def _i32_array(values: Sequence[int]):
+    return (ctypes.c_int32 * max(len(values), 1))(*[int(v) for v in values])
+
+
+def lora_pack_greedy(lengths: Sequence[int], capacity: int) -> Tuple[List[int], int]:
+    """(microbatch of each sample, number of microbatches); host only."""
+    n = len(lengths)
+    mb = (ctypes.c_int32 * max(n, 1))()
+    nmb = ctypes.c_int32(0)
+    _check(load().lora_pack_greedy(_i32_array(lengths), n, capacity, mb, ctypes.byref(nmb)))
+    return list(mb[:n]), nmb.value
+
+
+def lora_microbatch_segments(lengths: Sequence[int], adapter_of_sample: Sequence[int],
+                             mb_of_sample: Sequence[int], num_adapters: int,
+                             mb: int) -> Tuple[List[int], List[int], List[int]]:
+    """(sample order, seg_off, seg_adapter) of microbatch `mb`; host only."""
+    n = len(lengths)
+    order = (ctypes.c_int32 * max(n, 1))()
+    so = (ctypes.c_int64 * (num_adapters + 1))()
+    sa = (ctypes.c_int32 * num_adapters)()
+    nm, ns = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().lora_microbatch_segments(_i32_array(lengths), _i32_array(adapter_of_sample),
+                                           _i32_array(mb_of_sample), n, num_adapters, mb, order,
+                                           ctypes.byref(nm), so, sa, ctypes.byref(ns)))
+    return list(order[:nm.value]), list(so[:ns.value + 1]), list(sa[:ns.value])
+
+
+def lora_check_bubble_lemma(mb_of_sample: Sequence[int], adapter_of_sample: Sequence[int],
+                            batch_of_sample: Sequence[int], num_adapters: int, stages: int) -> int:
+    """Number of (adapter, batch) pairs whose next batch starts too early; host only."""
+    v = ctypes.c_int64(0)
+    _check(load().lora_check_bubble_lemma(_i32_array(mb_of_sample), _i32_array(adapter_of_sample),
+                                          _i32_array(batch_of_sample), len(mb_of_sample),
+                                          num_adapters, stages, ctypes.byref(v)))
+    return v.value
 
 
 def lora_dropout_mask(seed: int, offset: int, m: int, k: int, p: float, keep_bits=None,

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "device_common.hpp"
+#include "host_status.hpp"
 #include "launch.hpp"
 #include "lora_fused.h"
 
@@ -36,6 +37,18 @@ static lora_status fail(lora_status st, const char *fmt, ...) {
     g_last_error = buf;
     return st;
 }
+
+namespace lora {
+lora_status host_fail(lora_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+}  // namespace lora
 
 static lora_status hip_fail(hipError_t e, const char *what) {
     return fail(LORA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

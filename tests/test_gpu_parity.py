@@ -173,6 +173,33 @@ def test_multi_parity(case):
         check_close(f"dB[{a}]", g["dB"][a], o["dB"][a])
 
 
+def test_multi_parity_packed_microbatch():
+    # the host packer's output end to end: samples of four adapters packed into
+    # microbatches of at most 640 tokens; the segment table (rows grouped by
+    # adapter) of the one with the most adapters, then the most rows, drives
+    # the mixed-adapter forward and backward
+    rng = np.random.Generator(np.random.PCG64(41))
+    lengths = [int(v) for v in np.clip(np.rint(rng.lognormal(np.log(90.0), 0.75, 40)), 16, 400)]
+    adapters = [int(v) for v in rng.integers(0, 4, len(lengths))]
+    mb, count = lf.lora_pack_greedy(lengths, 640)
+    tables = [lf.lora_microbatch_segments(lengths, adapters, mb, 4, q) for q in range(count)]
+    _, seg_off, seg_ad = max(tables, key=lambda t: (len(t[2]), t[1][-1]))
+    m, k, n = seg_off[-1], 256, 264
+    ranks, alphas, ps = [16, 8, 32, 24], [2.0, 1.0, 0.5, 4.0], [0.1, 0.0, 0.2, 0.05]
+    log(f"packed microbatch: m={m} segs={seg_off} adapters={seg_ad}")
+    lf.multi_lora_check_segments(seg_off, seg_ad, m, ranks, max(ranks))
+    X, W, As, Bs, dY = multi_case(m, k, n, ranks, seed=141)
+    g = gpu_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, 9, 0)
+    o = oracle_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, 9, 0)
+    assert_bits_equal("keep_bits", g["keep"], o["bits"])
+    check_close("S", g["S"], o["S"], rel=1e-4)
+    check_close("Y", g["Y"], o["Y"])
+    check_close("dX", g["dX"], o["dX"])
+    for a in range(len(ranks)):
+        check_close(f"dA[{a}]", g["dA"][a], o["dA"][a])
+        check_close(f"dB[{a}]", g["dB"][a], o["dB"][a])
+
+
 def test_multi_single_segment_equals_single_bitwise():
     m, k, n, r = 640, 512, 264, 16
     X, W, As, Bs, dY = multi_case(m, k, n, [r], seed=7)
