@@ -50,7 +50,88 @@ def parse():
     ap.add_argument("--pack", action="store_true",
                     help="instead of the headline step: the host packer (greedy token-capacity "
                          "packing and segment tables) on a synthetic global batch; no GPU")
+    ap.add_argument("--dora", action="store_true",
+                    help="instead of the headline step: the DoRA norm of W + alpha A B per output "
+                         "feature at 8192 x 8192, ranks 16, 64 and 256 (one JSON line each)")
     return ap.parse_args()
+
+
+def dora_report(args):
+    """DoRA norm on the page's 8192 x 8192 weight shape.  One pass over W is the
+    compulsory traffic (bytes = 2kn + 2kr + 2rn + 4n per call); the kernel is
+    reported against HBM.  Beside it: the eager PyTorch form that builds the
+    dense A B (torch.linalg.vector_norm(W + alpha A B, dim=0) in fp32), and
+    the oracle on a column sample."""
+    import torch
+
+    import lora_fine_tuning_amd as lf
+
+    lf.load()
+    k = n = 8192
+    for r in (16, 64, 256):
+        g = torch.Generator(device="cuda").manual_seed(7 + r)
+        W = (torch.randn(k, n, device="cuda", generator=g) / k ** 0.5).bfloat16()
+        A = (torch.randn(k, r, device="cuda", generator=g) / k ** 0.5).bfloat16()
+        B = (torch.randn(r, n, device="cuda", generator=g) * 0.02 ** 0.5).bfloat16()
+        norm = torch.empty(n, dtype=torch.float32, device="cuda")
+        ws = torch.empty(lf.lora_dora_norm_workspace_size(k, n, r), dtype=torch.uint8, device="cuda")
+
+        def fused():
+            lf.lora_dora_norm(W, A, B, 2.0, norm=norm, workspace=ws)
+
+        def eager():
+            return torch.linalg.vector_norm(W.float() + 2.0 * (A.float() @ B.float()), dim=0)
+
+        for _ in range(args.warmup):
+            fused()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fused()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        # the pass over W alone: HIP events the library records on its launch stream
+        lf.lora_profiling_enable(True, capacity=4 * args.steps + 16)
+        lf.lora_profiling_reset()
+        for _ in range(args.steps):
+            fused()
+        c, tot = lf.lora_profiling_query("dora_norm_pass")
+        kern_ms = tot / max(c, 1)
+        lf.lora_profiling_enable(False)
+        for _ in range(2):
+            eager()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            eager()
+        e1.record()
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / 5
+        nbytes = 2 * k * n + 2 * k * r + 2 * r * n + 4 * n
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        line = {"metric": "DoRA norm of W + alpha A B per output feature, GB/s of compulsory traffic",
+                "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms": ms, "steps": args.steps,
+                "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16 in, fp32 sums",
+                "data": "synthetic", "config": {"workload": f"W {k} x {n}, r {r}"},
+                "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                "eager_torch": {"ms": eager_ms, "speedup": eager_ms / ms}}
+        if not args.no_cpu_baseline:
+            import numpy as np
+
+            import oracle
+            cols = np.arange(0, n, n // 16, dtype=np.int64)
+            Wc, Ac, Bc = (t.to("cpu", torch.float64).numpy() for t in (W, A, B))
+            t0 = time.perf_counter()
+            oracle.dora_norm(Wc, Ac, Bc, 2.0, cols=cols)
+            to = time.perf_counter() - t0
+            line["cpu_baseline"] = {"value": (len(cols) / n) * nbytes / to / 1e9, "unit": "GB/s",
+                                    "cores": oracle.num_threads(), "kind": "oracle",
+                                    "sample": f"{len(cols)} of {n} columns"}
+        print(json.dumps(line), flush=True)
+        del W, A, B, ws
 
 
 def pack_report(args):
@@ -303,6 +384,9 @@ def main():
         sys.exit(1)
     if args.configs:
         config_report(args)
+        return
+    if args.dora:
+        dora_report(args)
         return
     lf.load()
     dev = "cuda"

@@ -217,6 +217,24 @@ lora_status lora_check_bubble_lemma(const int32_t *mb_of_sample, const int32_t *
                                     const int32_t *batch_of_sample, int32_t num_samples,
                                     int32_t num_adapters, int32_t stages, int64_t *violations);
 
+/* ---- DoRA norm -----------------------------------------------------------
+ * DoRA rescales each output feature of the adapted weight by a learned
+ * magnitude over its norm.  This computes that norm for every output feature
+ * (a column here, since the layer is X W with W k x n):
+ *   norm[j] = || W[:, j] + alpha * (A B)[:, j] ||_2
+ * without storing the dense k x n product (page on the factored DoRA norm,
+ * "core method": the norm of W + sBA per output feature, s the LoRA scale).
+ * W (k x n), A (k x r) and B (r x n) are bf16 row-major device buffers,
+ * 16-byte aligned; norm is n fp32 (4-byte aligned).  Sums are fp32 and
+ * deterministic.  Requires 1 <= r <= 256, n % 8 == 0; the workspace holds
+ * per-split partial sums (lora_dora_norm_workspace_size bytes, 16-byte
+ * aligned).  LORA_ERR_UNSUPPORTED when A or B (with 32 spare rows) exceeds
+ * 2 GiB. */
+size_t lora_dora_norm_workspace_size(int64_t k, int64_t n, int32_t r);
+lora_status lora_dora_norm(const void *W, const void *A, const void *B, int64_t k, int64_t n,
+                           int32_t r, float alpha, float *norm, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* ---- pieces exposed for testing and as the frozen-layer baseline -------- */
 
 /* The dropout mask alone (same bits the forward stores). */

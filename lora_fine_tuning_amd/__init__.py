@@ -6,7 +6,8 @@ declared in include/lora_fused.h); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, LoraAdapter, LoraError, adapter_table, load, lora_check_bubble_lemma,
-    lora_dropout_mask, lora_microbatch_segments, lora_pack_greedy,
+    lora_dora_norm, lora_dora_norm_workspace_size, lora_dropout_mask, lora_microbatch_segments,
+    lora_pack_greedy,
     lora_frozen_bwd, lora_frozen_fwd, lora_linear_bwd, lora_linear_bwd_workspace_size,
     lora_linear_fwd, lora_linear_fwd_workspace_size, lora_profiling_enable,
     lora_profiling_query, lora_profiling_reset, multi_lora_bwd_workspace_size,

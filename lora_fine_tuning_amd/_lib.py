@@ -30,7 +30,7 @@ EXPORTS = [
     "lora_dropout_mask", "lora_frozen_fwd", "lora_frozen_bwd", "lora_profiling_enable",
     "lora_profiling_reset", "lora_profiling_query", "lora_status_string",
     "lora_last_error_message", "lora_pack_greedy", "lora_microbatch_segments",
-    "lora_check_bubble_lemma",
+    "lora_check_bubble_lemma", "lora_dora_norm_workspace_size", "lora_dora_norm",
 ]
 
 
@@ -75,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         P, SZ, P]),
         "multi_lora_check_segments": (I32, [P, P, I32, I64, P, I32, I32]),
         "lora_pack_greedy": (I32, [P, I32, I64, P, P]),
+        "lora_dora_norm_workspace_size": (SZ, [I64, I64, I32]),
+        "lora_dora_norm": (I32, [P, P, P, I64, I64, I32, F32, P, P, SZ, P]),
         "lora_microbatch_segments": (I32, [P, P, P, I32, I32, I32, P, P, P, P, P]),
         "lora_check_bubble_lemma": (I32, [P, P, P, I32, I32, I32, P]),
         "lora_dropout_mask": (I32, [U64, U64, I64, I64, F32, P, P]),
@@ -259,6 +261,24 @@ def multi_lora_check_segments(seg_off: Sequence[int], seg_adapter: Sequence[int]
     sa = (ctypes.c_int32 * len(seg_adapter))(*[int(v) for v in seg_adapter])
     rk = (ctypes.c_int32 * len(ranks))(*[int(v) for v in ranks])
     _check(load().multi_lora_check_segments(so, sa, len(seg_adapter), m, rk, len(ranks), r_max))
+
+
+def lora_dora_norm_workspace_size(k: int, n: int, r: int) -> int:
+    return int(load().lora_dora_norm_workspace_size(k, n, r))
+
+
+def lora_dora_norm(W, A, B, alpha: float, *, norm=None, workspace=None, stream=None):
+    """norm[j] = || W[:, j] + alpha (A B)[:, j] ||_2 (fp32, n values)."""
+    _need(W, torch.bfloat16, "W")
+    _need(A, torch.bfloat16, "A")
+    _need(B, torch.bfloat16, "B")
+    k, n = W.shape
+    r = A.shape[1]
+    norm = torch.empty(n, dtype=torch.float32, device=W.device) if norm is None else norm
+    ws = _workspace(lora_dora_norm_workspace_size(k, n, r), W.device, workspace)
+    _check(load().lora_dora_norm(_ptr(W), _ptr(A), _ptr(B), k, n, r, alpha, _ptr(norm), _ptr(ws),
+                                 ws.numel(), _stream(stream)))
+    return norm
 
 
 def _i32_array(values: Sequence[int]):

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "liblora_fused.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["api.cpp", "packer.cpp", "lowrank_kernels.hip", "gemm_kernels.hip"]
+SOURCES = ["api.cpp", "packer.cpp", "lowrank_kernels.hip", "gemm_kernels.hip", "dora_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

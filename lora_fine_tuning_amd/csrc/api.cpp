@@ -576,6 +576,39 @@ extern "C" lora_status multi_lora_check_segments(const int64_t *seg_off_host, co
 }
 
 // ---------------------------------------------------------------------------
+// DoRA norm
+// ---------------------------------------------------------------------------
+extern "C" size_t lora_dora_norm_workspace_size(int64_t k, int64_t n, int32_t r) {
+    (void)r;
+    if (k <= 0 || n <= 0 || k >= (1LL << 31) || n >= (1LL << 31)) return 0;
+    const DoraPlan pl = dora_plan(k, n);
+    return (size_t)pl.splits * (size_t)n * sizeof(float);
+}
+
+extern "C" lora_status lora_dora_norm(const void *W, const void *A, const void *B, int64_t k, int64_t n,
+                                      int32_t r, float alpha, float *norm, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    REQUIRE(k > 0 && k < (1LL << 31), "k = %lld out of range (0, 2^31)", (long long)k);
+    REQUIRE(n > 0 && n < (1LL << 31), "n = %lld out of range (0, 2^31)", (long long)n);
+    REQUIRE(n % 8 == 0, "n = %lld must be a multiple of 8", (long long)n);
+    CHECK(check_rank(r));
+    REQ_PTR(W, 16);
+    REQ_PTR(A, 16);
+    REQ_PTR(B, 16);
+    REQ_PTR(norm, 4);
+    if ((int64_t)(r + 32) * n * 2 >= (1LL << 31) || k * (int64_t)r * 2 >= (1LL << 31))
+        return fail(LORA_ERR_UNSUPPORTED, "A or B exceeds 2 GiB");
+    const DoraPlan pl = dora_plan(k, n);
+    const size_t need = (size_t)pl.splits * (size_t)n * sizeof(float);
+    if (workspace_bytes < need)
+        return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    REQ_PTR(workspace, 16);
+    HIPCHK(launch_dora_norm(W, A, B, (int)k, (int)n, r, alpha, pl, (float *)workspace, norm, stream),
+           "DoRA norm launch");
+    return LORA_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Pieces
 // ---------------------------------------------------------------------------
 extern "C" lora_status lora_dropout_mask(uint64_t seed, uint64_t offset, int64_t m, int64_t k, float p,

@@ -847,29 +847,9 @@ __global__ __launch_bounds__(256) void b2_kernel(B2Params P) {
 // (dY or X) and the small per-row operands (alpha*S or dS, the keep words)
 // flow global -> LDS through a 3-stage ring of direct-to-LDS loads, so two
 // sub-blocks are in flight while a third is consumed and no VGPRs stage data.
-// Tiles of 256 bf16 columns have 512-byte LDS rows with an XOR swizzle of
-// their 16-byte chunks that is conflict-free both for 16-lane b128 reads of
-// 16 consecutive rows and for 32-lane transposing reads of rows {0-3, 8-11}
-// (or {4-7, 12-15}) over two chunks.  The transposing reads hand each lane 8
-// consecutive rows of one column: the MFMA operand of a contraction over rows.
+// The tiles use the 512-byte-row swizzle and transposing reads of
+// device_common.hpp (swz512_off, tile_rows8).
 // ===========================================================================
-__device__ __forceinline__ int swz512(int r) {
-    return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
-}
-__device__ __forceinline__ uint32_t swz512_off(int row, int chunk) {
-    return (uint32_t)(row * 512 + ((chunk ^ swz512(row)) << 4));
-}
-// 8 consecutive rows (row0 .. row0+7, row0 % 8 == 0) of column 16*cb + (lane % 16)
-// of a swizzled 512-byte-row tile, as one MFMA operand.
-__device__ __forceinline__ uint4 tile_rows8(const lds_char *tile, int row0, int cb, int lane) {
-    const int a = lane & 15;
-    const int chunk = 2 * cb + ((a & 3) >> 1);
-    const int row = row0 + (a >> 2);
-    const uint2 lo = lds_read_tr4(tile + swz512_off(row, chunk) + (a & 1) * 8);
-    const uint2 hi = lds_read_tr4(tile + swz512_off(row + 4, chunk) + (a & 1) * 8);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-constexpr uint32_t kOOBL = 0x80000000u;  // an offset beyond every descriptor range
 
 // ----- B2 streaming: sub-blocks of 32 rows; stage = X 16 KiB + 8 aux KiB
 constexpr int B2S_ROWS = 32, B2S_X = 32 * 512, B2S_STAGE = B2S_X + 8 * 1024, B2S_NST = 3;

@@ -73,6 +73,7 @@ def _load():
         "oracle_lora_db_acc": (None, [P, P, I64, I64, I64, F64, P]),
         "oracle_lora_da_acc": (None, [P, P, P, I64, I64, I64, F32, P]),
         "oracle_num_threads": (ctypes.c_int, []),
+        "oracle_dora_norm": (None, [P, P, P, I64, I64, I64, F64, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -178,6 +179,20 @@ def lora_dx(dY, W, dS, A, keep, p) -> np.ndarray:
     if nrows:
         _load().oracle_lora_dx(_p(dY), _p(W), _p(dS), _p(A), _p(keep), nrows, k, n, r, p, _p(dX))
     return dX
+
+
+def dora_norm(W, A, B, alpha, cols=None) -> np.ndarray:
+    """|| W[:, j] + alpha (A B)[:, j] ||_2 for j in cols (all columns by default);
+    the page on the factored DoRA norm, "core method" (the norm of W + sBA per
+    output feature), written densely."""
+    W, A, B = _f64(W), _f64(A), _f64(B)
+    k, n = W.shape
+    r = A.shape[1]
+    cols = np.arange(n, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.zeros(len(cols), dtype=np.float64)
+    if len(cols):
+        _load().oracle_dora_norm(_p(W), _p(A), _p(B), k, n, r, float(alpha), _p(cols), len(cols), _p(out))
+    return out
 
 
 def lora_db_acc(S, dY, alpha, dB: np.ndarray) -> None:

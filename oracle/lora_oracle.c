@@ -35,6 +35,7 @@
  * each function; the arithmetic inside is a direct transcription of the
  * definition above.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -218,6 +219,28 @@ void oracle_lora_da_acc(const double *X, const uint8_t *keep, const double *dS, 
             }
             dA[t * r + c] += acc;
         }
+    }
+}
+
+/* DoRA norm of the adapted weight per output feature (page on the factored
+ * DoRA norm, "core method": the norm of W + sBA per output feature, with s the
+ * LoRA scale; with X W and W k x n an output feature is a column):
+ *   out[q] = sqrt( sum_i ( W[i][j] + alpha * sum_t A[i][t] B[t][j] )^2 ),
+ * j = cols[q].  The definition itself, dense, in double. */
+void oracle_dora_norm(const double *W, const double *A, const double *B, int64_t k, int64_t n, int64_t r,
+                      double alpha, const int64_t *cols, int64_t ncols, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < ncols; ++q) {
+        int64_t j = cols[q];
+        double acc = 0.0;
+        for (int64_t i = 0; i < k; ++i) {
+            double ab = 0.0;
+            for (int64_t t = 0; t < r; ++t) ab += A[i * r + t] * B[t * n + j];
+            double v = W[i * n + j] + alpha * ab;
+            acc += v * v;
+        }
+        out[q] = sqrt(acc);
     }
 }
 

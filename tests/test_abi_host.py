@@ -141,6 +141,20 @@ def test_mask_and_frozen_reject(lib):
     assert lib.lora_frozen_bwd(FAKE, FAKE + 8, 8, 16, 8, FAKE, None) == INVALID
 
 
+def test_dora_norm_rejects(lib):
+    f = lib.lora_dora_norm
+    ws = lf.lora_dora_norm_workspace_size(64, 64, 8)
+    assert ws > 0
+    assert f(FAKE, FAKE, FAKE, 64, 64, 0, 1.0, FAKE, FAKE, ws, None) == INVALID     # r = 0
+    assert f(FAKE, FAKE, FAKE, 64, 64, 257, 1.0, FAKE, FAKE, ws, None) == INVALID   # r > 256
+    assert f(FAKE, FAKE, FAKE, 64, 12, 8, 1.0, FAKE, FAKE, ws, None) == INVALID     # n % 8
+    assert f(FAKE, FAKE, FAKE, 0, 64, 8, 1.0, FAKE, FAKE, ws, None) == INVALID      # k = 0
+    assert f(FAKE + 8, FAKE, FAKE, 64, 64, 8, 1.0, FAKE, FAKE, ws, None) == INVALID  # W alignment
+    assert f(FAKE, FAKE, FAKE, 64, 64, 8, 1.0, None, FAKE, ws, None) == INVALID     # norm NULL
+    assert f(FAKE, FAKE, FAKE, 64, 64, 8, 1.0, FAKE, FAKE, ws - 4, None) == WORKSPACE
+    assert f(FAKE, FAKE, FAKE, 64, 1 << 22, 256, 1.0, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+
+
 def test_check_segments():
     lf.multi_lora_check_segments([0, 5, 5, 12], [1, 0, 1], 12, [4, 8], 8)
     bad = [
