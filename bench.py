@@ -53,7 +53,64 @@ def parse():
     ap.add_argument("--dora", action="store_true",
                     help="instead of the headline step: the DoRA norm of W + alpha A B per output "
                          "feature at 8192 x 8192, ranks 16, 64 and 256 (one JSON line each)")
+    ap.add_argument("--concat", action="store_true",
+                    help="instead of the headline step: at p = 0, the library's forward against the "
+                         "concatenated down-projection X [W | A] plus a separate Y += alpha S B pass")
     return ap.parse_args()
+
+
+def concat_report(args):
+    """The concatenated down-projection for p = 0: S comes out of the base GEMM
+    as r extra output columns (X [W | A]), so X is read once, but the LoRA term
+    then needs its own pass over Y (Y += alpha S B, read and write of Y) because
+    no work-group holds S for its rows before its epilogue.  Timed from its
+    parts on the headline shapes: this library's GEMM on the k x (n + r) weight
+    (its 256-column tiles give the r extra columns a tile of their own), and
+    torch.addmm for the update (hipBLASLt with beta = 1).  Beside it, the
+    library's forward at p = 0 (the mask-free F1 pass over X, then the GEMM
+    with the LoRA term in its epilogue)."""
+    import torch
+
+    import lora_fine_tuning_amd as lf
+
+    lf.load()
+    m, k, r, alpha = args.m, 4096, args.r, 2.0
+    g = torch.Generator(device="cuda").manual_seed(3)
+
+    def timed(fn, iters):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    for n in (int(v) for v in args.shapes.split(",")):
+        X = torch.randn(m, k, device="cuda", generator=g).bfloat16()
+        W = (torch.randn(k, n, device="cuda", generator=g) / k ** 0.5).bfloat16()
+        A = (torch.randn(k, r, device="cuda", generator=g) / k ** 0.5).bfloat16()
+        B = (torch.randn(r, n, device="cuda", generator=g) * 0.02 ** 0.5).bfloat16()
+        Wc = torch.cat([W, A], dim=1).contiguous()
+        Y = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+        Yc = torch.empty(m, n + r, device="cuda", dtype=torch.bfloat16)
+        S = torch.empty(m, r, device="cuda", dtype=torch.float32)
+        ws = torch.empty(max(lf.lora_linear_fwd_workspace_size(m, k, n, r), 1), dtype=torch.uint8, device="cuda")
+        Sb = torch.randn(m, r, device="cuda", generator=g).bfloat16()
+        fused = timed(lambda: lf.lora_linear_fwd(X, W, A, B, alpha, 0.0, Y=Y, S=S, workspace=ws), args.steps)
+        gemm_cat = timed(lambda: lf.lora_frozen_fwd(X, Wc, Y=Yc), args.steps)
+        gemm = timed(lambda: lf.lora_frozen_fwd(X, W, Y=Y), args.steps)
+        update = timed(lambda: Y.addmm_(Sb, B, alpha=alpha), args.steps)
+        print(json.dumps({"metric": "forward ms at p = 0: fused path vs concatenated down-projection",
+                          "config": {"workload": f"m {m} k {k} n {n} r {r}"},
+                          "fused_fwd_ms": fused, "frozen_gemm_ms": gemm,
+                          "concat_gemm_ms": gemm_cat, "update_pass_ms": update,
+                          "concat_total_ms": gemm_cat + update,
+                          "concat_over_fused": (gemm_cat + update) / fused}), flush=True)
+        del X, W, A, B, Wc, Y, Yc, S, ws, Sb
 
 
 def dora_report(args):
@@ -387,6 +444,9 @@ def main():
         return
     if args.dora:
         dora_report(args)
+        return
+    if args.concat:
+        concat_report(args)
         return
     lf.load()
     dev = "cuda"
