@@ -58,6 +58,8 @@ SINGLE_CASES = [
     (333, 264, 264, 36, 1.0, 0.2),     # rank tiles, second one ragged (rank not a multiple of 8)
     (520, 1024, 264, 96, 0.5, 0.1),    # three rank tiles
     (300, 264, 136, 80, 1.0, 0.1),     # ranks past 64 with a ragged last column tile of dX
+    (200, 136, 8, 4, 0.0, 0.5),        # alpha 0 (the LoRA term and its gradients vanish), n = 8
+    (128, 256, 264, 16, 2.0, 0.95),    # heavy dropout: scale 20
 ]
 
 
@@ -70,6 +72,31 @@ def test_single_parity(m, k, n, r, alpha, p):
     o = oracle_single(X, W, A, B, dY, alpha, p, seed, offset)
     stats = compare_single(g, o, p)
     log(f"  {stats}")
+
+
+def offset_view(t: torch.Tensor) -> torch.Tensor:
+    """The same values on the GPU, one element (2 bytes) past a 16-byte boundary."""
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device="cuda")
+    v = buf[1:1 + t.numel()].view(t.shape)
+    v.copy_(t.to("cuda"))
+    return v
+
+
+@pytest.mark.parametrize("m,k,n,r", [(300, 264, 264, 16), (333, 264, 264, 64), (257, 512, 136, 24)])
+def test_single_unaligned_adapter(m, k, n, r):
+    # A, B, dA and dB only need 2-byte alignment: the 16-byte paths must step aside
+    log(f"unaligned adapter m={m} k={k} n={n} r={r}")
+    X, W, A, B, dY = small_case(m, k, n, r, seed=3 * m + r)
+    Ad, Bd = offset_view(A), offset_view(B)
+    assert Ad.data_ptr() % 16 == 2 and Bd.data_ptr() % 16 == 2
+    dA, dB = offset_view(torch.zeros_like(A)), offset_view(torch.zeros_like(B))
+    Xd, Wd, dYd = X.cuda(), W.cuda(), dY.cuda()
+    Y, S, keep = lf.lora_linear_fwd(Xd, Wd, Ad, Bd, 2.0, 0.1, 5, 0)
+    dX, _, _ = lf.lora_linear_bwd(dYd, Xd, Wd, Ad, Bd, S, keep, 2.0, 0.1, dA=dA, dB=dB)
+    torch.cuda.synchronize()
+    g = {"Y": Y.cpu(), "S": S.cpu(), "keep": keep.cpu(), "dX": dX.cpu(), "dA": dA.cpu(), "dB": dB.cpu()}
+    o = oracle_single(X, W, A, B, dY, 2.0, 0.1, 5, 0)
+    log(f"  {compare_single(g, o, 0.1)}")
 
 
 def test_single_config0_workload():
