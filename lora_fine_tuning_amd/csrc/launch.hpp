@@ -24,6 +24,11 @@ inline int rank_tiles(int r_lds) { return r_lds > 32 ? (r_lds + 31) / 32 : 1; }
 // F1's streaming form (each work-group covers all of k, no partial sums)
 // serves ranks up to 128; its 32-bit buffer offsets need 64*k < 2^31.
 inline bool f1_streaming(int r_lds, int64_t k) { return r_lds <= 128 && k * 64 < (int64_t(1) << 31); }
+// The single-adapter streaming F1 takes rank tiles of 64 when the rank spans an
+// even number of 32-rank tiles (33..64, 97..128).
+inline bool f1_rank64(int r_lds, bool multi) {
+    return !multi && r_lds > 32 && r_lds <= 128 && ((r_lds + 31) / 32) % 2 == 0;
+}
 
 // Rows per B2 work item (the dA partials are one per item): 256, or taller
 // when the grid (items x 256-column tiles of k x rank tiles) would still have

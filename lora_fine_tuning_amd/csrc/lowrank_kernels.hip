@@ -1384,10 +1384,17 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
         // streaming form: 4 work-groups of 16 rows per chunk, all of k each,
         // times the rank tiles
         const dim3 g4(4 * chunk_cap, rank_tiles(P.r_lds));
-        if (P.r_lds <= 16)
+        if (P.r_lds <= 16) {
             launch_with_lds(f1s_kernel<1>, g4, (size_t)F1S_WAVES * 2 * F1S_UNIT * 16 * 2, stream, P, 64 * F1S_WAVES);
-        else
+        } else if (f1_rank64(P.r_lds, src.table != nullptr)) {
+            // one adapter with an even number of 32-rank tiles: half as many
+            // passes over X in tiles of 64 (one work-group per CU; measured
+            // faster at 64 and 128 ranks, slower at 96)
+            launch_with_lds(f1s_kernel<4>, dim3(4 * chunk_cap, (P.r_lds + 63) / 64),
+                            (size_t)F1S_WAVES * 1 * F1S_UNIT * 64 * 2, stream, P, 64 * F1S_WAVES);
+        } else {
             launch_with_lds(f1s_kernel<2>, g4, (size_t)F1S_WAVES * 1 * F1S_UNIT * 32 * 2, stream, P, 64 * F1S_WAVES);
+        }
         return finish_launch(slot, stream);
     }
     const dim3 grid(chunk_cap, KS);
