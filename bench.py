@@ -425,7 +425,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU path is a design note, not part of this build", file=sys.stderr)
+              "sharding over several GPUs is described, not implemented", file=sys.stderr)
         sys.exit(2)
     if args.pack:
         pack_report(args)
