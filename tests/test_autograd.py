@@ -1,0 +1,69 @@
+"""The autograd glue (lora_fine_tuning_amd/autograd.py) against direct C-ABI
+calls and the oracle: the Function returns exactly the library's outputs and
+gradients for inputs with leading batch dimensions, and the module advances
+its dropout counter so calls get fresh, reproducible masks."""
+import numpy as np
+import pytest
+import torch
+
+import lora_fine_tuning_amd as lf
+from parity import bf16_randn, check_close, f64, oracle_single
+
+
+def case(seed, b=2, t=150, k=264, n=136, r=16):
+    g = torch.Generator().manual_seed(seed)
+    X = bf16_randn((b, t, k), 1.0, g)
+    W = bf16_randn((k, n), (1.0 / k) ** 0.5, g)
+    A = bf16_randn((k, r), (1.0 / k) ** 0.5, g)
+    B = bf16_randn((r, n), 0.02 ** 0.5, g)
+    dY = bf16_randn((b, t, n), 1.0, g)
+    return X, W, A, B, dY
+
+
+@pytest.mark.gpu
+def test_function_matches_library_and_oracle():
+    X, W, A, B, dY = case(1)
+    Xd, Wd, dYd = X.cuda().requires_grad_(), W.cuda(), dY.cuda()
+    Ad, Bd = A.cuda().requires_grad_(), B.cuda().requires_grad_()
+    Y = lf.lora_linear(Xd, Wd, Ad, Bd, 2.0, 0.1, 11, 8)
+    Y.backward(dYd)
+    torch.cuda.synchronize()
+    # the same calls by hand
+    X2 = X.reshape(-1, X.shape[-1]).cuda()
+    Yr, S, keep = lf.lora_linear_fwd(X2, Wd, Ad.detach(), Bd.detach(), 2.0, 0.1, 11, 8)
+    dX, dA, dB = lf.lora_linear_bwd(dYd.reshape(-1, dY.shape[-1]), X2, Wd, Ad.detach(), Bd.detach(), S, keep,
+                                    2.0, 0.1)
+    assert torch.equal(Y.detach().reshape(-1, Y.shape[-1]), Yr)
+    assert torch.equal(Xd.grad.reshape(-1, X.shape[-1]), dX)
+    assert torch.equal(Ad.grad, dA) and torch.equal(Bd.grad, dB)
+    o = oracle_single(X.reshape(-1, X.shape[-1]), W, A, B, dY.reshape(-1, dY.shape[-1]), 2.0, 0.1, 11, 8)
+    check_close("Y", Y.detach().reshape(-1, Y.shape[-1]).cpu(), o["Y"])
+    check_close("dX", Xd.grad.reshape(-1, X.shape[-1]).cpu(), o["dX"])
+    check_close("dA", Ad.grad.cpu(), o["dA"])
+    check_close("dB", Bd.grad.cpu(), o["dB"])
+
+
+@pytest.mark.gpu
+def test_module_dropout_counter():
+    X, W, A, B, dY = case(2)
+    m1 = lf.LoraLinear(W.cuda(), 16, 2.0, 0.2, seed=5)
+    with torch.no_grad():
+        m1.B.copy_(B.cuda())
+    Xd = X.cuda()
+    y1 = m1(Xd)
+    y2 = m1(Xd)
+    assert m1.offset == 2 * X.numel()
+    assert not torch.equal(y1, y2)            # a fresh mask on the second call
+    m2 = lf.LoraLinear(W.cuda(), 16, 2.0, 0.2, seed=5)
+    with torch.no_grad():
+        m2.B.copy_(B.cuda())
+    assert torch.equal(m2(Xd), y1)            # the same state reproduces the first mask
+    m2.eval()
+    ye = m2(Xd)
+    assert m2.offset == X.numel()             # no dropout, no counter use
+    ref = f64(X.reshape(-1, X.shape[-1])) @ f64(W) + 2.0 * (f64(X.reshape(-1, X.shape[-1])) @ f64(m2.A.detach().cpu())) @ f64(B)
+    check_close("eval Y", ye.reshape(-1, ye.shape[-1]).cpu(), ref)
+    # gradients reach A and B, not the frozen weight
+    m2.train()
+    m2(Xd).float().sum().backward()
+    assert m2.A.grad is not None and m2.B.grad is not None and not m2.weight.requires_grad
