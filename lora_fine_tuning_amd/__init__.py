@@ -14,4 +14,6 @@ from ._lib import (  # noqa: F401
     multi_lora_check_segments, multi_lora_fwd_workspace_size, multi_lora_linear_bwd,
     multi_lora_linear_fwd,
 )
-from .autograd import LoraLinear, LoraLinearFunction, lora_linear  # noqa: F401,E402
+from .autograd import (  # noqa: F401,E402
+    LoraLinear, LoraLinearFunction, MultiLoraLinearFunction, lora_linear, multi_lora_linear,
+)

@@ -40,6 +40,42 @@ def lora_linear(X, W, A, B, alpha: float, p: float = 0.0, seed: int = 0, offset:
     return LoraLinearFunction.apply(X, W, A, B, alpha, p, seed, offset)
 
 
+class MultiLoraLinearFunction(torch.autograd.Function):
+    """Mixed-adapter batch: rows [seg_off[s], seg_off[s+1]) of X (m x k) use
+    adapter seg_adapter[s]; the adapters come as A0, B0, A1, B1, ... and each
+    gets its gradients summed over its rows (papers.chlience.com notes, section
+    5 "FusedMultiLoRA")."""
+
+    @staticmethod
+    def forward(ctx, X, W, seg_off, seg_adapter, alphas, ps, seed: int, offset: int, *AB):
+        As, Bs = AB[0::2], AB[1::2]
+        r_max = max(a.shape[1] for a in As)
+        table = _lib.adapter_table(As, Bs, alphas, ps)
+        Y, S, keep = _lib.multi_lora_linear_fwd(X, W, table, len(As), seg_off, seg_adapter, r_max, seed, offset)
+        ctx.save_for_backward(X, W, seg_off, seg_adapter, S, keep, *AB)
+        ctx.alphas, ctx.ps, ctx.r_max = list(alphas), list(ps), r_max
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, W, seg_off, seg_adapter, S, keep, *AB = ctx.saved_tensors
+        As, Bs = AB[0::2], AB[1::2]
+        dAs = [torch.empty_like(a) for a in As]
+        dBs = [torch.empty_like(b) for b in Bs]
+        table = _lib.adapter_table(As, Bs, ctx.alphas, ctx.ps, dAs, dBs)
+        dX = _lib.multi_lora_linear_bwd(dY.contiguous(), X, W, table, len(As), seg_off, seg_adapter, S, keep,
+                                        ctx.r_max)
+        grads = []
+        for da, db in zip(dAs, dBs):
+            grads += [da, db]
+        return (dX, None, None, None, None, None, None, None, *grads)
+
+
+def multi_lora_linear(X, W, seg_off, seg_adapter, As, Bs, alphas, ps, seed: int = 0, offset: int = 0):
+    AB = [t for pair in zip(As, Bs) for t in pair]
+    return MultiLoraLinearFunction.apply(X, W, seg_off, seg_adapter, list(alphas), list(ps), seed, offset, *AB)
+
+
 class LoraLinear(torch.nn.Module):
     """A frozen k x n weight with one LoRA adapter (A k x r, B r x n; B starts
     at zero).  Dropout draws from the library's counter-based generator under
