@@ -45,6 +45,7 @@
 namespace lora {
 
 constexpr int GBM = 256, GBN = 256;
+constexpr int kStoreNT = 2;  // buffer-store cache policy: nt (non-temporal)
 
 struct GemmParams {
     const uint16_t *Arow;  // M x K
@@ -551,10 +552,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         for (int it = 0; it < 32; ++it) {
             const int r = it * 4 + (lane >> 4);
             const uint4 v = *(const uint4 *)(cw + r * 256 + ((cc ^ (r & 15)) << 4));
-            // rows past M fall outside rC; columns past N are dropped here
+            // rows past M fall outside rC; columns past N are dropped here.
+            // Non-temporal stores (cache-policy bit nt): the output is not
+            // read again by this kernel, and writing it through while the
+            // matrix cores are busy keeps it from sitting dirty in the caches
+            // and being written back under the next kernel's loads.
             const uint32_t off = col < P.N ? (uint32_t)((size_t)(wrow0 + r - m0) * N2 + (size_t)col * 2) : kOOB;
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
-                                                   rC, off, 0, 0);
+                                                   rC, off, 0, kStoreNT);
         }
     };
 
