@@ -829,23 +829,46 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 
     // ---- B3, single adapter with r <= 64: the column-side A fragments (one
     // or two rank chunks of 32) are the same for every 16-row band, loaded once
+    // Mixed adapters, a wave whose rows meet exactly two segments of ranks <=
+    // 32: the same two fragment slots hold the first item's ranks 0..31 and
+    // the second item's; rows outside an item read zeros, so each band adds
+    // both terms.  Both items and their fragments are looked up once, not per
+    // band.
     uint4 cf1[2][NT16];
     bool one_chunk = false;  // r <= 64 (the name predates the second chunk)
-    ExtItem it1;
-    bool rvec1 = false;
+    ExtItem it1, it2;        // items of fragment slots 0 and 1
+    int rk2 = 32;            // first rank of slot 1
+    bool rvec1 = false, rvec2 = false;
     if (EPI == 2 && (!MULTI || wave_one_seg)) {
         if (MULTI) it1 = wit;
         else get_item<EPI, MULTI>(P, 0, it1);
         one_chunk = it1.r <= 64 || (!MULTI && ahi);
-        rvec1 = svec && (it1.r & 7) == 0;
-        if (one_chunk) {
-            const bool avec = (it1.r & 7) == 0 && (((uintptr_t)it1.w) & 15) == 0;
-            const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it1, wcol0);
+        it2 = it1;
+        rvec1 = rvec2 = svec && (it1.r & 7) == 0;
+    }
+    if constexpr (MULTI && EPI == 2) {
+        if (!wave_one_seg && wrow0 < P.M && wseg < P.nseg) {
+            int s2 = wseg + 1;
+            while (s2 < P.nseg && P.seg_off[s2 + 1] <= P.seg_off[s2]) ++s2;  // skip empty segments
+            if (s2 < P.nseg && get_item<EPI, MULTI>(P, wseg, it1) && get_item<EPI, MULTI>(P, s2, it2) &&
+                it1.lo <= wrow0 && it1.hi == it2.lo && it2.hi >= min(wrow0 + 128, P.M) && it1.r <= 32 &&
+                it2.r <= 32) {
+                one_chunk = true;
+                rk2 = 0;
+                rvec1 = svec && (it1.r & 7) == 0;
+                rvec2 = svec && (it2.r & 7) == 0;
+            }
+        }
+    }
+    if (EPI == 2 && one_chunk) {
+        const bool avec1 = (it1.r & 7) == 0 && (((uintptr_t)it1.w) & 15) == 0;
+        const bool avec2 = (it2.r & 7) == 0 && (((uintptr_t)it2.w) & 15) == 0;
+        const __amdgpu_buffer_rsrc_t rW1 = ext_rsrc<EPI>(P, it1, wcol0);
+        const __amdgpu_buffer_rsrc_t rW2 = ext_rsrc<EPI>(P, it2, wcol0);
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int tn = 0; tn < NT16; ++tn)
-                    cf1[c][tn] = col_ext_frag<EPI>(P, rW, wcol0, it1, wcol0 + tn * 16 + l16, 32 * c, lane, avec);
+        for (int tn = 0; tn < NT16; ++tn) {
+            cf1[0][tn] = col_ext_frag<EPI>(P, rW1, wcol0, it1, wcol0 + tn * 16 + l16, 0, lane, avec1);
+            cf1[1][tn] = col_ext_frag<EPI>(P, rW2, wcol0, it2, wcol0 + tn * 16 + l16, rk2, lane, avec2);
         }
     }
 
@@ -869,17 +892,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
             for (int tn = 0; tn < NT16; ++tn) acc2[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (one_chunk) {
-                // both chunks' row-side loads first; the second is all zeros
-                // (out-of-range offsets) when r <= 32
+                // both slots' row-side loads first; one item with r <= 32
+                // leaves slot 1 all zeros (out-of-range offsets)
                 uint4 hi0, lo0, hi1, lo1;
                 row_ext_frags(P, rS, wrow0, it1, row, 0, lane, rvec1, hi0, lo0);
-                row_ext_frags(P, rS, wrow0, it1, row, 32, lane, rvec1, hi1, lo1);
+                row_ext_frags(P, rS, wrow0, it2, row, rk2, lane, rvec2, hi1, lo1);
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) {
                     acc2[tn] = mfma16x16x32(cf1[0][tn], hi0, acc2[tn]);
                     acc2[tn] = mfma16x16x32(cf1[0][tn], lo0, acc2[tn]);
                 }
-                if (it1.r > 32) {
+                if (it1.r > 32 || rk2 == 0) {
 #pragma unroll
                     for (int tn = 0; tn < NT16; ++tn) {
                         acc2[tn] = mfma16x16x32(cf1[1][tn], hi1, acc2[tn]);
