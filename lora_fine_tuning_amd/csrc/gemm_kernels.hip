@@ -929,16 +929,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             } else {
                 const int band0 = wrow0 + tm * 16;
                 int s_begin = 0, s_end = 1;
-                if (MULTI) {
+                if (MULTI && !wave_one_seg) {
                     // first segment ending past the band, stepping on from the wave's
                     s_begin = wseg;
                     while (s_begin < P.nseg && P.seg_off[s_begin + 1] <= (int64_t)band0) ++s_begin;
                     s_end = P.nseg;
                 }
                 for (int s = s_begin; s < s_end; ++s) {
-                    if (MULTI && P.seg_off[s] >= (int64_t)(band0 + 16)) break;
                     ExtItem it;
-                    if (!get_item<EPI, MULTI>(P, s, it)) continue;
+                    if (MULTI && wave_one_seg) {
+                        it = wit;  // the wave's one segment, looked up once
+                    } else {
+                        if (MULTI && P.seg_off[s] >= (int64_t)(band0 + 16)) break;
+                        if (!get_item<EPI, MULTI>(P, s, it)) continue;
+                    }
                     if (it.hi <= band0 || it.lo >= band0 + 16) continue;
                     const bool rvec = svec && (it.r & 7) == 0;
                     const bool avec = (it.r & 7) == 0 && (((uintptr_t)it.w) & 15) == 0;
