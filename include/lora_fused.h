@@ -123,7 +123,8 @@ size_t lora_linear_bwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r
  * blog, section 4.1, backward items 3 and 5): one pass over dY yields dS and
  * dB; one pass over X and the mask yields dA; an MFMA GEMM computes dY W^T
  * and adds the masked s*(dS A^T) before the single write of dX.  m == 0
- * writes zero dA and dB. */
+ * writes zero dA and dB.  dX may be NULL: the input gradient is then not
+ * computed (its GEMM is skipped), e.g. for a layer whose input needs none. */
 lora_status lora_linear_bwd(const void *dY, const void *X, const void *W, const void *A,
                             const void *B, const float *S, const uint32_t *keep_bits,
                             int64_t m, int64_t k, int64_t n, int32_t r, float alpha, float p,
@@ -154,7 +155,8 @@ size_t multi_lora_bwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r_
 
 /* Backward for a mixed-adapter batch: dX, and every adapter's dA and dB
  * (through the pointers in the adapter table; summed over all of that
- * adapter's rows; zero for adapters with no rows). */
+ * adapter's rows; zero for adapters with no rows).  dX may be NULL: the input
+ * gradient is then not computed. */
 lora_status multi_lora_linear_bwd(const void *dY, const void *X, const void *W,
                                   const lora_adapter *adapters, int32_t num_adapters,
                                   const int64_t *seg_off, const int32_t *seg_adapter,

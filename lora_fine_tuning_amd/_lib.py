@@ -170,8 +170,8 @@ def lora_linear_fwd(X, W, A, B, alpha: float, p: float, seed: int = 0, offset: i
 
 
 def lora_linear_bwd(dY, X, W, A, B, S, keep_bits, alpha: float, p: float, *, dX=None, dA=None,
-                    dB=None, workspace=None, stream=None):
-    """Returns (dX, dA, dB)."""
+                    dB=None, workspace=None, stream=None, want_dX: bool = True):
+    """Returns (dX, dA, dB); dX is None (and its GEMM skipped) when want_dX is False."""
     for t, nm in ((dY, "dY"), (X, "X"), (W, "W"), (A, "A"), (B, "B")):
         _need(t, torch.bfloat16, nm)
     _need(S, torch.float32, "S")
@@ -179,7 +179,10 @@ def lora_linear_bwd(dY, X, W, A, B, S, keep_bits, alpha: float, p: float, *, dX=
     n = W.shape[1]
     r = A.shape[1]
     dev = X.device
-    dX = torch.empty((m, k), dtype=torch.bfloat16, device=dev) if dX is None else dX
+    if want_dX and dX is None:
+        dX = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    if not want_dX:
+        dX = None
     dA = torch.empty((k, r), dtype=torch.bfloat16, device=dev) if dA is None else dA
     dB = torch.empty((r, n), dtype=torch.bfloat16, device=dev) if dB is None else dB
     ws = _workspace(lora_linear_bwd_workspace_size(m, k, n, r), dev, workspace)
@@ -236,7 +239,7 @@ def multi_lora_linear_fwd(X, W, adapters: torch.Tensor, num_adapters: int, seg_o
 
 def multi_lora_linear_bwd(dY, X, W, adapters: torch.Tensor, num_adapters: int, seg_off,
                           seg_adapter, S, keep_bits, r_max: int, *, dX=None, workspace=None,
-                          stream=None):
+                          stream=None, want_dX: bool = True):
     _need(dY, torch.bfloat16, "dY")
     _need(X, torch.bfloat16, "X")
     _need(W, torch.bfloat16, "W")
@@ -245,7 +248,10 @@ def multi_lora_linear_bwd(dY, X, W, adapters: torch.Tensor, num_adapters: int, s
     n = W.shape[1]
     nseg = seg_adapter.numel()
     dev = X.device
-    dX = torch.empty((m, k), dtype=torch.bfloat16, device=dev) if dX is None else dX
+    if want_dX and dX is None:
+        dX = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    if not want_dX:
+        dX = None
     ws = _workspace(multi_lora_bwd_workspace_size(m, k, n, r_max, num_adapters, nseg), dev,
                     workspace)
     _check(load().multi_lora_linear_bwd(_ptr(dY), _ptr(X), _ptr(W), _ptr(adapters), num_adapters,

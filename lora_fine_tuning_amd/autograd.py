@@ -31,9 +31,11 @@ class LoraLinearFunction(torch.autograd.Function):
     def backward(ctx, dY):
         X2, W, A, B, S, keep = ctx.saved_tensors
         dY2 = dY.reshape(-1, dY.shape[-1]).contiguous()
+        want_dX = ctx.needs_input_grad[0]
         dX, dA, dB = _lib.lora_linear_bwd(dY2, X2, W, A, B, S, keep if ctx.has_keep else None,
-                                          ctx.alpha, ctx.p)
-        return dX.reshape(*ctx.lead, W.shape[0]), None, dA, dB, None, None, None, None
+                                          ctx.alpha, ctx.p, want_dX=want_dX)
+        dX = dX.reshape(*ctx.lead, W.shape[0]) if want_dX else None
+        return dX, None, dA, dB, None, None, None, None
 
 
 def lora_linear(X, W, A, B, alpha: float, p: float = 0.0, seed: int = 0, offset: int = 0):
@@ -64,7 +66,7 @@ class MultiLoraLinearFunction(torch.autograd.Function):
         dBs = [torch.empty_like(b) for b in Bs]
         table = _lib.adapter_table(As, Bs, ctx.alphas, ctx.ps, dAs, dBs)
         dX = _lib.multi_lora_linear_bwd(dY.contiguous(), X, W, table, len(As), seg_off, seg_adapter, S, keep,
-                                        ctx.r_max)
+                                        ctx.r_max, want_dX=ctx.needs_input_grad[0])
         grads = []
         for da, db in zip(dAs, dBs):
             grads += [da, db]

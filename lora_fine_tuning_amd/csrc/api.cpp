@@ -389,7 +389,7 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
         REQ_PTR(dY, 16);
         REQ_PTR(X, 16);
         REQ_PTR(S, 4);
-        REQ_PTR(dX, 16);
+        REQUIRE(dX == nullptr || aligned(dX, 16), "dX must be 16-byte aligned (or NULL: no input gradient)");
         REQUIRE(keep_bits != nullptr || p == 0.0f, "keep_bits may be NULL only when p == 0");
         REQUIRE(aligned(keep_bits, 4), "keep_bits must be 4-byte aligned");
     }
@@ -413,7 +413,7 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
                          dApart, stream), "B2 launch");
     HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r, src, pl.rows2, chunks, stream),
            "dA reduction launch");
-    if (m > 0)
+    if (m > 0 && dX != nullptr)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r, p == 0.0f ? nullptr : keep_bits,
                            (int)((k + 31) / 32), src, stream), "B3 launch");
     return LORA_OK;
@@ -516,7 +516,7 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
         REQ_PTR(X, 16);
         REQ_PTR(S, 4);
         REQ_PTR(keep_bits, 4);
-        REQ_PTR(dX, 16);
+        REQUIRE(dX == nullptr || aligned(dX, 16), "dX must be 16-byte aligned (or NULL: no input gradient)");
     }
     const BwdPlan pl = plan_bwd(m, k, n, r_max, true, num_segments);
     if (workspace_bytes < pl.bytes)
@@ -549,7 +549,7 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
                "B2 launch");
     HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r_max, src, pl.rows2, chunks, stream),
            "dA reduction launch");
-    if (m > 0)
+    if (m > 0 && dX != nullptr)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r_max, keep_bits, (int)((k + 31) / 32),
                            src, stream), "B3 launch");
     return LORA_OK;

@@ -107,6 +107,7 @@ def _bwd(lib, **kw):
     (dict(keep=None), INVALID),
     (dict(dA=None), INVALID),
     (dict(wsb=0), WORKSPACE),
+    (dict(dX=None), WORKSPACE),  # dX may be NULL (no input gradient); the workspace check still runs
 ])
 def test_bwd_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status

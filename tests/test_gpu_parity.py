@@ -99,6 +99,23 @@ def test_single_unaligned_adapter(m, k, n, r):
     log(f"  {compare_single(g, o, 0.1)}")
 
 
+def test_bwd_without_input_gradient():
+    # dX = NULL skips the dX GEMM; dA and dB are those of the full call, bit for bit
+    m, k, n, r = 520, 264, 264, 24
+    X, W, A, B, dY = small_case(m, k, n, r, seed=77)
+    Xd, Wd, Ad, Bd, dYd = (t.cuda() for t in (X, W, A, B, dY))
+    Y, S, keep = lf.lora_linear_fwd(Xd, Wd, Ad, Bd, 2.0, 0.1, 3, 0)
+    _, dA, dB = lf.lora_linear_bwd(dYd, Xd, Wd, Ad, Bd, S, keep, 2.0, 0.1)
+    dX0, dA0, dB0 = lf.lora_linear_bwd(dYd, Xd, Wd, Ad, Bd, S, keep, 2.0, 0.1, want_dX=False)
+    torch.cuda.synchronize()
+    assert dX0 is None and torch.equal(dA, dA0) and torch.equal(dB, dB0)
+    # the same through autograd: an input without requires_grad gets no gradient
+    Ag, Bg = Ad.clone().requires_grad_(), Bd.clone().requires_grad_()
+    lf.lora_linear(Xd, Wd, Ag, Bg, 2.0, 0.1, 3, 0).backward(dYd)
+    torch.cuda.synchronize()
+    assert Xd.grad is None and torch.equal(Ag.grad, dA) and torch.equal(Bg.grad, dB)
+
+
 def test_single_config0_workload():
     w = workload(0)
     t = make_tensors(w)
