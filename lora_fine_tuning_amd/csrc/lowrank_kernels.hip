@@ -268,8 +268,9 @@ __global__ __launch_bounds__(256) void f1_kernel(F1Params P) {
 
 // ----- F1 streaming form (ranks <= 32 per launch slice; larger ranks in rank
 // tiles of 32).  Work-group = 16 rows of a chunk over all of k, so S leaves
-// the kernel finished (no split-k partials, no second launch).  Its 8 waves
-// take 8 consecutive ranges of k in 128-column units.  Lane l owns row
+// the kernel finished (no split-k partials, no second launch).  Its 4 waves
+// take 4 consecutive ranges of k in 128-column units (4 waves with longer
+// ranges measured no slower than 8 at rank 16 and faster at 64).  Lane l owns row
 // (l % 16) and columns 8*(l/16) .. +7 of each 32-column step: one Philox
 // block, one keep byte, one MFMA row-side fragment.  Per unit, each wave
 // copies the 128 rows of A it needs (k-major, rl bf16 per row) into a
@@ -277,11 +278,11 @@ __global__ __launch_bounds__(256) void f1_kernel(F1Params P) {
 // rank-side fragments back with transposing LDS reads; the next unit's A and
 // X loads are in flight while the current unit is hashed, masked and
 // multiplied.  The waves' partial S meet in LDS and are summed in wave order.
-constexpr int F1S_WAVES = 8;
+constexpr int F1S_WAVES = 4;
 constexpr int F1S_UNIT = 128;  // k columns per unit (4 MFMA steps)
 
 template <int MAXT>  // rank blocks of 16: rl = 16 * MAXT
-__global__ __launch_bounds__(512) void f1s_kernel(F1Params P) {
+__global__ __launch_bounds__(64 * F1S_WAVES) void f1s_kernel(F1Params P) {
     constexpr int RL = 16 * MAXT;
     constexpr int SLAB = F1S_UNIT * RL * 2;  // bytes of A per unit
     constexpr int NAV = SLAB / (16 * 64);    // 16-byte A loads per lane per unit
