@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the LoRA linear layer (forward + backward) on one MI355X.
 
-A step is one forward and one backward pass of the LoRA linear layer for both
-projection shapes of the LLaMA-8B-like workload (m = 8192 tokens,
-k = 4096 -> n = 4096 and k = 4096 -> n = 14336, r = 16, alpha = 2, p = 0.1),
-inputs already resident in HBM.  Every step runs the whole path: dropout mask
-and down-projection, base GEMM with the fused LoRA epilogue, dS/dB, dA, and the
-input-gradient GEMM with the fused masked LoRA term.
+A step is one forward and one backward pass of the mixed-adapter LoRA linear
+layer on the 70B MLP down_proj shape (m = 8192 tokens, k = 28672 -> n = 8192,
+8 adapters of ranks 8, 16, 16, 32, 32, 64, 64, 128 over 8 Dirichlet(1)
+segments, alpha 2, p 0.1), inputs already resident in HBM.  Every step runs
+the whole path: router, dropout mask and down-projection, base GEMM with the
+fused LoRA epilogue, dS/dB, dA, and the input-gradient GEMM with the fused
+masked LoRA term.  Each step is timed by its own HIP events with the caches
+flushed before it; the reported time is the median.
 
-Prints one JSON line: tokens/s (m / step time), per-step milliseconds, the
-roofline of the dominant kernel (algorithmic FLOPs per launch / its average
-launch time from HIP events on the launch stream), the same-GEMM frozen layer
-for the slowdown ratio, and the CPU oracle timed on a bounded row sample.
+Prints one JSON line: tokens/s (m / median step time), the roofline of the
+dominant kernel (algorithmic FLOPs per launch / its average launch time from
+HIP events on the launch stream), the frozen layer (this library's GEMM and
+torch.matmul) for the slowdown ratio, the LLaMA-8B projections and the small
+workload as extra keys, and the CPU oracle timed on a row sample.
 """
 from __future__ import annotations
 
@@ -32,18 +35,18 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=4096,
-                    help="rows (tokens) of the workload the CPU oracle is timed on")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=128,
+                    help="rows (tokens) of the headline workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--shapes", default="4096,14336", help="n of each projection (k = 4096)")
-    ap.add_argument("--m", type=int, default=8192)
-    ap.add_argument("--r", type=int, default=16)
+    ap.add_argument("--shapes", default="4096,14336", help="--concat: n of each projection (k = 4096)")
+    ap.add_argument("--m", type=int, default=8192, help="--concat: tokens")
+    ap.add_argument("--r", type=int, default=16, help="--concat: rank")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB (byte-counter calibration)")
-    ap.add_argument("--unfused-only", action="store_true",
-                    help="time only the eager PyTorch LoRA sequence (for its byte counters)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline workload (no other workloads; for counter runs)")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the headline step: the mixed-adapter workloads and the rank/token "
                          "sweep, fused vs frozen, one JSON line per case")
@@ -389,7 +392,7 @@ def config_report(args):
             torch.cuda.empty_cache()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama8b_m8192_hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_b3_70b_downproj_m8192_hbm_traffic.md")
 
 
 def source_digest() -> str:
@@ -421,6 +424,136 @@ def committed_traffic(kernel: str):
     return vals.get(kernel)
 
 
+class Timer:
+    """Per-step HIP-event timing on one stream.  Each trial is bracketed by its
+    own event pair; between trials (outside the events) a 512 MiB scratch
+    buffer is overwritten, which evicts the 256 MB Infinity Cache and the L2s,
+    so every trial starts from HBM (median of event-timed trials with the
+    caches flushed, the timing method of the Scaling DoRA page, "reproduction
+    and evaluation")."""
+
+    FLUSH_BYTES = 512 << 20
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+        self.scratch = torch.empty(self.FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def flush(self):
+        self.scratch.fill_(1.0)
+
+    def trials(self, fn, steps, warmup, flush=True):
+        torch = self.torch
+        for _ in range(warmup):
+            if flush:
+                self.flush()
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            if flush:
+                self.flush()
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+    def median(self, fn, steps, warmup, flush=True):
+        t = sorted(self.trials(fn, steps, warmup, flush))
+        return t[len(t) // 2]
+
+
+def mixed_case(lf, torch, w, stream):
+    """Device tensors, the adapter table and preallocated outputs of a
+    mixed-adapter workload; returns (fused step, frozen steps, per-row ranks)."""
+    from synth import make_tensors_device
+    import numpy as np
+
+    t = make_tensors_device(w, "cuda")
+    X, W, dY, As, Bs = t["X"], t["W"], t["dY"], t["A"], t["B"]
+    dAs = [torch.empty_like(a) for a in As]
+    dBs = [torch.empty_like(b) for b in Bs]
+    alphas = [a.alpha for a in w.adapters]
+    ps = [a.p for a in w.adapters]
+    table = lf.adapter_table(As, Bs, alphas, ps, dAs, dBs)
+    so = torch.as_tensor(w.seg_off).cuda()
+    sa = torch.as_tensor(w.seg_adapter).cuda()
+    m, k, n, rm, na, ns = w.m, w.k, w.n, w.r_max, len(As), len(w.seg_adapter)
+    Y = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    S = torch.empty(m, rm, dtype=torch.float32, device="cuda")
+    keep = torch.empty(m, (k + 31) // 32, dtype=torch.int32, device="cuda")
+    dX = torch.empty(m, k, dtype=torch.bfloat16, device="cuda")
+    wsf = torch.empty(max(1, lf.multi_lora_fwd_workspace_size(m, k, n, rm, na, ns)), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(max(1, lf.multi_lora_bwd_workspace_size(m, k, n, rm, na, ns)), dtype=torch.uint8,
+                      device="cuda")
+
+    def step():
+        lf.multi_lora_linear_fwd(X, W, table, na, so, sa, rm, w.seed, w.offset, Y=Y, S=S, keep_bits=keep,
+                                 workspace=wsf, stream=stream)
+        lf.multi_lora_linear_bwd(dY, X, W, table, na, so, sa, S, keep, rm, dX=dX, workspace=wsb, stream=stream)
+
+    def frozen_ours():
+        lf.lora_frozen_fwd(X, W, Y=Y, stream=stream)
+        lf.lora_frozen_bwd(dY, W, dX=dX, stream=stream)
+
+    def frozen_torch():
+        torch.matmul(X, W, out=Y)
+        torch.matmul(dY, W.t(), out=dX)
+
+    row_r = np.zeros(m, dtype=np.int64)
+    for s in range(ns):
+        row_r[w.seg_off[s]:w.seg_off[s + 1]] = w.adapters[int(w.seg_adapter[s])].r
+    return step, frozen_ours, frozen_torch, row_r, t
+
+
+def single_case(lf, torch, m, k, n, r, alpha, p, variant, stream, cid=1):
+    from synth import AdapterSpec, Workload, make_tensors_device
+    w = Workload(f"m{m} k{k} n{n}", cid, variant, m, k, n, [AdapterSpec(r, alpha, p)])
+    t = make_tensors_device(w, "cuda")
+    X, W, A, B, dY = t["X"], t["W"], t["A"][0], t["B"][0], t["dY"]
+    Y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((m, r), dtype=torch.float32, device="cuda")
+    keep = torch.empty((m, (k + 31) // 32), dtype=torch.int32, device="cuda")
+    dX = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((k, r), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((r, n), dtype=torch.bfloat16, device="cuda")
+    wsf = torch.empty(max(1, lf.lora_linear_fwd_workspace_size(m, k, n, r)), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(1, lf.lora_linear_bwd_workspace_size(m, k, n, r)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        lf.lora_linear_fwd(X, W, A, B, alpha, p, 0, 0, Y=Y, S=S, keep_bits=keep, workspace=wsf, stream=stream)
+        lf.lora_linear_bwd(dY, X, W, A, B, S, keep, alpha, p, dX=dX, dA=dA, dB=dB, workspace=wsb, stream=stream)
+
+    def frozen_ours():
+        lf.lora_frozen_fwd(X, W, Y=Y, stream=stream)
+        lf.lora_frozen_bwd(dY, W, dX=dX, stream=stream)
+
+    def frozen_torch():
+        torch.matmul(X, W, out=Y)
+        torch.matmul(dY, W.t(), out=dX)
+
+    ua = A.detach().clone().requires_grad_(True)
+    ub = B.detach().clone().requires_grad_(True)
+
+    def unfused():
+        # the eager PyTorch LoRA layer (dropout, three matmuls, scale, add;
+        # backward by autograd); its mask comes from torch's own generator
+        ua.grad = None
+        ub.grad = None
+        xg = X.detach().requires_grad_(True)
+        xd = torch.nn.functional.dropout(xg, p=p, training=True)
+        y = xg @ W + alpha * ((xd @ ua) @ ub)
+        y.backward(dY)
+
+    return step, frozen_ours, frozen_torch, unfused
+
+
+KERNEL_NAMES = ("router", "f1_mask_down", "sum_s_partials", "gemm_f2_fwd_lora", "b1_ds_db", "reduce_ds_db",
+                "b2_da", "reduce_da", "gemm_b3_bwd_dx")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -431,10 +564,11 @@ def main():
         pack_report(args)
         return
 
+    import numpy as np
     import torch
 
     import lora_fine_tuning_amd as lf
-    from synth import AdapterSpec, Workload, make_tensors_device
+    from synth import workload
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -449,204 +583,203 @@ def main():
         concat_report(args)
         return
     lf.load()
-    dev = "cuda"
-    m, k, r, alpha, p = args.m, 4096, args.r, 2.0, 0.1
-    ns = [int(v) for v in args.shapes.split(",")]
-
-    shapes = []
-    for vi, n in enumerate(ns):
-        w = Workload(f"m{m} k{k} n{n}", 1, vi, m, k, n, [AdapterSpec(r, alpha, p)])
-        t = make_tensors_device(w, dev)
-        X, W, A, B, dY = t["X"], t["W"], t["A"][0], t["B"][0], t["dY"]
-        st = {
-            "n": n, "X": X, "W": W, "A": A, "B": B, "dY": dY,
-            "Y": torch.empty((m, n), dtype=torch.bfloat16, device=dev),
-            "S": torch.empty((m, r), dtype=torch.float32, device=dev),
-            "keep": torch.empty((m, (k + 31) // 32), dtype=torch.int32, device=dev),
-            "dX": torch.empty((m, k), dtype=torch.bfloat16, device=dev),
-            "dA": torch.empty((k, r), dtype=torch.bfloat16, device=dev),
-            "dB": torch.empty((r, n), dtype=torch.bfloat16, device=dev),
-            "wsf": torch.empty(max(1, lf.lora_linear_fwd_workspace_size(m, k, n, r)),
-                               dtype=torch.uint8, device=dev),
-            "wsb": torch.empty(max(1, lf.lora_linear_bwd_workspace_size(m, k, n, r)),
-                               dtype=torch.uint8, device=dev),
-        }
-        shapes.append(st)
     stream = torch.cuda.current_stream()
+    timer = Timer(torch, stream)
+    K, Wm = args.steps, args.warmup
 
-    def step():
-        for st in shapes:
-            lf.lora_linear_fwd(st["X"], st["W"], st["A"], st["B"], alpha, p, 0, 0, Y=st["Y"],
-                               S=st["S"], keep_bits=st["keep"], workspace=st["wsf"], stream=stream)
-            lf.lora_linear_bwd(st["dY"], st["X"], st["W"], st["A"], st["B"], st["S"], st["keep"],
-                               alpha, p, dX=st["dX"], dA=st["dA"], dB=st["dB"],
-                               workspace=st["wsb"], stream=stream)
+    # ---- the headline: 70B MLP down_proj, 8 adapters of ranks 8..128
+    w = workload(4)
+    m, k, n = w.m, w.k, w.n
+    step, frozen_ours, frozen_torch, row_r, tens = mixed_case(lf, torch, w, stream)
+    print(f"[bench] {w.name}: warmup {Wm}, {K} flushed trials", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_all = timer.trials(step, K, Wm)
+    ts = sorted(t_all)
+    ms = ts[len(ts) // 2]
+    print(f"[bench] fused fwd+bwd median {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    def frozen_step(kind):
-        for st in shapes:
-            if kind == "ours":
-                lf.lora_frozen_fwd(st["X"], st["W"], Y=st["Y"], stream=stream)
-                lf.lora_frozen_bwd(st["dY"], st["W"], dX=st["dX"], stream=stream)
-            else:
-                torch.matmul(st["X"], st["W"], out=st["Y"])
-                torch.matmul(st["dY"], st["W"].t(), out=st["dX"])
+    # per-kernel HIP events on the launch stream over a second, identical timed region
+    lf.lora_profiling_enable(True, capacity=64 * K + 64)
+    lf.lora_profiling_reset()
+    timer.trials(step, K, 0)
+    kernels = {}
+    for name in KERNEL_NAMES:
+        cnt, tot = lf.lora_profiling_query(name)
+        kernels[name] = {"launches": cnt, "total_ms": round(tot, 4),
+                         "avg_us": round(tot / cnt * 1e3, 2) if cnt else None}
+    lf.lora_profiling_enable(False)
 
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+    ms_fo = timer.median(frozen_ours, K, Wm)
+    ms_ft = timer.median(frozen_torch, K, Wm)
+    ms_b2b = sum(timer.trials(step, K, 0, flush=False)) / K
+    print(f"[bench] frozen ours {ms_fo:.3f} ms, torch {ms_ft:.3f} ms", file=sys.stderr, flush=True)
 
-    # The unfused comparator: the eager PyTorch LoRA layer (dropout, three
-    # matmuls, scale, add; backward by autograd), bf16, same shapes.  Its mask
-    # comes from torch's own generator; only its time and bytes are used.
-    unfused = []
-    for st in shapes:
-        ua = st["A"].detach().clone().requires_grad_(True)
-        ub = st["B"].detach().clone().requires_grad_(True)
-        unfused.append((st, ua, ub))
+    # algorithmic FLOPs per launch: F2 2mkn + 2n sum_i r_i; B3 2mnk + 2k sum_i r_i
+    sr = float(row_r.sum())
+    flops = {"gemm_f2_fwd_lora": 2.0 * m * k * n + 2.0 * n * sr,
+             "gemm_b3_bwd_dx": 2.0 * m * n * k + 2.0 * k * sr}
+    dom = max(flops, key=lambda nm: kernels[nm]["total_ms"])
+    achieved = flops[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+    traffic = committed_traffic(dom)
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else round(traffic)}
+    # HBM-bound kernels: algorithmic bytes per launch (per token 2k + k/8 + 4 r_i for
+    # F1 and B2, 2n + 8 r_i for B1; plus each adapter's A, B, dA, dB once) / event time
+    kw = (k + 31) // 32
+    ra = sum(a.r for a in w.adapters)
+    hbm_bytes = {"f1_mask_down": 2.0 * m * k + 4.0 * m * kw + 4.0 * sr + 2.0 * k * ra,
+                 "b1_ds_db": 2.0 * m * n + 8.0 * sr + 4.0 * n * ra,
+                 "b2_da": 2.0 * m * k + 4.0 * m * kw + 4.0 * sr + 2.0 * k * ra}
+    hbm = {}
+    for nm, b in hbm_bytes.items():
+        if kernels[nm]["avg_us"]:
+            gbs = b / (kernels[nm]["avg_us"] * 1e-6) / 1e9
+            hbm[nm] = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
-    def unfused_step():
-        for st, ua, ub in unfused:
-            ua.grad = None
-            ub.grad = None
-            xg = st["X"].detach().requires_grad_(True)
-            xd = torch.nn.functional.dropout(xg, p=p, training=True)
-            y = xg @ st["W"] + alpha * ((xd @ ua) @ ub)
-            y.backward(st["dY"])
-
-    def copy_calibration():
+    if args.copy_calib_mib:
         # ends a counter run with device copies of known size (byte-counter scale)
-        if not args.copy_calib_mib:
-            return
         nel = args.copy_calib_mib * (1 << 20) // 4
-        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        src = torch.ones(nel, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + written per copy, 3 copies",
               file=sys.stderr, flush=True)
+        del src, dst
 
-    if args.unfused_only:
-        ms_u = timed(unfused_step, args.steps, args.warmup)
-        copy_calibration()
-        print(json.dumps({"unfused_torch_ms": round(ms_u, 4), "steps": args.steps, "warmup": args.warmup}))
-        return
+    # ---- the LLaMA-8B projections (r 16), each alone and both as one step
+    extra = {}
+    if not args.headline_only:
+        c1 = {}
+        for vi, nn in enumerate((4096, 14336)):
+            s1, fo1, ft1, un1 = single_case(lf, torch, 8192, 4096, nn, 16, 2.0, 0.1, vi, stream)
+            f1 = timer.median(s1, K, Wm)
+            o1 = timer.median(fo1, K, Wm)
+            t1 = timer.median(ft1, K, Wm)
+            u1 = timer.median(un1, max(K // 4, 5), 2)
+            c1[f"k4096_n{nn}"] = {"fused_ms": round(f1, 4), "frozen_ours_ms": round(o1, 4),
+                                  "frozen_torch_ms": round(t1, 4), "fused_over_frozen": round(f1 / min(o1, t1), 4),
+                                  "unfused_torch_ms": round(u1, 4), "tokens_per_s": round(8192 / (f1 * 1e-3), 1)}
+            del s1, fo1, ft1, un1
+            torch.cuda.empty_cache()
+        both = sum(v["fused_ms"] for v in c1.values())
+        both_frozen = sum(min(v["frozen_ours_ms"], v["frozen_torch_ms"]) for v in c1.values())
+        c1["both_shapes"] = {"fused_ms": round(both, 4), "fused_over_frozen": round(both / both_frozen, 4),
+                             "tokens_per_s": round(8192 / (both * 1e-3), 1)}
+        extra["llama8b_projections_m8192_r16"] = c1
+        # ---- the small workload (m 512, k = n 1024, r 16): launch- and cache-bound
+        s0, fo0, ft0, _ = single_case(lf, torch, 512, 1024, 1024, 16, 2.0, 0.1, 0, stream, cid=0)
+        f0, o0, t0 = timer.median(s0, K, Wm), timer.median(fo0, K, Wm), timer.median(ft0, K, Wm)
+        extra["small_m512_k1024_n1024_r16"] = {"fused_ms": round(f0, 4), "tokens_per_s": round(512 / (f0 * 1e-3), 1),
+                                               "frozen_ours_ms": round(o0, 4), "frozen_torch_ms": round(t0, 4),
+                                               "fused_over_frozen": round(f0 / min(o0, t0), 4)}
+    print(f"[bench] other workloads done", file=sys.stderr, flush=True)
 
-    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
-    ms = timed(step, args.steps, args.warmup)
-    print(f"[bench] fused fwd+bwd {ms:.3f} ms/step", file=sys.stderr, flush=True)
-
-    # per-kernel HIP events on the launch stream, over a second timed region
-    lf.lora_profiling_enable(True, capacity=64 * args.steps + 64)
-    lf.lora_profiling_reset()
-    ms_prof = timed(step, args.steps, 0)
-    kernels = {}
-    for name in ("f1_mask_down", "sum_s_partials", "gemm_f2_fwd_lora", "b1_ds_db", "sum_ds_partials",
-                 "reduce_db", "reduce_ds_db", "b2_da", "reduce_da", "gemm_b3_bwd_dx"):
-        cnt, tot = lf.lora_profiling_query(name)
-        kernels[name] = {"launches": cnt, "total_ms": tot,
-                         "avg_us": (tot / cnt * 1e3) if cnt else None}
-    lf.lora_profiling_enable(False)
-
-    ms_frozen_ours = timed(lambda: frozen_step("ours"), args.steps, args.warmup)
-    ms_frozen_torch = timed(lambda: frozen_step("torch"), args.steps, args.warmup)
-    print(f"[bench] frozen ours {ms_frozen_ours:.3f} ms, torch {ms_frozen_torch:.3f} ms",
-          file=sys.stderr, flush=True)
-    ms_unfused = timed(unfused_step, args.steps, args.warmup)
-    print(f"[bench] unfused torch LoRA {ms_unfused:.3f} ms", file=sys.stderr, flush=True)
-
-    # algorithmic FLOPs per launch (both shapes): F2 2mkn + 2mrn; B3 2mnk + 2mrk
-    flops = {
-        "gemm_f2_fwd_lora": sum(2.0 * m * k * st["n"] + 2.0 * m * r * st["n"] for st in shapes),
-        "gemm_b3_bwd_dx": sum(2.0 * m * st["n"] * k + 2.0 * m * r * k for st in shapes),
-    }
-    dom = max(flops, key=lambda nm: kernels[nm]["total_ms"])
-    kd = kernels[dom]
-    achieved = flops[dom] / (kd["total_ms"] / args.steps * 1e-3) / 1e12  # TFLOP/s
-    traffic = committed_traffic(dom)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if traffic is None else round(traffic)}
-    # HBM-bound kernels: algorithmic bytes per launch (both shapes) / event time
-    kw = (k + 31) // 32
-    hbm_bytes = {
-        "f1_mask_down": sum(m * k * 2 + m * kw * 4 + m * r * 4 + k * r * 2 for _ in shapes),
-        "b1_ds_db": sum(m * st["n"] * 2 + 2 * m * r * 4 + 2 * r * st["n"] * 2 for st in shapes),
-        "b2_da": sum(m * k * 2 + m * kw * 4 + m * r * 4 + k * r * 2 for _ in shapes),
-    }
-    hbm = {}
-    for nm, b in hbm_bytes.items():
-        t = kernels[nm]["total_ms"] / args.steps * 1e-3
-        hbm[nm] = {"GB/s": round(b / t / 1e9, 1), "frac": round(b / t / 1e9 / PEAK_HBM_GBS, 4)}
-
-    tokens_per_s = m / (ms * 1e-3)
     result = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": round(m / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": Wm,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"LoRA linear fwd+bwd, m={m} tokens through k={k}->n="
-                               f"{'+'.join(str(n) for n in ns)} (r={r}, alpha={alpha}, p={p})",
-                   "m": m, "k": k, "n": ns, "r": r, "alpha": alpha, "p": p},
+        "config": {"workload": f"70B MLP down_proj LoRA linear fwd+bwd: m={m} tokens, k={k} -> n={n}, "
+                               f"8 adapters r={[a.r for a in w.adapters]} in 8 Dirichlet(1) segments "
+                               f"{np.diff(w.seg_off).tolist()}, alpha=2, p=0.1",
+                   "m": m, "k": k, "n": n, "ranks": [a.r for a in w.adapters],
+                   "segments": w.seg_off.tolist(), "timing": "median of per-step HIP-event trials, "
+                   "512 MiB cache flush between trials"},
+        "ms_per_step_mean": round(sum(t_all) / K, 4),
+        "ms_per_step_min": round(ts[0], 4),
+        "ms_per_step_back_to_back": round(ms_b2b, 4),
         "roofline": roofline,
-        "frozen": {"ours_ms": round(ms_frozen_ours, 4), "torch_matmul_ms": round(ms_frozen_torch, 4),
-                   "fused_over_frozen": round(ms / min(ms_frozen_ours, ms_frozen_torch), 4)},
-        "unfused_torch": {"ms": round(ms_unfused, 4), "fused_speedup": round(ms_unfused / ms, 4)},
-        "kernels": {nm: {kk: (round(v, 3) if isinstance(v, float) else v) for kk, v in d.items()}
-                    for nm, d in kernels.items()},
-        "ms_per_step_with_kernel_events": round(ms_prof, 4),
+        "frozen": {"ours_ms": round(ms_fo, 4), "torch_matmul_ms": round(ms_ft, 4),
+                   "fused_over_frozen": round(ms / min(ms_fo, ms_ft), 4)},
+        "kernels": kernels,
         "hbm_kernels": hbm,
+        "other_workloads": extra,
         "gemm_source_digest": source_digest(),
     }
-    copy_calibration()
+    del step, frozen_ours, frozen_torch
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(m, k, ns, r, alpha, p, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(w, tens, args.cpu_rows)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(m, k, ns, r, alpha, p, rows):
-    """The oracle (fp64 C, OpenMP) timed on `rows` tokens of the same workload:
-    forward and backward of both projections for those rows; the per-adapter
-    reductions run over the sampled rows only."""
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, tens, rows):
+    """The oracle (double-precision C, OpenMP over rows, built as it stands)
+    timed on a row sample of the same workload: the first rows/8 rows of each
+    of the 8 segments, forward and backward of their adapters (mask, S, Y; dS,
+    dB, dA, dX), on up to one host thread per sampled row of a segment, then
+    on one thread for a smaller sample."""
+    import ctypes
+
     import numpy as np
     import torch
 
     import oracle
-    from synth import AdapterSpec, Workload, make_tensors
 
     oracle.build(force=False)
-    total = 0.0
-    for vi, n in enumerate(ns):
-        w = Workload(f"m{rows} k{k} n{n}", 1, vi, rows, k, n, [AdapterSpec(r, alpha, p)])
-        t = make_tensors(w)
-        X, W, A, B, dY = (np.ascontiguousarray(v.to(torch.float64).numpy())
-                          for v in (t["X"], t["W"], t["A"][0], t["B"][0], t["dY"]))
+    per = max(1, rows // len(w.seg_adapter))
+    idx, so, sa = [], [0], []
+    for s in range(len(w.seg_adapter)):
+        lo, hi = int(w.seg_off[s]), int(w.seg_off[s + 1])
+        take = list(range(lo, min(hi, lo + per)))
+        idx += take
+        so.append(so[-1] + len(take))
+        sa.append(int(w.seg_adapter[s]))
+    ii = torch.as_tensor(idx, device="cuda")
+    to64 = lambda t: np.ascontiguousarray(t.to("cpu", torch.float64).numpy())  # noqa: E731
+    X, dY, W = to64(tens["X"][ii]), to64(tens["dY"][ii]), to64(tens["W"])
+    ads = [{"A": to64(a), "B": to64(b), "alpha": ad.alpha, "p": np.float32(ad.p)}
+           for a, b, ad in zip(tens["A"], tens["B"], w.adapters)]
+
+    def run(nrows_per_seg):
+        so2, sa2, sel = [0], [], []
+        for s in range(len(sa)):
+            take = list(range(so[s], min(so[s + 1], so[s] + nrows_per_seg)))
+            sel += take
+            so2.append(so2[-1] + len(take))
+            sa2.append(sa[s])
+        Xs, dYs = np.ascontiguousarray(X[sel]), np.ascontiguousarray(dY[sel])
         t0 = time.perf_counter()
-        oracle.lora_fwd(X, W, A, B, alpha, np.float32(p), 0, 0)
-        oracle.lora_bwd(dY, X, W, A, B, alpha, np.float32(p), 0, 0)
-        total += time.perf_counter() - t0
-    return {"value": round(rows / total, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{rows} of {m} tokens, fwd+bwd of both projections (fp64 C oracle; "
-                      f"{total:.1f} s)"}
+        oracle.multi_lora_fwd(Xs, W, ads, so2, sa2, w.r_max, 0, 0)
+        oracle.multi_lora_bwd(dYs, Xs, W, ads, so2, sa2, w.r_max, 0, 0)
+        return len(sel), time.perf_counter() - t0
+
+    n_all, t_all = run(per)
+    threads = oracle.num_threads()
+    one = None
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        n1, t1 = run(max(1, per // 16))
+        gomp.omp_set_num_threads(threads)
+        one = {"value": round(n1 / t1, 3), "rows": n1, "seconds": round(t1, 2)}
+    except OSError:
+        pass
+    # the oracle parallelises over the rows of one segment at a time
+    return {"value": round(n_all / t_all, 3), "unit": "tokens/s", "cores": min(threads, per), "kind": "oracle",
+            "sample": f"{n_all} of {w.m} tokens ({per} from each of the 8 segments), forward and backward, "
+                      f"double-precision C oracle, {t_all:.1f} s",
+            "cpu_model": cpu_model(), "single_thread": one}
 
 
 if __name__ == "__main__":

@@ -56,8 +56,8 @@
  * alignment of S and keep_bits; 0 <= m < 2^31; 0 < k, n < 2^31 with
  * k % 8 == 0 and n % 8 == 0; 1 <= r <= 256; 0 <= p < 1; offset % 8 == 0;
  * workspace large enough (LORA_ERR_INVALID_ARG / LORA_ERR_WORKSPACE).  The
- * forward calls return LORA_ERR_UNSUPPORTED when B (r or r_max by n bf16)
- * exceeds 2 GiB.  When m == 0 the m-sized buffers (X, Y, S,
+ * layer calls (forward and backward) return LORA_ERR_UNSUPPORTED when B
+ * (r or r_max by n bf16) or A (k by r or r_max bf16) exceeds 2 GiB.  When m == 0 the m-sized buffers (X, Y, S,
  * keep_bits, dY, dX) may be NULL.  The multi-adapter tables live in device memory and
  * are never read on the host: an invalid table (segments not ordered, not
  * covering [0, m), adapter index out of range, adapter rank > r_max) gives

@@ -13,6 +13,7 @@ import ctypes
 import os
 from typing import List, Optional, Sequence, Tuple
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -192,25 +193,105 @@ def lora_linear_bwd(dY, X, W, A, B, S, keep_bits, alpha: float, p: float, *, dX=
     return dX, dA, dB
 
 
-def adapter_table(As: Sequence[torch.Tensor], Bs: Sequence[torch.Tensor], alphas, ps,
-                  dAs: Optional[Sequence[torch.Tensor]] = None,
-                  dBs: Optional[Sequence[torch.Tensor]] = None, device=None) -> torch.Tensor:
-    """Pack lora_adapter records into a device uint8 tensor (the table the
-    multi-adapter calls read on the device)."""
-    n = len(As)
-    recs = (LoraAdapter * n)()
-    for i in range(n):
+def _check_adapters(As, Bs, alphas, ps, dAs=None, dBs=None, k=None, n=None):
+    """Host checks of a mixed-adapter set that the library cannot make (its
+    table lives on the device): bf16, contiguous device tensors; A_i k x r_i and
+    B_i r_i x n with 1 <= r_i <= 256 and the same k and n for every adapter;
+    finite alpha; 0 <= p < 1 (as the float32 the table stores); gradient
+    buffers shaped like their parameters.  Returns (k, n, ranks)."""
+    na = len(As)
+    if na < 1 or len(Bs) != na or len(alphas) != na or len(ps) != na:
+        raise ValueError("As, Bs, alphas and ps must have the same, non-zero length")
+    for grads, nm in ((dAs, "dAs"), (dBs, "dBs")):
+        if grads is not None and len(grads) != na:
+            raise ValueError(f"{nm} must have one tensor per adapter")
+    k = As[0].shape[0] if k is None else int(k)
+    n = Bs[0].shape[1] if n is None else int(n)
+    dev = As[0].device
+    ranks = []
+    for i in range(na):
+        A, B = As[i], Bs[i]
+        for t, nm in ((A, f"A[{i}]"), (B, f"B[{i}]")):
+            if t.dtype != torch.bfloat16:
+                raise TypeError(f"{nm} must be torch.bfloat16, got {t.dtype}")
+            if not t.is_contiguous():
+                raise ValueError(f"{nm} must be contiguous")
+        if A.dim() != 2 or B.dim() != 2:
+            raise ValueError(f"adapter {i}: A and B must be 2-D")
+        r = A.shape[1]
+        if A.shape[0] != k or B.shape != (r, n):
+            raise ValueError(f"adapter {i}: A {tuple(A.shape)} and B {tuple(B.shape)} do not fit "
+                             f"k = {k}, n = {n} (A must be k x r, B r x n)")
+        if not 1 <= r <= 256:
+            raise ValueError(f"adapter {i}: rank {r} outside [1, 256]")
+        with np.errstate(over="ignore"):
+            a32, p32 = np.float32(alphas[i]), np.float32(ps[i])
+        if not np.isfinite(a32):
+            raise ValueError(f"adapter {i}: alpha {alphas[i]} is not finite")
+        if not (p32 >= 0.0 and p32 < 1.0):
+            raise ValueError(f"adapter {i}: dropout p = {ps[i]} must be in [0, 1)")
+        for grads, ref, nm in ((dAs, A, "dA"), (dBs, B, "dB")):
+            if grads is None:
+                continue
+            g = grads[i]
+            if g.dtype != torch.bfloat16 or not g.is_contiguous() or g.shape != ref.shape:
+                raise ValueError(f"adapter {i}: {nm} must be a contiguous bf16 {tuple(ref.shape)} tensor")
+        ranks.append(r)
+    # device last, so that host tests can reach every other check with CPU tensors
+    for i in range(na):
+        ts = [As[i], Bs[i]] + [g[i] for g in (dAs, dBs) if g is not None]
+        if any(t.device.type != "cuda" or t.device != dev for t in ts):
+            raise ValueError(f"adapter {i}: every tensor must be on one GPU ({dev})")
+    return k, n, ranks
+
+
+def _pack_table(As, Bs, alphas, ps, dA_ptrs, dB_ptrs) -> bytes:
+    na = len(As)
+    recs = (LoraAdapter * na)()
+    for i in range(na):
         recs[i].A = As[i].data_ptr()
         recs[i].B = Bs[i].data_ptr()
-        recs[i].dA = dAs[i].data_ptr() if dAs is not None else 0
-        recs[i].dB = dBs[i].data_ptr() if dBs is not None else 0
+        recs[i].dA = dA_ptrs[i]
+        recs[i].dB = dB_ptrs[i]
         recs[i].r = As[i].shape[1]
         recs[i].alpha = float(alphas[i])
         recs[i].p = float(ps[i])
         recs[i].reserved = 0
-    raw = bytes(recs)
+    return bytes(recs)
+
+
+def adapter_table(As: Sequence[torch.Tensor], Bs: Sequence[torch.Tensor], alphas, ps,
+                  dAs: Optional[Sequence[torch.Tensor]] = None,
+                  dBs: Optional[Sequence[torch.Tensor]] = None, device=None, *,
+                  k: Optional[int] = None, n: Optional[int] = None) -> torch.Tensor:
+    """Pack lora_adapter records into a device uint8 tensor (the table the
+    multi-adapter calls read on the device), after the host checks of
+    _check_adapters.  The table remembers k, n and the ranks, which the
+    multi-adapter wrappers check against X, W and r_max."""
+    k, n, ranks = _check_adapters(As, Bs, alphas, ps, dAs, dBs, k, n)
+    raw = _pack_table(As, Bs, alphas, ps,
+                      [d.data_ptr() for d in dAs] if dAs is not None else [0] * len(As),
+                      [d.data_ptr() for d in dBs] if dBs is not None else [0] * len(As))
     host = torch.frombuffer(bytearray(raw), dtype=torch.uint8)
-    return host.to(device if device is not None else As[0].device)
+    table = host.to(device if device is not None else As[0].device)
+    table._lora_meta = (k, n, tuple(ranks))
+    return table
+
+
+def _check_table(adapters: torch.Tensor, num_adapters: int, k: int, n: int, r_max: int) -> None:
+    if adapters.dtype != torch.uint8 or adapters.device.type != "cuda" or not adapters.is_contiguous():
+        raise ValueError("adapters must be a contiguous device uint8 table (see adapter_table)")
+    if adapters.numel() < num_adapters * ctypes.sizeof(LoraAdapter):
+        raise ValueError(f"adapter table holds fewer than {num_adapters} records")
+    meta = getattr(adapters, "_lora_meta", None)
+    if meta is not None:
+        tk, tn, ranks = meta
+        if (tk, tn) != (k, n):
+            raise ValueError(f"adapter table was built for k = {tk}, n = {tn}; X and W give k = {k}, n = {n}")
+        if len(ranks) != num_adapters:
+            raise ValueError(f"adapter table has {len(ranks)} adapters, num_adapters = {num_adapters}")
+        if max(ranks) > r_max:
+            raise ValueError(f"r_max = {r_max} is below the largest adapter rank {max(ranks)}")
 
 
 def multi_lora_linear_fwd(X, W, adapters: torch.Tensor, num_adapters: int, seg_off, seg_adapter,
@@ -222,6 +303,7 @@ def multi_lora_linear_fwd(X, W, adapters: torch.Tensor, num_adapters: int, seg_o
     _need(seg_adapter, torch.int32, "seg_adapter")
     m, k = X.shape
     n = W.shape[1]
+    _check_table(adapters, num_adapters, k, n, r_max)
     nseg = seg_adapter.numel()
     dev = X.device
     Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if Y is None else Y
@@ -246,6 +328,7 @@ def multi_lora_linear_bwd(dY, X, W, adapters: torch.Tensor, num_adapters: int, s
     _need(S, torch.float32, "S")
     m, k = X.shape
     n = W.shape[1]
+    _check_table(adapters, num_adapters, k, n, r_max)
     nseg = seg_adapter.numel()
     dev = X.device
     if want_dX and dX is None:

@@ -9,6 +9,8 @@ this file only reshapes tensors and keeps the dropout counter.
 """
 from __future__ import annotations
 
+from collections import OrderedDict
+
 import torch
 
 from . import _lib
@@ -42,6 +44,63 @@ def lora_linear(X, W, A, B, alpha: float, p: float = 0.0, seed: int = 0, offset:
     return LoraLinearFunction.apply(X, W, A, B, alpha, p, seed, offset)
 
 
+class _AdapterSet:
+    """The device adapter table of one set of adapter tensors, built once and
+    reused by every call with the same tensors, scales and dropout ratios.
+
+    The backward writes all gradients of the set into one flat bf16 buffer per
+    call; the table's dA / dB pointer slots are set to that buffer's pieces
+    by one device-side add (constant piece offsets plus the buffer's base
+    address, a kernel argument), so no call after the first copies from host
+    memory or waits for the device, and the calls can be captured in a graph.
+    Calls that share a set must run in stream order (one stream)."""
+
+    def __init__(self, As, Bs, alphas, ps):
+        self.table = _lib.adapter_table(As, Bs, alphas, ps)
+        self.k, self.n, ranks = self.table._lora_meta
+        self.num = len(As)
+        self.r_max = max(ranks)
+        self.shapes = [(tuple(a.shape), tuple(b.shape)) for a, b in zip(As, Bs)]
+        offs, pos = [], 0
+        for sa, sb in self.shapes:
+            na, nb = sa[0] * sa[1], sb[0] * sb[1]
+            offs.append((pos, pos + (na + 7) // 8 * 8))  # pieces start on 16-byte boundaries
+            pos += (na + 7) // 8 * 8 + (nb + 7) // 8 * 8
+        self.total = pos
+        self.elem_off = offs
+        self.byte_off = torch.tensor([[2 * a, 2 * b] for a, b in offs], dtype=torch.int64,
+                                     device=self.table.device)
+
+    def gradient_buffers(self):
+        flat = torch.empty(max(self.total, 1), dtype=torch.bfloat16, device=self.table.device)
+        slots = self.table.view(torch.int64).view(self.num, 6)[:, 2:4]  # dA, dB of each record
+        torch.add(self.byte_off, flat.data_ptr(), out=slots)
+        dAs, dBs = [], []
+        for (oa, ob), (sa, sb) in zip(self.elem_off, self.shapes):
+            dAs.append(flat[oa:oa + sa[0] * sa[1]].view(sa))
+            dBs.append(flat[ob:ob + sb[0] * sb[1]].view(sb))
+        return dAs, dBs
+
+
+_SETS: "OrderedDict[tuple, _AdapterSet]" = OrderedDict()
+_SETS_MAX = 256
+
+
+def _adapter_set(As, Bs, alphas, ps) -> _AdapterSet:
+    # layout is part of the key: a tensor that would fail the checks never hits the cache
+    key = (As[0].device,) + tuple((a.data_ptr(), tuple(a.shape), a.dtype, a.is_contiguous(), a.device,
+                                   b.data_ptr(), tuple(b.shape), b.dtype, b.is_contiguous(), b.device,
+                                   float(al), float(p)) for a, b, al, p in zip(As, Bs, alphas, ps))
+    st = _SETS.get(key)
+    if st is None:
+        st = _SETS[key] = _AdapterSet(As, Bs, alphas, ps)
+        while len(_SETS) > _SETS_MAX:
+            _SETS.popitem(last=False)
+    else:
+        _SETS.move_to_end(key)
+    return st
+
+
 class MultiLoraLinearFunction(torch.autograd.Function):
     """Mixed-adapter batch: rows [seg_off[s], seg_off[s+1]) of X (m x k) use
     adapter seg_adapter[s]; the adapters come as A0, B0, A1, B1, ... and each
@@ -51,22 +110,20 @@ class MultiLoraLinearFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, X, W, seg_off, seg_adapter, alphas, ps, seed: int, offset: int, *AB):
         As, Bs = AB[0::2], AB[1::2]
-        r_max = max(a.shape[1] for a in As)
-        table = _lib.adapter_table(As, Bs, alphas, ps)
-        Y, S, keep = _lib.multi_lora_linear_fwd(X, W, table, len(As), seg_off, seg_adapter, r_max, seed, offset)
-        ctx.save_for_backward(X, W, seg_off, seg_adapter, S, keep, *AB)
-        ctx.alphas, ctx.ps, ctx.r_max = list(alphas), list(ps), r_max
+        st = _adapter_set(As, Bs, alphas, ps)
+        Y, S, keep = _lib.multi_lora_linear_fwd(X, W, st.table, st.num, seg_off, seg_adapter, st.r_max, seed,
+                                                offset)
+        ctx.save_for_backward(X, W, seg_off, seg_adapter, S, keep)
+        ctx.adapter_set = st
         return Y
 
     @staticmethod
     def backward(ctx, dY):
-        X, W, seg_off, seg_adapter, S, keep, *AB = ctx.saved_tensors
-        As, Bs = AB[0::2], AB[1::2]
-        dAs = [torch.empty_like(a) for a in As]
-        dBs = [torch.empty_like(b) for b in Bs]
-        table = _lib.adapter_table(As, Bs, ctx.alphas, ctx.ps, dAs, dBs)
-        dX = _lib.multi_lora_linear_bwd(dY.contiguous(), X, W, table, len(As), seg_off, seg_adapter, S, keep,
-                                        ctx.r_max, want_dX=ctx.needs_input_grad[0])
+        X, W, seg_off, seg_adapter, S, keep = ctx.saved_tensors
+        st = ctx.adapter_set
+        dAs, dBs = st.gradient_buffers()
+        dX = _lib.multi_lora_linear_bwd(dY.contiguous(), X, W, st.table, st.num, seg_off, seg_adapter, S, keep,
+                                        st.r_max, want_dX=ctx.needs_input_grad[0])
         grads = []
         for da, db in zip(dAs, dBs):
             grads += [da, db]

@@ -174,11 +174,13 @@ static lora_status check_rank(int32_t r) {
     return LORA_OK;
 }
 
-// The fused epilogue of the forward GEMM addresses B (r x n bf16) with 32-bit
-// byte offsets.
-static lora_status check_b_size(int32_t r, int64_t n) {
+// The GEMM epilogues and the dS/dB kernel address B (r x n bf16) and A
+// (k x r bf16) with 32-bit byte offsets.
+static lora_status check_b_size(int32_t r, int64_t k, int64_t n) {
     if ((int64_t)r * n * 2 >= (1LL << 31))
         return fail(LORA_ERR_UNSUPPORTED, "B of %d x %lld bf16 exceeds 2 GiB", r, (long long)n);
+    if ((int64_t)r * k * 2 >= (1LL << 31))
+        return fail(LORA_ERR_UNSUPPORTED, "A of %lld x %d bf16 exceeds 2 GiB", (long long)k, r);
     return LORA_OK;
 }
 
@@ -340,7 +342,7 @@ extern "C" lora_status lora_linear_fwd(const void *X, const void *W, const void 
     CHECK(check_shape(m, k, n));
     CHECK(check_rank(r));
     CHECK(check_p(p));
-    CHECK(check_b_size(r, n));
+    CHECK(check_b_size(r, k, n));
     REQUIRE(offset % 8 == 0, "offset = %llu must be a multiple of 8", (unsigned long long)offset);
     REQ_PTR(W, 16);
     REQ_PTR(A, 2);
@@ -380,6 +382,7 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
     CHECK(check_shape(m, k, n));
     CHECK(check_rank(r));
     CHECK(check_p(p));
+    CHECK(check_b_size(r, k, n));
     REQ_PTR(W, 16);
     REQ_PTR(A, 2);
     REQ_PTR(B, 2);
@@ -469,7 +472,7 @@ extern "C" lora_status multi_lora_linear_fwd(const void *X, const void *W, const
                                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
     CHECK(check_shape(m, k, n));
     CHECK(check_multi(adapters, num_adapters, seg_off, seg_adapter, num_segments, r_max));
-    CHECK(check_b_size(r_max, n));
+    CHECK(check_b_size(r_max, k, n));
     REQUIRE(offset % 8 == 0, "offset = %llu must be a multiple of 8", (unsigned long long)offset);
     REQ_PTR(W, 16);
     if (m == 0) return LORA_OK;
@@ -510,6 +513,7 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
                                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
     CHECK(check_shape(m, k, n));
     CHECK(check_multi(adapters, num_adapters, seg_off, seg_adapter, num_segments, r_max));
+    CHECK(check_b_size(r_max, k, n));
     REQ_PTR(W, 16);
     if (m > 0) {
         REQ_PTR(dY, 16);

@@ -451,14 +451,17 @@ __global__ __launch_bounds__(64 * F1S_WAVES) void f1s_kernel(F1Params P) {
     for (int i = tid; i < 16 * RL; i += 64 * F1S_WAVES) {
         const int rr = i / RL, cl = i % RL;
         const int orow = row_lo + rr;
-        if (orow >= row_hi || cl >= ncol) continue;
+        if (orow >= row_hi) continue;
         float v = 0.f;
         if (r0 + cl < r) {
 #pragma unroll
             for (int w = 0; w < F1S_WAVES; ++w) v += red[(w * 16 + rr) * RL + cl];
             v *= s;
         }
-        P.out[(size_t)orow * P.RS + r0 + cl] = v;
+        if (cl < ncol) P.out[(size_t)orow * P.RS + r0 + cl] = v;
+        // hi / lo columns run to s2_rp, past the S columns (ncol) of the last
+        // rank tile: those past r are written as zeros too, since the forward
+        // GEMM reads every one of them
         if (P.s2 != nullptr && r0 + cl < P.s2_rp) {
             // the forward epilogue's split of alpha*S, same arithmetic
             uint32_t hi, lo;

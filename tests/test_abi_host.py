@@ -108,6 +108,8 @@ def _bwd(lib, **kw):
     (dict(dA=None), INVALID),
     (dict(wsb=0), WORKSPACE),
     (dict(dX=None), WORKSPACE),  # dX may be NULL (no input gradient); the workspace check still runs
+    (dict(r=256, n=1 << 22), UNSUPPORTED),  # B of 256 x 2^22 bf16 = 2 GiB (read by the dS/dB pass)
+    (dict(r=256, k=1 << 22), UNSUPPORTED),  # A of 2^22 x 256 bf16 = 2 GiB (read by the dX epilogue)
 ])
 def test_bwd_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status
@@ -132,6 +134,24 @@ def test_multi_rejects(lib):
              None) == INVALID  # r_max 0
     assert b(FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1, FAKE, FAKE, 64, 64, 64, 16, FAKE, FAKE, 0,
              None) == WORKSPACE
+    # r_max x n of B beyond 2 GiB: forward and backward alike
+    assert f(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1, 64, 64, 1 << 22, 256, 0, 0, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+             None) == UNSUPPORTED
+    assert b(FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1, FAKE, FAKE, 64, 64, 1 << 22, 256, FAKE, FAKE, 1 << 40,
+             None) == UNSUPPORTED
+
+
+def test_launch_without_device_returns_hip_error(lib):
+    # valid arguments on a host with no GPU: the launch itself fails, and the
+    # status is LORA_ERR_HIP with HIP's own message (nothing is dereferenced)
+    hip = ctypes.CDLL("libamdhip64.so")
+    count = ctypes.c_int(-1)
+    if hip.hipGetDeviceCount(ctypes.byref(count)) == 0 and count.value > 0:
+        pytest.skip("a device is present")
+    assert lib.lora_frozen_fwd(FAKE, FAKE, 64, 64, 64, FAKE, None) == HIPERR
+    assert b"device" in lib.lora_last_error_message()
+    assert lib.lora_dropout_mask(0, 0, 4, 64, 0.1, FAKE, None) == HIPERR
+    assert _fwd(lib, ws=FAKE, wsb=1 << 30) == HIPERR
 
 
 def test_mask_and_frozen_reject(lib):
@@ -196,3 +216,43 @@ def test_workspace_sizes():
 def test_adapter_record_layout():
     assert ctypes.sizeof(_lib.LoraAdapter) == 48
     assert _lib.LoraAdapter.r.offset == 32 and _lib.LoraAdapter.p.offset == 40
+
+
+def test_adapter_table_host_checks():
+    # every check but the device's runs on CPU tensors; a valid set of CPU
+    # tensors then fails only on the device
+    import torch
+    k, n = 64, 32
+    bf = torch.bfloat16
+
+    def mk(r, kk=k, nn=n):
+        return torch.zeros(kk, r, dtype=bf), torch.zeros(r, nn, dtype=bf)
+
+    A1, B1 = mk(8)
+    A2, B2 = mk(16)
+    good = dict(As=[A1, A2], Bs=[B1, B2], alphas=[1.0, 2.0], ps=[0.1, 0.0])
+
+    def expect(exc, text, **kw):
+        a = dict(good)
+        a.update(kw)
+        with pytest.raises(exc) as e:
+            _lib.adapter_table(a["As"], a["Bs"], a["alphas"], a["ps"], a.get("dAs"), a.get("dBs"))
+        assert text in str(e.value), str(e.value)
+
+    expect(TypeError, "bfloat16", As=[A1.float(), A2])
+    expect(ValueError, "contiguous", Bs=[B1, torch.zeros(n, 16, dtype=bf).t()])
+    expect(ValueError, "do not fit", As=[A1, torch.zeros(k + 8, 16, dtype=bf)])      # k differs
+    expect(ValueError, "do not fit", Bs=[B1, torch.zeros(16, n + 8, dtype=bf)])      # n differs
+    expect(ValueError, "do not fit", Bs=[B1, torch.zeros(12, n, dtype=bf)])          # rank of B != A
+    expect(ValueError, "rank", As=[A1, torch.zeros(k, 300, dtype=bf)], Bs=[B1, torch.zeros(300, n, dtype=bf)])
+    expect(ValueError, "dropout", ps=[0.1, 1.0])
+    expect(ValueError, "dropout", ps=[-0.5, 0.0])
+    expect(ValueError, "dropout", ps=[0.1, 0.999999999])   # rounds to 1.0 as a float32
+    expect(ValueError, "alpha", alphas=[float("inf"), 1.0])
+    expect(ValueError, "alpha", alphas=[1.0, 1e39])         # overflows a float32
+    expect(ValueError, "same", ps=[0.1])
+    expect(ValueError, "dA", dAs=[torch.zeros(k, 8, dtype=bf), torch.zeros(k, 8, dtype=bf)],
+           dBs=[torch.zeros_like(B1), torch.zeros_like(B2)])
+    expect(ValueError, "dB", dAs=[torch.zeros_like(A1), torch.zeros_like(A2)],
+           dBs=[torch.zeros_like(B1), torch.zeros(n, 16, dtype=bf).t()])
+    expect(ValueError, "GPU")                                # otherwise valid, but on the host

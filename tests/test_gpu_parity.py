@@ -2,7 +2,7 @@
 the oracle finishes in seconds (several tiles plus ragged tails), and the edge
 cases: m = 0, ragged m/k/n, ranks 1..256, p = 0, mixed-adapter tiles, empty
 and tile-straddling segments, unused adapters, determinism, a non-default
-stream, and the frozen GEMMs against a plain PyTorch fp32 product."""
+stream, 0xFF-filled workspaces, and the frozen GEMMs against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -114,6 +114,24 @@ def test_bwd_without_input_gradient():
     lf.lora_linear(Xd, Wd, Ag, Bg, 2.0, 0.1, 3, 0).backward(dYd)
     torch.cuda.synchronize()
     assert Xd.grad is None and torch.equal(Ag.grad, dA) and torch.equal(Bg.grad, dB)
+
+
+@pytest.mark.parametrize("m,k,n,r", [(300, 264, 264, 33), (333, 264, 264, 36), (300, 264, 136, 80),
+                                     (520, 1024, 264, 96), (96, 256, 264, 256), (257, 264, 520, 17)])
+def test_single_garbage_workspace(m, k, n, r):
+    # workspaces filled with 0xFF bytes (NaN as bf16 or fp32): every value the
+    # kernels read from them must have been written by the same call
+    log(f"0xFF workspaces m={m} k={k} n={n} r={r}")
+    X, W, A, B, dY = small_case(m, k, n, r, seed=5 * m + r)
+    Xd, Wd, Ad, Bd, dYd = (t.cuda() for t in (X, W, A, B, dY))
+    wsf = torch.full((max(lf.lora_linear_fwd_workspace_size(m, k, n, r), 1),), 0xFF, dtype=torch.uint8,
+                     device="cuda")
+    wsb = torch.full((lf.lora_linear_bwd_workspace_size(m, k, n, r),), 0xFF, dtype=torch.uint8, device="cuda")
+    Y, S, keep = lf.lora_linear_fwd(Xd, Wd, Ad, Bd, 2.0, 0.1, 6, 0, workspace=wsf)
+    dX, dA, dB = lf.lora_linear_bwd(dYd, Xd, Wd, Ad, Bd, S, keep, 2.0, 0.1, workspace=wsb)
+    torch.cuda.synchronize()
+    g = {"Y": Y.cpu(), "S": S.cpu(), "keep": keep.cpu(), "dX": dX.cpu(), "dA": dA.cpu(), "dB": dB.cpu()}
+    log(f"  {compare_single(g, oracle_single(X, W, A, B, dY, 2.0, 0.1, 6, 0), 0.1)}")
 
 
 def test_single_config0_workload():
@@ -257,6 +275,70 @@ def test_multi_single_segment_equals_single_bitwise():
     assert torch.equal(s["dB"], mu["dB"][0])
 
 
+def test_multi_garbage_workspace():
+    m, k, n, ranks, alphas, ps, seg_off, seg_ad = MULTI_CASES[2]
+    log("mixed adapters, 0xFF workspaces")
+    X, W, As, Bs, dY = multi_case(m, k, n, ranks, seed=102)
+    dev = "cuda"
+    Xd, Wd, dYd = X.to(dev), W.to(dev), dY.to(dev)
+    Ad, Bd = [a.to(dev) for a in As], [b.to(dev) for b in Bs]
+    dAd = [torch.full_like(a, 7.0) for a in Ad]
+    dBd = [torch.full_like(b, 7.0) for b in Bd]
+    r_max, na, ns = max(ranks), len(ranks), len(seg_ad)
+    table = lf.adapter_table(Ad, Bd, alphas, ps, dAd, dBd)
+    so = torch.as_tensor(np.asarray(seg_off, dtype=np.int64)).to(dev)
+    sa = torch.as_tensor(np.asarray(seg_ad, dtype=np.int32)).to(dev)
+    wsf = torch.full((lf.multi_lora_fwd_workspace_size(m, k, n, r_max, na, ns),), 0xFF, dtype=torch.uint8,
+                     device=dev)
+    wsb = torch.full((lf.multi_lora_bwd_workspace_size(m, k, n, r_max, na, ns),), 0xFF, dtype=torch.uint8,
+                     device=dev)
+    Y, S, keep = lf.multi_lora_linear_fwd(Xd, Wd, table, na, so, sa, r_max, 5, 0, workspace=wsf)
+    dX = lf.multi_lora_linear_bwd(dYd, Xd, Wd, table, na, so, sa, S, keep, r_max, workspace=wsb)
+    torch.cuda.synchronize()
+    o = oracle_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, 5, 0)
+    assert_bits_equal("keep_bits", keep.cpu(), o["bits"])
+    check_close("S", S.cpu(), o["S"], rel=1e-4)
+    check_close("Y", Y.cpu(), o["Y"])
+    check_close("dX", dX.cpu(), o["dX"])
+    for a in range(na):
+        check_close(f"dA[{a}]", dAd[a].cpu(), o["dA"][a])
+        check_close(f"dB[{a}]", dBd[a].cpu(), o["dB"][a])
+
+
+def test_multi_bwd_without_input_gradient():
+    # dX = NULL skips the dX GEMM of the mixed form too; dA and dB are those of
+    # the full call bit for bit, directly and through the autograd wrapper
+    m, k, n, ranks = 600, 256, 264, [16, 64, 8]
+    alphas, ps = [2.0, 1.0, 0.5], [0.1, 0.2, 0.0]
+    seg_off, seg_ad = [0, 100, 430, 600], [2, 0, 1]
+    X, W, As, Bs, dY = multi_case(m, k, n, ranks, seed=91)
+    dev = "cuda"
+    Xd, Wd, dYd = X.to(dev), W.to(dev), dY.to(dev)
+    Ad, Bd = [a.to(dev) for a in As], [b.to(dev) for b in Bs]
+    so = torch.as_tensor(np.asarray(seg_off, dtype=np.int64)).to(dev)
+    sa = torch.as_tensor(np.asarray(seg_ad, dtype=np.int32)).to(dev)
+    full = ([torch.empty_like(a) for a in Ad], [torch.empty_like(b) for b in Bd])
+    part = ([torch.empty_like(a) for a in Ad], [torch.empty_like(b) for b in Bd])
+    t_full = lf.adapter_table(Ad, Bd, alphas, ps, *full)
+    t_part = lf.adapter_table(Ad, Bd, alphas, ps, *part)
+    Y, S, keep = lf.multi_lora_linear_fwd(Xd, Wd, t_full, 3, so, sa, 64, 4, 0)
+    dX = lf.multi_lora_linear_bwd(dYd, Xd, Wd, t_full, 3, so, sa, S, keep, 64)
+    dX0 = lf.multi_lora_linear_bwd(dYd, Xd, Wd, t_part, 3, so, sa, S, keep, 64, want_dX=False)
+    torch.cuda.synchronize()
+    assert dX is not None and dX0 is None
+    for i in range(3):
+        assert torch.equal(full[0][i], part[0][i]) and torch.equal(full[1][i], part[1][i]), i
+    Ag = [a.clone().requires_grad_() for a in Ad]
+    Bg = [b.clone().requires_grad_() for b in Bd]
+    Y2 = lf.multi_lora_linear(Xd, Wd, so, sa, Ag, Bg, alphas, ps, 4, 0)
+    assert torch.equal(Y2.detach(), Y)
+    Y2.backward(dYd)
+    torch.cuda.synchronize()
+    assert Xd.grad is None
+    for i in range(3):
+        assert torch.equal(Ag[i].grad, full[0][i]) and torch.equal(Bg[i].grad, full[1][i]), i
+
+
 def test_multi_deterministic():
     m, k, n, ranks, alphas, ps, seg_off, seg_ad = MULTI_CASES[0]
     X, W, As, Bs, dY = multi_case(m, k, n, ranks, seed=100)
@@ -269,7 +351,8 @@ def test_multi_deterministic():
 
 
 # ----------------------------------------------------------------------------
-# Frozen GEMMs against a plain PyTorch fp32 product
+# Frozen GEMMs against the oracle's products (its forward with B = 0 is X W;
+# its input gradient with dS = 0 is dY W^T)
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("m,k,n", [(512, 1024, 1024), (300, 200, 136), (1000, 264, 520)])
 def test_frozen_gemms(m, k, n):
@@ -280,5 +363,10 @@ def test_frozen_gemms(m, k, n):
     Y = lf.lora_frozen_fwd(X.cuda(), W.cuda())
     dX = lf.lora_frozen_bwd(dY.cuda(), W.cuda())
     torch.cuda.synchronize()
-    check_close("XW", Y.cpu(), X.float() @ W.float())
-    check_close("dY W^T", dX.cpu(), dY.float() @ W.float().t())
+    Xn, Wn, dYn = (np.ascontiguousarray(t.to(torch.float64).numpy()) for t in (X, W, dY))
+    r = 1
+    Y_ref = oracle.lora_y(Xn, Wn, np.zeros((m, r)), np.zeros((r, n)), 1.0)
+    dX_ref = oracle.lora_dx(dYn, Wn, np.zeros((m, r)), np.zeros((k, r)), np.ones((m, k), dtype=np.uint8),
+                            np.float32(0.0))
+    check_close("XW", Y.cpu(), Y_ref)
+    check_close("dY W^T", dX.cpu(), dX_ref)
