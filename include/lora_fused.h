@@ -131,6 +131,25 @@ lora_status lora_linear_bwd(const void *dY, const void *X, const void *W, const 
                             void *dX, void *dA, void *dB,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same backward for callers that cannot allocate device memory (code
+ * under graph capture, tight training loops, harnesses that forbid
+ * allocation): it takes no workspace and uses a scratch array of
+ * lora_linear_bwd_noalloc_max_scratch() bytes (64 MiB) that the library holds
+ * in static device memory, one per GPU, until the process ends.  It never
+ * allocates or frees.  The scratch of the current device is used (the stream
+ * must belong to it).  A shape whose workspace (lora_linear_bwd_workspace_size)
+ * exceeds the scratch returns LORA_ERR_UNSUPPORTED before anything is
+ * enqueued.  Every call on one GPU shares that GPU's scratch: calls that may
+ * overlap in time on one GPU (different streams, different host threads
+ * without ordering) race and must not be made; calls in one stream's order
+ * are safe.  Outputs, checks and errors are otherwise those of
+ * lora_linear_bwd, whose kernels it runs. */
+size_t lora_linear_bwd_noalloc_max_scratch(void);
+lora_status lora_linear_bwd_noalloc(const void *dY, const void *X, const void *W, const void *A,
+                                    const void *B, const float *S, const uint32_t *keep_bits,
+                                    int64_t m, int64_t k, int64_t n, int32_t r, float alpha, float p,
+                                    void *dX, void *dA, void *dB, hipStream_t stream);
+
 /* ---- mixed-adapter batch (FusedMultiLoRA) ------------------------------- */
 
 /* Segments: rows [seg_off[s], seg_off[s+1]) use adapter seg_adapter[s];

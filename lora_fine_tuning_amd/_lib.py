@@ -32,6 +32,7 @@ EXPORTS = [
     "lora_profiling_reset", "lora_profiling_query", "lora_status_string",
     "lora_last_error_message", "lora_pack_greedy", "lora_microbatch_segments",
     "lora_check_bubble_lemma", "lora_dora_norm_workspace_size", "lora_dora_norm",
+    "lora_linear_bwd_noalloc_max_scratch", "lora_linear_bwd_noalloc",
 ]
 
 
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                   SZ, P]),
         "lora_linear_bwd": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, F32, F32, P, P, P, P,
                                   SZ, P]),
+        "lora_linear_bwd_noalloc_max_scratch": (SZ, []),
+        "lora_linear_bwd_noalloc": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, F32, F32, P, P, P, P]),
         "multi_lora_linear_fwd": (I32, [P, P, P, I32, P, P, I32, I64, I64, I64, I32, U64, U64, P,
                                         P, P, P, SZ, P]),
         "multi_lora_linear_bwd": (I32, [P, P, P, P, I32, P, P, I32, P, P, I64, I64, I64, I32, P,
@@ -190,6 +193,28 @@ def lora_linear_bwd(dY, X, W, A, B, S, keep_bits, alpha: float, p: float, *, dX=
     _check(load().lora_linear_bwd(_ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(S),
                                   _ptr(keep_bits), m, k, n, r, alpha, p, _ptr(dX), _ptr(dA),
                                   _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)))
+    return dX, dA, dB
+
+
+def lora_linear_bwd_noalloc_max_scratch() -> int:
+    return int(load().lora_linear_bwd_noalloc_max_scratch())
+
+
+def lora_linear_bwd_noalloc(dY, X, W, A, B, S, keep_bits, alpha: float, p: float, dX, dA, dB, *,
+                            stream=None):
+    """lora_linear_bwd without a workspace (the library's static scratch);
+    every output must be given, since the point is to allocate nothing."""
+    for t, nm in ((dY, "dY"), (X, "X"), (W, "W"), (A, "A"), (B, "B"), (dA, "dA"), (dB, "dB")):
+        _need(t, torch.bfloat16, nm)
+    _need(S, torch.float32, "S")
+    if dX is not None:
+        _need(dX, torch.bfloat16, "dX")
+    m, k = X.shape
+    n = W.shape[1]
+    r = A.shape[1]
+    _check(load().lora_linear_bwd_noalloc(_ptr(dY), _ptr(X), _ptr(W), _ptr(A), _ptr(B), _ptr(S),
+                                          _ptr(keep_bits), m, k, n, r, alpha, p, _ptr(dX), _ptr(dA),
+                                          _ptr(dB), _stream(stream)))
     return dX, dA, dB
 
 

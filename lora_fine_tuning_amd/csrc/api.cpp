@@ -649,3 +649,60 @@ extern "C" lora_status lora_frozen_bwd(const void *dY, const void *W, int64_t m,
            "frozen bwd launch");
     return LORA_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Backward without a workspace argument, for callers that cannot allocate
+// device memory (code under graph capture, tight loops, harnesses that forbid
+// it).  Its scratch is a file-scope device array of kScratchBytes: every GPU
+// the library runs on holds one copy until the process ends.  The array's
+// name is a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+static lora_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(LORA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                    kScratchDevices - 1);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(LORA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LORA_OK;
+}
+
+extern "C" size_t lora_linear_bwd_noalloc_max_scratch(void) { return kScratchBytes; }
+
+extern "C" lora_status lora_linear_bwd_noalloc(const void *dY, const void *X, const void *W, const void *A,
+                                               const void *B, const float *S, const uint32_t *keep_bits,
+                                               int64_t m, int64_t k, int64_t n, int32_t r, float alpha, float p,
+                                               void *dX, void *dA, void *dB, hipStream_t stream) {
+    CHECK(check_shape(m, k, n));
+    CHECK(check_rank(r));
+    const size_t need = plan_bwd(m, k, n, r, false, 0).bytes;
+    if (need > kScratchBytes)
+        return fail(LORA_ERR_UNSUPPORTED,
+                    "shape m=%lld k=%lld n=%lld r=%d needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use lora_linear_bwd with a workspace)",
+                    (long long)m, (long long)k, (long long)n, r, need, kScratchBytes);
+    void *ws = nullptr;
+    CHECK(scratch_of_current_device(&ws));
+    return lora_linear_bwd(dY, X, W, A, B, S, keep_bits, m, k, n, r, alpha, p, dX, dA, dB, ws, kScratchBytes,
+                           stream);
+}

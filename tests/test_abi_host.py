@@ -256,3 +256,16 @@ def test_adapter_table_host_checks():
     expect(ValueError, "dB", dAs=[torch.zeros_like(A1), torch.zeros_like(A2)],
            dBs=[torch.zeros_like(B1), torch.zeros(n, 16, dtype=bf).t()])
     expect(ValueError, "GPU")                                # otherwise valid, but on the host
+
+
+def test_bwd_noalloc_host_checks(lib):
+    f = lib.lora_linear_bwd_noalloc
+    cap = lib.lora_linear_bwd_noalloc_max_scratch()
+    assert cap == 64 << 20
+    # a shape whose workspace exceeds the static scratch is refused before any device call
+    big = (8192, 4096, 4096, 256)
+    assert lf.lora_linear_bwd_workspace_size(*big) > cap
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, *big, 1.0, 0.1, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert b"scratch" in lib.lora_last_error_message()
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 60, 64, 8, 1.0, 0.1, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 0, 1.0, 0.1, FAKE, FAKE, FAKE, None) == INVALID
