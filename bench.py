@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-rows", type=int, default=128,
+    ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows (tokens) of the headline workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shapes", default="4096,14336", help="--concat: n of each projection (k = 4096)")
@@ -770,7 +770,7 @@ def cpu_baseline(w, tens, rows):
     try:
         gomp = ctypes.CDLL("libgomp.so.1")
         gomp.omp_set_num_threads(1)
-        n1, t1 = run(max(1, per // 16))
+        n1, t1 = run(max(1, per // 32))
         gomp.omp_set_num_threads(threads)
         one = {"value": round(n1 / t1, 3), "rows": n1, "seconds": round(t1, 2)}
     except OSError:

@@ -202,6 +202,69 @@ __device__ __forceinline__ int first_segment(const GemmParams &P, int m0) {
 }
 
 
+// ---- B3 with the rank-side matrix staged in LDS.  The adapter items of one
+// 256-row tile (at most two; consecutive segments of one adapter count as
+// one), each with r <= 128, r a multiple of 8 and a 16-byte aligned A.  Every
+// thread of the work-group computes the same plan.
+struct TileItems {
+    int n;
+    ExtItem it[2];  // indexed by constants only (no dynamic index: registers, not scratch)
+    int rp[2];      // ranks rounded up to a multiple of 32
+};
+
+// Every field of an item as a wave-uniform value (SGPRs).
+__device__ __forceinline__ ExtItem uniform_item(const ExtItem &it) {
+    ExtItem u;
+    u.lo = __builtin_amdgcn_readfirstlane(it.lo);
+    u.hi = __builtin_amdgcn_readfirstlane(it.hi);
+    u.r = __builtin_amdgcn_readfirstlane(it.r);
+    u.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, it.scale)));
+    const uint64_t w = (uint64_t)(uintptr_t)it.w;
+    const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)w), wh = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
+    u.w = (const uint16_t *)(uintptr_t)(((uint64_t)wh << 32) | wl);
+    return u;
+}
+
+template <bool MULTI>
+__device__ __forceinline__ bool plan_tile_items(const GemmParams &P, int m0, TileItems &ti) {
+    const int rend = min(m0 + GBM, P.M);
+    int n = 0;
+    ExtItem a{}, b{};
+    if (!MULTI) {
+        get_item<2, false>(P, 0, a);
+        n = 1;
+    } else {
+        for (int s = first_segment(P, m0); s < P.nseg && P.seg_off[s] < (int64_t)rend; ++s) {
+            ExtItem it;
+            if (!get_item<2, true>(P, s, it)) continue;
+            if (it.hi <= m0 || it.lo >= rend) continue;
+            if (n == 1 && it.w == a.w && it.r == a.r && it.scale == a.scale && it.lo == a.hi) {
+                a.hi = it.hi;  // the same adapter goes on: one item
+                continue;
+            }
+            if (n == 2) return false;
+            if (n == 0) a = it;
+            else b = it;
+            ++n;
+        }
+        if (n == 0) return false;
+    }
+    if (a.r > 128 || (a.r & 7) != 0 || (((uintptr_t)a.w) & 15) != 0) return false;
+    if (n == 2 && (b.r > 128 || (b.r & 7) != 0 || (((uintptr_t)b.w) & 15) != 0)) return false;
+    ti.n = __builtin_amdgcn_readfirstlane(n);
+    ti.it[0] = uniform_item(a);
+    ti.it[1] = uniform_item(b);
+    ti.rp[0] = (ti.it[0].r + 31) & ~31;
+    ti.rp[1] = (ti.it[1].r + 31) & ~31;
+    return true;
+}
+
+// LDS slab of 64 ranks of A for the tile's 256 columns: 128-byte column rows,
+// the 16-byte chunk holding ranks 8q .. 8q+7 of column c at chunk position
+// q ^ ((c >> 1) & 7) (16 consecutive columns read at one rank chunk hit 16
+// distinct 16-byte bank groups).
+__device__ __forceinline__ uint32_t slab_off(int c, int q) { return (uint32_t)(c * 128 + ((q ^ ((c >> 1) & 7)) << 4)); }
+
 constexpr int BK = 64;              // K depth of one LDS stage
 constexpr int NST = 2;              // stages in the LDS ring
 constexpr int ROWB = BK * 2;        // bytes per LDS row of a K-contiguous tile
@@ -471,27 +534,38 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j, std::false_type{});
     }
-    // B3, one adapter with 64 < r <= 128 (16-byte A rows): A's ranks 64..127 of
-    // the tile's 256 columns go to the 32 KiB past the ring (128-byte rows,
-    // 16-byte chunk q of column c at q ^ (c & 7)), loaded during the K loop
-    bool ahi = false;
-    if constexpr (EPI == 2 && !MULTI && FAST == 0) {
-        ahi = P.ext_r > 64 && P.ext_r <= 128 && (P.ext_r & 7) == 0 && (((uintptr_t)P.ext) & 15) == 0;
-        if (ahi) {
-            const uint32_t abytes = (uint32_t)P.N * (uint32_t)P.ext_r * 2u;
-            const sgpr4_t d = make_desc(P.ext, abytes);
+    // B3 (not the all-loads-first forms): when the tile's items fit (see
+    // plan_tile_items), A is staged in LDS for the epilogue.  The slab of the
+    // first item's ranks 0..63 goes to the 32 KiB past the ring now, loaded
+    // during the K loop; the rest follows the K loop into the idle ring.
+    TileItems ti;
+    bool lds_epi = false;
+    auto slab_dma = [&](const ExtItem &it, int rbase, uint32_t dst) {
+        // the item is the same in every lane: its address and size go to SGPRs
+        const uint64_t ab = (uint64_t)P.N * (uint64_t)it.r * 2u;
+        const uint64_t wp = (uint64_t)(uintptr_t)it.w;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)wp);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(wp >> 32));
+        const uint32_t nb = __builtin_amdgcn_readfirstlane((uint32_t)(ab < 0x7FFFFFF0ull ? ab : 0x7FFFFFF0ull));
+        const sgpr4_t d = make_desc((const void *)(uintptr_t)(((uint64_t)hi << 32) | lo), nb);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int j = 8 * wave + q, c = 8 * j + (lane >> 3);
-                const int lq = (lane & 7) ^ (c & 7);  // logical 8-rank chunk of the lane's 16 bytes
-                const uint32_t off = (n0 + c < P.N && 64 + 8 * lq < P.ext_r)
-                    ? ((uint32_t)(n0 + c) * (uint32_t)P.ext_r + 64u + 8u * lq) * 2u : kOOB;
-                dma16(d, off, pf_lds + j * 1024);
-            }
+        for (int q = 0; q < 8; ++q) {
+            const int j = 8 * wave + q, c = 8 * j + (lane >> 3);
+            const int lq = (lane & 7) ^ ((c >> 1) & 7);  // logical 8-rank chunk of the lane's 16 bytes
+            const uint32_t off = (n0 + c < P.N && rbase + 8 * lq < it.r)
+                ? ((uint32_t)(n0 + c) * (uint32_t)it.r + (uint32_t)(rbase + 8 * lq)) * 2u : kOOB;
+            dma16(d, off, dst + j * 1024);
         }
+    };
+    if constexpr (EPI == 2 && FAST == 0) {
+        const bool svec0 = (P.RS & 7) == 0 && (((uintptr_t)P.Sx) & 15) == 0;
+        lds_epi = svec0 && (P.keep == nullptr || P.keep16) && plan_tile_items<MULTI>(P, m0, ti);
+        // one item of rank <= 32 in a mixed batch: the all-loads-first epilogue below
+        if (MULTI && lds_epi && ti.n == 1 && ti.it[0].r <= 32 && P.multi_fast) lds_epi = false;
+        if (lds_epi) slab_dma(ti.it[0], 0, pf_lds);
     }
     if constexpr (PF) epi_prefetch();
-    if (ahi) wait_vmcnt<NDMA + 8>();
+    if (lds_epi) wait_vmcnt<NDMA + 8>();
     else wait_vmcnt<PF ? NDMA + NPF : NDMA>();
     asm volatile("" ::: "memory");  // keep the LDS reads below the barrier
     __builtin_amdgcn_s_barrier();
@@ -501,6 +575,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         read_frag(0, 0, 0, 0, t);
         read_frag(0, 0, 0, 1, t);
     }
+    // No scalar load may still be in flight when the K loop starts (the
+    // compiler sinks the epilogue's kernel-argument loads to here): one would
+    // make it wait for every LDS read (lgkmcnt 0) at the top of each MFMA step
+    // instead of only for the fragments the next MFMAs use.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
     // One stage: step 0 (reads of its step 1), then -- once stage kt+1 has
     // landed everywhere and stage kt's buffer is no longer read -- step 1 with
     // the reads of step 0 of stage kt+1 and the loads of stage kt+2 into the
@@ -749,6 +828,137 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         fast_epilogue(it);
         return;
     } else {
+    // ---- B3, A staged in LDS (plan_tile_items).  After the K loop the ring
+    // holds: [0, 32 KiB) the output staging, 8 KiB per wave (two 16-row
+    // bands); slabs of 64 ranks at 32, 64 and 96 KiB, the first item's ranks
+    // 0..63 already past the ring.  The wave runs its 16-row bands in order:
+    // the next band's S / dS rows and mask words are loaded while the current
+    // band's rank-deep MFMAs run, its rank chunks (at most four) come from the
+    // slabs, the masked sum is staged and its 16 rows are stored at once.
+    if constexpr (EPI == 2 && FAST == 0) {
+        if (lds_epi) {
+            const uint32_t slab_at[4] = {(uint32_t)(NST * STAGE_BYTES), 32768u, 65536u, 98304u};
+            __syncthreads();  // every wave is done with the ring; slab 0 landed everywhere
+            if (ti.rp[0] > 64) slab_dma(ti.it[0], 64, smem_lds + slab_at[1]);
+            if (ti.n == 2) {
+                slab_dma(ti.it[1], 0, smem_lds + slab_at[2]);
+                if (ti.rp[1] > 64) slab_dma(ti.it[1], 64, smem_lds + slab_at[3]);
+            }
+            // A band's rank chunks: those of each item its 16 rows meet, item 0's
+            // first (rows outside an item read zeros, so the band sums them all).
+            // Up to four chunks come from registers loaded during the previous
+            // band; a band meeting both items may have up to four more, loaded
+            // when needed.
+            auto band_nc0 = [&](int tm) {
+                const int b0 = wrow0 + 16 * tm, b1 = min(b0 + 16, P.M);
+                return (b0 < ti.it[0].hi && b1 > ti.it[0].lo) ? ti.rp[0] >> 5 : 0;
+            };
+            auto band_nsl = [&](int tm, int nc0) {
+                const int b0 = wrow0 + 16 * tm, b1 = min(b0 + 16, P.M);
+                return nc0 + ((ti.n == 2 && b0 < ti.it[1].hi && b1 > ti.it[1].lo) ? ti.rp[1] >> 5 : 0);
+            };
+            const bool has_keep = P.keep != nullptr;
+            const __amdgpu_buffer_rsrc_t rK = make_rsrc(has_keep ? P.keep + (size_t)min(wrow0, P.M) * P.KW : P.keep,
+                                                        has_keep ? (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.KW * 4u : 0u);
+            // S / dS of band tm, chunk j: ranks rr0 + 8 (lane / 16) .. +7 of the lane's row
+            auto load_slot = [&](int tm, int j, int nc0, float4 (&f)[2]) {
+                const bool second = j >= nc0;
+                const ExtItem &it = second ? ti.it[1] : ti.it[0];
+                const int rb = 32 * (second ? j - nc0 : j) + 8 * lg;
+                const int row = wrow0 + tm * 16 + l16;
+                const bool ok = row >= it.lo && row < it.hi && rb < it.r;
+                const uint32_t off = ok ? (uint32_t)((tm * 16 + l16) * P.RS + rb) * 4u : kOOB;
+                f[0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off, 0, 0));
+                f[1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, ok ? off + 16u : kOOB, 0, 0));
+            };
+            float4 rf[2][4][2];
+            uint4 kw[2];
+            int nc0b[2], nslb[2];
+            auto load_band = [&](int tm, int slot) {
+                const int nc0 = band_nc0(tm), nsl = band_nsl(tm, nc0);
+                nc0b[slot] = nc0;
+                nslb[slot] = nsl;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j < nsl) load_slot(tm, j, nc0, rf[slot][j]);
+                kw[slot] = has_keep ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                 rK, (uint32_t)((tm * 16 + l16) * P.KW + (wcol0 >> 5)) * 4u, 0, 0))
+                                    : make_uint4(~0u, ~0u, ~0u, ~0u);
+            };
+            const int swl = (l16 >> 1) & 7;
+            // rank-deep MFMAs of chunk j (the row side in f) into acc2
+            auto mfma_slot = [&](int j, int nc0, const float4 (&f)[2], f32x4_t (&acc2)[NT16]) {
+                const bool second = j >= nc0;
+                const int rr0 = 32 * (second ? j - nc0 : j);
+                const float sc = second ? ti.it[1].scale : ti.it[0].scale;
+                float v[8] = {f[0].x, f[0].y, f[0].z, f[0].w, f[1].x, f[1].y, f[1].z, f[1].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] *= sc;
+                uint4 hi, lo;
+                split_frag(v, hi, lo);
+                const int q = ((rr0 >> 5) & 1) * 4 + lg;  // 8-rank chunk inside the slab
+                const lds_char *sb = (const lds_char *)smem + slab_at[(second ? 2 : 0) + (rr0 >> 6)];
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) {
+                    const int c = wn * 128 + tn * 16 + l16;
+                    const uint4 cf = *(const uint4 *)(sb + c * 128 + ((q ^ swl) << 4));
+                    acc2[tn] = mfma16x16x32(cf, hi, acc2[tn]);
+                    acc2[tn] = mfma16x16x32(cf, lo, acc2[tn]);
+                }
+            };
+            load_band(0, 0);
+            wait_vmcnt<0>();
+            __syncthreads();  // the slabs landed
+            lds_char *stg = (lds_char *)smem + wave * 8192;
+#pragma unroll
+            for (int tm = 0; tm < NT16; ++tm) {
+                const int cur = tm & 1;
+                if (tm + 1 < NT16) load_band(tm + 1, cur ^ 1);
+                const int nc0 = nc0b[cur], nsl = nslb[cur];
+                f32x4_t acc2[NT16];
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) acc2[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j < nsl) mfma_slot(j, nc0, rf[cur][j], acc2);
+                for (int j = 4; j < nsl; ++j) {  // a band meeting both items
+                    float4 f[2];
+                    load_slot(tm, j, nc0, f);
+                    mfma_slot(j, nc0, f, acc2);
+                }
+                // masked sum into the band's staging rows (rows past M and
+                // columns past N are staged too; the stores drop them)
+                lds_char *sbnd = stg + (tm & 1) * 4096;
+                const uint4 k4 = kw[cur];
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) {
+                    const uint32_t w = (tn >> 1) == 0 ? k4.x : (tn >> 1) == 1 ? k4.y : (tn >> 1) == 2 ? k4.z : k4.w;
+                    const uint32_t kwb = w >> (((tn & 1) << 4) + 4 * lg);
+                    float x[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t keep = (uint32_t)((int32_t)(kwb << (31 - e)) >> 31);
+                        x[e] = acc[tm][tn][e] + __uint_as_float(__float_as_uint(acc2[tn][e]) & keep);
+                    }
+                    const int ch = (2 * tn + (lg >> 1)) ^ l16;
+                    *(uint2 *)(sbnd + l16 * 256 + ch * 16 + (lg & 1) * 8) =
+                        make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+                }
+                // the band's 16 rows: 4 stores of 4 whole 256-byte rows per wave
+                const int cc = lane & 15;
+                const int col = wcol0 + cc * 8;
+#pragma unroll
+                for (int it4 = 0; it4 < 4; ++it4) {
+                    const int rr = it4 * 4 + (lane >> 4);
+                    const uint4 v = *(const uint4 *)(sbnd + rr * 256 + ((cc ^ rr) << 4));
+                    const uint32_t off = col < P.N ? (uint32_t)((size_t)(wrow0 + tm * 16 + rr - m0) * N2 + (size_t)col * 2) : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                                           rC, off, 0, kStoreNT);
+                }
+            }
+            return;
+        }
+    }
     // mixed adapters: the wave's first segment, found once
     const int wseg = MULTI ? first_segment(P, wrow0) : 0;
     // B3 with mixed adapters: a wave whose rows all lie in one segment (wave-
@@ -842,7 +1052,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     if (EPI == 2 && (!MULTI || wave_one_seg)) {
         if (MULTI) it1 = wit;
         else get_item<EPI, MULTI>(P, 0, it1);
-        one_chunk = it1.r <= 64 || (!MULTI && ahi);
+        one_chunk = it1.r <= 64;
         it2 = it1;
         rvec1 = rvec2 = svec && (it1.r & 7) == 0;
     }
@@ -871,8 +1081,6 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             cf1[1][tn] = col_ext_frag<EPI>(P, rW2, wcol0, it2, wcol0 + tn * 16 + l16, rk2, lane, avec2);
         }
     }
-
-    if (ahi) __syncthreads();  // every wave's part of the A copy landed (K = 0 never waited)
 
     // ---- output (B3 adds the masked rank-deep term one 16-row band at a time)
     const bool has_keep = EPI == 2 && P.keep != nullptr;
@@ -907,23 +1115,6 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                     for (int tn = 0; tn < NT16; ++tn) {
                         acc2[tn] = mfma16x16x32(cf1[1][tn], hi1, acc2[tn]);
                         acc2[tn] = mfma16x16x32(cf1[1][tn], lo1, acc2[tn]);
-                    }
-                }
-                if (!MULTI && ahi) {
-                    // ranks 64..127: column-side fragments from the LDS copy of A
-                    const lds_char *pa = (const lds_char *)smem + NST * STAGE_BYTES;
-#pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2) {
-                        uint4 hi, lo;
-                        row_ext_frags(P, rS, wrow0, it1, row, 64 + 32 * c2, lane, rvec1, hi, lo);
-                        const int lq = 4 * c2 + lg;
-#pragma unroll
-                        for (int tn = 0; tn < NT16; ++tn) {
-                            const int c = wn * 128 + tn * 16 + l16;
-                            const uint4 cf = *(const uint4 *)(pa + c * 128 + ((lq ^ (c & 7)) << 4));
-                            acc2[tn] = mfma16x16x32(cf, hi, acc2[tn]);
-                            acc2[tn] = mfma16x16x32(cf, lo, acc2[tn]);
-                        }
                     }
                 }
             } else {

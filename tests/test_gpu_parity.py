@@ -214,6 +214,10 @@ MULTI_CASES = [
      [0, 100, 200, 333], [1, 1, 0]),                           # same adapter twice in a row
     (600, 256, 264, [64, 16, 24], [2.0, 1.0, 0.5], [0.1, 0.2, 0.0],
      [0, 520, 600], [0, 2]),                                   # whole 128-row waves inside a rank-64 segment
+    (600, 264, 136, [128, 120], [1.0, 2.0], [0.1, 0.2],
+     [0, 300, 600], [0, 1]),                                   # a 16-row band meeting ranks 128 and 120 (8 chunks)
+    (520, 136, 264, [128, 64, 8], [2.0, 0.5, 4.0], [0.1, 0.0, 0.3],
+     [0, 200, 390, 520], [1, 0, 2]),                           # bands meeting ranks 64 | 128 and 128 | 8
 ]
 
 
