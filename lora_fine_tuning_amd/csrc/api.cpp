@@ -265,12 +265,14 @@ struct BwdPlan {
     B1Shape b1;
     int C2;
     int ds_parts;  // dS partials written by B1 (one per column tile)
+    bool b2w;      // the single-pass dA kernel (and its per-adapter sum launch)
+    int items2;    // its grid rows of work items
     size_t off_ds, off_dspart, off_dbpart, off_dapart, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
-    size_t off_t_b1, off_c_b1;
+    size_t off_t_b1, off_c_b1, off_aditems;
     size_t bytes;
 };
 
-BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_t nseg) {
+BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_t nseg, int32_t nad) {
     BwdPlan p{};
     p.RS = RS;
     const int rl = ((RS + 15) / 16) * 16;
@@ -280,11 +282,18 @@ BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_
     p.b1 = b1_shape(m, n, rl, RS, multi, nseg);
     p.C2 = rl <= 128 ? 256 : 128;
     p.ds_parts = p.b1.CT;
+    p.b2w = b2w_ok(rl, RS);
+    p.items2 = multi ? p.chunk_cap_bwd : cdiv(m, p.rows2);
+    const int nct2 = cdiv(k, 256);
     Carve c;
     p.off_ds = c.take((size_t)m * RS * sizeof(float));
     p.off_dspart = c.take(p.ds_parts > 1 ? (size_t)p.ds_parts * m * RS * sizeof(float) : 0);
     p.off_dbpart = c.take((size_t)p.b1.slots * RS * n * sizeof(float));
-    p.off_dapart = c.take((size_t)p.chunk_cap_bwd * k * RS * sizeof(float));
+    if (p.b2w)
+        p.off_dapart = c.take((size_t)p.chunk_cap_bwd * nct2 * 256 * 16 * b2w_blocks(rl) * sizeof(float));
+    else
+        p.off_dapart = c.take((size_t)p.chunk_cap_bwd * k * RS * sizeof(float));
+    p.off_aditems = c.take(multi ? (size_t)nad * sizeof(int32_t) : 0);
     if (multi) {
         p.off_t_f1 = c.take((size_t)p.chunk_cap_f1 * sizeof(ChunkEntry));
         p.off_c_f1 = c.take(sizeof(int32_t));
@@ -331,7 +340,7 @@ extern "C" size_t lora_linear_fwd_workspace_size(int64_t m, int64_t k, int64_t n
 
 extern "C" size_t lora_linear_bwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r) {
     if (m < 0 || k <= 0 || n <= 0 || r < 1) return 0;
-    return plan_bwd(m, k, n, r, false, 0).bytes;
+    return plan_bwd(m, k, n, r, false, 0, 1).bytes;
 }
 
 extern "C" lora_status lora_linear_fwd(const void *X, const void *W, const void *A, const void *B,
@@ -396,7 +405,7 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
         REQUIRE(keep_bits != nullptr || p == 0.0f, "keep_bits may be NULL only when p == 0");
         REQUIRE(aligned(keep_bits, 4), "keep_bits must be 4-byte aligned");
     }
-    const BwdPlan pl = plan_bwd(m, k, n, r, false, 0);
+    const BwdPlan pl = plan_bwd(m, k, n, r, false, 0, 1);
     if (workspace_bytes < pl.bytes)
         return fail(LORA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, pl.bytes);
     if (pl.bytes) REQ_PTR(workspace, 16);
@@ -411,11 +420,16 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
     HIPCHK(launch_b1_reduce(dSpart, m > 0 ? pl.ds_parts : 1, dS, dBpart, (int)m, (int)n, r, src, pl.b1.rows,
                             pl.b1.slots, stream),
            "dS/dB reduction launch");
-    if (m > 0)
-        HIPCHK(launch_b2(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, pl.rows2, src, chunks, pl.C2,
-                         dApart, stream), "B2 launch");
-    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r, src, pl.rows2, chunks, stream),
-           "dA reduction launch");
+    if (pl.b2w) {
+        HIPCHK(launch_b2w(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, pl.rows2, src, pl.items2,
+                          dApart, nullptr, stream), "B2 launch");
+    } else {
+        if (m > 0)
+            HIPCHK(launch_b2(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, pl.rows2, src, chunks,
+                             pl.C2, dApart, stream), "B2 launch");
+        HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r, src, pl.rows2, chunks, stream),
+               "dA reduction launch");
+    }
     if (m > 0 && dX != nullptr)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r, p == 0.0f ? nullptr : keep_bits,
                            (int)((k + 31) / 32), src, stream), "B3 launch");
@@ -446,9 +460,8 @@ extern "C" size_t multi_lora_fwd_workspace_size(int64_t m, int64_t k, int64_t n,
 
 extern "C" size_t multi_lora_bwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r_max,
                                                 int32_t num_adapters, int32_t num_segments) {
-    (void)num_adapters;
-    if (m < 0 || k <= 0 || n <= 0 || r_max < 1 || num_segments < 0) return 0;
-    return plan_bwd(m, k, n, r_max, true, num_segments).bytes;
+    if (m < 0 || k <= 0 || n <= 0 || r_max < 1 || num_segments < 0 || num_adapters < 1) return 0;
+    return plan_bwd(m, k, n, r_max, true, num_segments, num_adapters).bytes;
 }
 
 static AdapterSource multi_source(const lora_adapter *adapters, int32_t nad, const int64_t *seg_off,
@@ -522,7 +535,7 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
         REQ_PTR(keep_bits, 4);
         REQUIRE(dX == nullptr || aligned(dX, 16), "dX must be 16-byte aligned (or NULL: no input gradient)");
     }
-    const BwdPlan pl = plan_bwd(m, k, n, r_max, true, num_segments);
+    const BwdPlan pl = plan_bwd(m, k, n, r_max, true, num_segments, num_adapters);
     if (workspace_bytes < pl.bytes)
         return fail(LORA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, pl.bytes);
     REQ_PTR(workspace, 16);
@@ -534,10 +547,12 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
     src.count_bwd = (const int32_t *)ws_at(workspace, pl.off_c_bwd);
     src.chunks_b1 = (const ChunkEntry *)ws_at(workspace, pl.off_t_b1);
     src.count_b1 = (const int32_t *)ws_at(workspace, pl.off_c_b1);
+    int32_t *aditems = (int32_t *)ws_at(workspace, pl.off_aditems);
     HIPCHK(launch_router(seg_off, seg_adapter, num_segments, (int)m, adapters, num_adapters, r_max,
                          (ChunkEntry *)src.chunks_f1, (int32_t *)src.count_f1, pl.chunk_cap_f1,
                          (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, pl.rows2, pl.chunk_cap_bwd,
-                         (ChunkEntry *)src.chunks_b1, (int32_t *)src.count_b1, pl.b1.rows, pl.b1.slots, stream),
+                         (ChunkEntry *)src.chunks_b1, (int32_t *)src.count_b1, pl.b1.rows, pl.b1.slots, stream,
+                         aditems),
            "router launch");
     float *dS = (float *)ws_at(workspace, pl.off_ds);
     float *dSpart = pl.ds_parts > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
@@ -548,11 +563,16 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
     HIPCHK(launch_b1_reduce(dSpart, m > 0 ? pl.ds_parts : 1, dS, dBpart, (int)m, (int)n, r_max, src, pl.b1.rows,
                             pl.b1.slots, stream),
            "dS/dB reduction launch");
-    if (m > 0)
-        HIPCHK(launch_b2(X, keep_bits, dS, (int)m, (int)k, r_max, pl.rows2, src, chunks, pl.C2, dApart, stream),
-               "B2 launch");
-    HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r_max, src, pl.rows2, chunks, stream),
-           "dA reduction launch");
+    if (pl.b2w) {
+        HIPCHK(launch_b2w(X, keep_bits, dS, (int)m, (int)k, r_max, pl.rows2, src, pl.items2, dApart, aditems,
+                          stream), "B2 launch");
+    } else {
+        if (m > 0)
+            HIPCHK(launch_b2(X, keep_bits, dS, (int)m, (int)k, r_max, pl.rows2, src, chunks, pl.C2, dApart, stream),
+                   "B2 launch");
+        HIPCHK(launch_grad_reduce(1, dApart, (int)m, (int)k, (int)n, r_max, src, pl.rows2, chunks, stream),
+               "dA reduction launch");
+    }
     if (m > 0 && dX != nullptr)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r_max, keep_bits, (int)((k + 31) / 32),
                            src, stream), "B3 launch");
@@ -695,7 +715,7 @@ extern "C" lora_status lora_linear_bwd_noalloc(const void *dY, const void *X, co
                                                void *dX, void *dA, void *dB, hipStream_t stream) {
     CHECK(check_shape(m, k, n));
     CHECK(check_rank(r));
-    const size_t need = plan_bwd(m, k, n, r, false, 0).bytes;
+    const size_t need = plan_bwd(m, k, n, r, false, 0, 1).bytes;
     if (need > kScratchBytes)
         return fail(LORA_ERR_UNSUPPORTED,
                     "shape m=%lld k=%lld n=%lld r=%d needs %zu bytes of scratch; the static scratch holds %zu "

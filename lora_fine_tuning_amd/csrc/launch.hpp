@@ -32,10 +32,10 @@ inline bool f1_rank64(int r_lds, bool multi) {
 
 // Rows per B2 work item (the dA partials are one per item): 256, or taller
 // when the grid (items x 256-column tiles of k x rank tiles) would still have
-// about 1024 work-groups -- fewer partials for wide k or many rank tiles.
+// about 512 work-groups -- fewer partials for wide k or many rank tiles.
 inline int b2_rows(int64_t m, int64_t k, int r_lds) {
-    const int rt = r_lds > 32 ? (r_lds + 31) / 32 : 1;
-    const int64_t want = m * ((k + 255) / 256) * rt / 1024;
+    const int rt = r_lds > 128 ? (r_lds + 31) / 32 : 1;
+    const int64_t want = m * ((k + 255) / 256) * rt / 512;
     int64_t rows = std::max<int64_t>(kBwdRows, (want + 31) / 32 * 32);
     rows = std::min<int64_t>(rows, std::max<int64_t>(kBwdRows, (m + 31) / 32 * 32));
     // the kernels address an item's rows of X with 32-bit offsets
@@ -81,10 +81,12 @@ struct AdapterSource {
 // Which router table a kernel's work items come from.
 enum WorkTable { kTabF1 = 0, kTabBwd = 1, kTabB1 = 2 };
 
+// ad_items (may be NULL): work items of each adapter in the backward table.
 hipError_t launch_router(const int64_t *seg_off, const int32_t *seg_adapter, int nseg, int m,
                          const lora_adapter *adapters, int nad, int r_cap, ChunkEntry *t_f1,
                          int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int rows_bwd, int cap_bwd,
-                         ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream);
+                         ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream,
+                         int32_t *ad_items = nullptr);
 
 // s2 (streaming form only; may be NULL): also write alpha*S split into bf16
 // [hi | lo] rows of 2*s2_rp columns for the forward GEMM's extra K columns.
@@ -143,6 +145,22 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
 // nparts == 1) and dB = per-adapter sum of its row-group partials, one launch.
 hipError_t launch_b1_reduce(const float *dSpart, int nparts, float *dS, const float *dBpart, int m, int n,
                             int RS, const AdapterSource &src, int rows, int slots, hipStream_t stream);
+
+// The single-pass dA kernel (ranks up to 128 in one pass over X) serves
+// r_lds <= 128 when S / dS rows are 16-byte pieces (RS % 4 == 0).  Its
+// partials are [item][ceil(k/256)][256][16 * b2w_blocks] fp32; a second
+// launch adds each adapter's partials in item order and writes dA.
+inline int b2w_blocks(int r_lds) {
+    const int nb = (r_lds + 15) / 16;
+    return nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : 8;
+}
+inline bool b2w_ok(int r_lds, int RS) { return r_lds <= 128 && RS % 4 == 0; }
+// items: grid rows of work items (single: ceil(m / rows); multi: the
+// backward table's capacity); ad_items: multi only (the router's
+// per-adapter counts).
+hipError_t launch_b2w(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS, int rows,
+                      const AdapterSource &src, int items, float *part, const int32_t *ad_items,
+                      hipStream_t stream);
 
 // rows: rows per partial of the single-adapter form; slots: partials
 // written (an upper bound in the mixed-adapter form, where the router's chunk

@@ -11,6 +11,7 @@
 // contraction here runs on MFMA 16x16x32 bf16 with fp32 accumulation; fp32
 // operands (S, dS) enter as hi+lo bf16 pairs so they keep ~fp32 precision.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -36,10 +37,16 @@ struct RouterTables {
 
 __global__ __launch_bounds__(1024) void router_kernel(const int64_t *seg_off, const int32_t *seg_ad,
                                                      int nseg, int m, const lora_adapter *adapters,
-                                                     int nad, int r_cap, RouterTables T) {
+                                                     int nad, int r_cap, RouterTables T, int32_t *ad_items) {
     __shared__ int sc[3][1024];
     const int tid = threadIdx.x;
     int carry[3] = {0, 0, 0};
+    // work items of each adapter in the backward table (table 1), for the
+    // fused per-adapter sums of the dA kernel
+    if (ad_items != nullptr) {
+        for (int i = tid; i < nad; i += 1024) ad_items[i] = 0;
+        __syncthreads();
+    }
     for (int base = 0; base < nseg; base += 1024) {
         const int s = base + tid;
         int lo = 0, hi = 0, a = -1, nq[3] = {0, 0, 0};
@@ -58,6 +65,7 @@ __global__ __launch_bounds__(1024) void router_kernel(const int64_t *seg_off, co
                 for (int j = 0; j < 3; ++j)
                     nq[j] = T.tab[j].rows > 0 ? (hi - lo + T.tab[j].rows - 1) / T.tab[j].rows : 0;
         }
+        if (ad_items != nullptr && nq[1] > 0) atomicAdd(&ad_items[a], nq[1]);
 #pragma unroll
         for (int j = 0; j < 3; ++j) sc[j][tid] = nq[j];
         __syncthreads();
@@ -1003,6 +1011,297 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
     }
 }
 
+// ----- B2, one pass over X for ranks up to 128.
+// Work-group = one work item (rows of one adapter) x 256 columns of k, all
+// ranks at once (16 * MAXT of them).  Rows go in sub-blocks of 32 through a
+// 3- or 4-stage ring of direct-to-LDS loads: X (32 x 256 bf16, swizzled 512-byte
+// rows), the rows' mask words (32 x 8 words) and their dS (32 x RPT fp32).
+// Wave w owns the 16-column blocks 4w .. 4w+3 and accumulates
+// (s*keep.X)^T dS for them over all the item's rows, then writes its part of
+// the item's partial; dA_reduce_kernel adds the partials of each adapter.
+// The rank-side operand (s*dS split into bf16 hi + lo) is the same for all
+// four waves: up to 32 ranks each wave splits it itself; above that the four
+// waves split a quarter each into a shared LDS tile (one more barrier per
+// sub-block), which the MFMAs then read with transposing LDS reads.
+struct B2WParams {
+    const uint16_t *X;
+    const uint32_t *keep;
+    const float *dS;
+    int m, k, RS, KW;
+    RowWork work;   // work items: the router's backward table, or rows_per_chunk rows
+    int nct;        // column tiles of 256
+    float *part;    // [item][nct][256][RPT]
+};
+
+template <int MAXT>
+struct B2W {
+    static constexpr int RPT = 16 * MAXT;                  // ranks per partial row
+    static constexpr int NA = 1 + (32 * RPT * 4) / 1024;   // aux 1 KiB loads: mask, then dS
+    static constexpr int NPW = (NA + 3) / 4;               // aux loads per wave (the rest hit a dummy slot)
+    static constexpr int X_BYTES = 32 * 512;
+    static constexpr int STAGE = X_BYTES + 4 * NPW * 1024;
+    static constexpr int NST = MAXT == 2 ? 3 : 4;          // ring depth (LDS: 2 WGs per CU up to 32 ranks, else 1)
+    static constexpr bool SPLIT_TILE = MAXT >= 4;           // the shared hi | lo tile (32 x 512 bytes)
+    static constexpr int LDS = NST * STAGE + (SPLIT_TILE ? 32 * 512 : 0);
+};
+
+template <int MAXT>
+__global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
+    using C = B2W<MAXT>;
+    constexpr int RPT = C::RPT;
+    extern __shared__ uint4 b2w_smem[];
+    lds_char *smem = (lds_char *)b2w_smem;
+    lds_char *split = smem + C::NST * C::STAGE;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, li = lane & 15;
+    const int ct = blockIdx.y, k0 = ct * 256;
+
+    int row_lo, row_hi;
+    AdapterView ad;
+    if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
+    const int r = ad.r;
+    const int nbt = (r + 15) >> 4;
+    const float s = drop_scale(ad.p);
+    const int nrows = row_hi - row_lo;
+    const int nsb = (nrows + 31) / 32;
+    const bool has_mask = P.keep != nullptr;
+    auto clampb = [](uint64_t v) { return (uint32_t)(v < 0x7FFFFFF0ull ? v : 0x7FFFFFF0ull); };
+    const sgpr4_t dX = make_desc(P.X + (size_t)row_lo * P.k, clampb((uint64_t)nrows * P.k * 2));
+    const sgpr4_t dK = make_desc(has_mask ? P.keep + (size_t)row_lo * P.KW : P.keep,
+                                 has_mask ? clampb((uint64_t)nrows * P.KW * 4) : 0u);
+    const sgpr4_t dD = make_desc(P.dS + (size_t)row_lo * P.RS, clampb((uint64_t)nrows * P.RS * 4));
+
+    // this lane's X offsets inside sub-block 0 (4 loads of 2 rows x 512 bytes)
+    uint32_t offX[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rr = 2 * (4 * wave + j) + (lane >> 5);
+        const int col = k0 + 8 * ((lane & 31) ^ swz512(rr));
+        offX[j] = col < P.k ? (uint32_t)(((size_t)rr * P.k + col) * 2) : kOOBL;
+    }
+    // aux slot q: 0 = mask words (row lane/2, words 4 (lane&1) .. +3 of the
+    // tile), 1 .. NA-1 = dS floats [(q-1) * 256 + 4 lane, +4) of the 32 x RPT
+    // block (row-major, ranks past r or RS read zeros); slots past NA are
+    // dummies loading zeros into the stage's spare kibibytes
+    auto issue = [&](int sb, int stage) {
+        const uint32_t base = lds0 + stage * C::STAGE;
+        const bool live = sb < nsb;
+        const uint32_t xo = (uint32_t)((size_t)sb * 32 * P.k * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            dma16(dX, (live && offX[j] != kOOBL) ? offX[j] + xo : kOOBL, base + (4 * wave + j) * 1024);
+#pragma unroll
+        for (int q0 = 0; q0 < C::NPW; ++q0) {
+            const int q = wave * C::NPW + q0;
+            const uint32_t dst = base + C::X_BYTES + q * 1024;
+            uint32_t off = kOOBL;
+            if (q == 0) {
+                const int w0 = (k0 >> 5) + 4 * (lane & 1);
+                const int row = sb * 32 + (lane >> 1);
+                if (live && has_mask && w0 < P.KW && row < nrows) off = (uint32_t)(((size_t)row * P.KW + w0) * 4);
+            } else if (q < C::NA) {
+                const int f = (q - 1) * 256 + 4 * lane;
+                const int row = sb * 32 + f / RPT, col = f % RPT;
+                if (live && row < nrows && col < r && col < P.RS) off = (uint32_t)(((size_t)row * P.RS + col) * 4);
+            }
+            dma16(q == 0 ? dK : dD, off, dst);
+        }
+    };
+    // the shared tile: rows 8w .. 8w+7 of the sub-block's s*dS, split; lane l
+    // takes row 8w + l/8 and ranks RPL*(l%8) .. +RPL-1; hi parts go to columns
+    // 0 .. RPT-1 of the 512-byte tile row, lo parts to RPT .. 2RPT-1
+    auto coop_split = [&](const float *ds) {
+        constexpr int RPL = RPT / 8;
+        const int row = 8 * wave + (lane >> 3), c0 = RPL * (lane & 7);
+#pragma unroll
+        for (int h = 0; h < RPL; h += 8) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = s * ds[row * RPT + c0 + h + e];
+            uint4 hi, lo;
+            split_frag(v, hi, lo);
+            *(uint4 *)(split + swz512_off(row, (c0 + h) >> 3)) = hi;
+            *(uint4 *)(split + swz512_off(row, (RPT + c0 + h) >> 3)) = lo;
+        }
+    };
+
+    // The main loop is instantiated per number of 16-rank blocks the chunk's
+    // adapter needs (1, 2, 4 or 8, at most MAXT), so the MFMA stream has no
+    // per-block branches and the accumulators stay in fixed registers.
+    constexpr int NPS = 4 + C::NPW;  // loads per wave per stage
+    auto body = [&](auto nb_c) {
+        constexpr int NB = decltype(nb_c)::value;
+        constexpr bool SHARED = C::SPLIT_TILE && NB >= 4;
+        f32x4_t acc[4][NB];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < NB; ++y) acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < C::NST - 1; ++q) issue(q, q);
+        wait_vmcnt<NPS * (C::NST - 2)>();
+        __syncthreads();
+        int stage = 0, lstage = C::NST - 1;
+        for (int sb = 0; sb < nsb; ++sb) {
+            issue(sb + C::NST - 1, lstage);
+            const lds_char *xt = smem + stage * C::STAGE;
+            const uint32_t *mk = (const uint32_t *)(xt + C::X_BYTES);
+            const float *ds = (const float *)(xt + C::X_BYTES + 1024);
+            // dS operand (N = rank): rows 8g .. 8g+7 of rank 16 bt + li, times s
+            uint4 bhi[NB], blo[NB];
+            if constexpr (SHARED) {
+                coop_split(ds);
+                __syncthreads();  // the tile is whole (the last reads of the previous one were before the loop's barrier)
+#pragma unroll
+                for (int bt = 0; bt < NB; ++bt) {
+                    bhi[bt] = tile_rows8(split, 8 * g, bt, lane);
+                    blo[bt] = tile_rows8(split, 8 * g, RPT / 16 + bt, lane);
+                }
+            } else {
+#pragma unroll
+                for (int bt = 0; bt < NB; ++bt) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = s * ds[(8 * g + e) * RPT + 16 * bt + li];
+                    split_frag(v, bhi[bt], blo[bt]);
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int cb = 4 * wave + mb;
+                uint4 xf = tile_rows8(xt, 8 * g, cb, lane);
+                if (has_mask) {
+                    const int bit = 16 * (cb & 1) + li;
+                    uint32_t mm[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t w0 = mk[(8 * g + 2 * q) * 8 + (cb >> 1)];
+                        const uint32_t w1 = mk[(8 * g + 2 * q + 1) * 8 + (cb >> 1)];
+                        mm[q] = (((w0 >> bit) & 1u) ? 0x0000FFFFu : 0u) | (((w1 >> bit) & 1u) ? 0xFFFF0000u : 0u);
+                    }
+                    xf = make_uint4(xf.x & mm[0], xf.y & mm[1], xf.z & mm[2], xf.w & mm[3]);
+                }
+#pragma unroll
+                for (int bt = 0; bt < NB; ++bt) {
+                    acc[mb][bt] = mfma16x16x32(xf, bhi[bt], acc[mb][bt]);
+                    acc[mb][bt] = mfma16x16x32(xf, blo[bt], acc[mb][bt]);
+                }
+            }
+            wait_vmcnt<NPS * (C::NST - 2)>();
+            __syncthreads();
+            stage = stage == C::NST - 1 ? 0 : stage + 1;
+            lstage = lstage == C::NST - 1 ? 0 : lstage + 1;
+        }
+        wait_vmcnt<0>();
+        // this item's partial: columns ct*256 .. +255 of its [nct*256][16 NB]
+        // block (the item's slot holds nct*256*RPT floats)
+        float *pp = P.part + (size_t)blockIdx.x * P.nct * 256 * RPT + (size_t)ct * 256 * (16 * NB);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int bt = 0; bt < NB; ++bt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) pp[((4 * wave + mb) * 16 + 4 * g + v) * (16 * NB) + 16 * bt + li] = acc[mb][bt][v];
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
+    if constexpr (MAXT == 1) {
+        body(I1{});
+    } else if constexpr (MAXT == 2) {
+        if (nbt <= 1) body(I1{});
+        else body(I2{});
+    } else if constexpr (MAXT == 4) {
+        if (nbt <= 1) body(I1{});
+        else if (nbt <= 2) body(I2{});
+        else body(I4{});
+    } else {
+        if (nbt <= 1) body(I1{});
+        else if (nbt <= 2) body(I2{});
+        else if (nbt <= 4) body(I4{});
+        else body(I8{});
+    }
+}
+
+// dA of every adapter from the single-pass kernel's partials: an item of
+// adapter a holds a [columns][RPa] block, RPa = 16 * (1, 2, 4 or 8, the
+// 16-rank blocks its pass ran).  Thread t of work-group (x, a) owns float4
+// 256 x + t of that block and adds that float4 of each of a's work items in
+// work-item order (8 items' loads in flight at a time); adapters without
+// rows get zeros.  Work-groups past an adapter's block exit at once.
+struct DAReduceParams {
+    const float *part;
+    int k, nct, RPT;
+    RowWork work;
+    int items;                // single: number of items; multi: the table's capacity
+    const int32_t *ad_items;  // multi: the router's per-adapter item counts
+};
+
+__global__ __launch_bounds__(256) void da_reduce_kernel(DAReduceParams P) {
+    __shared__ int s_ad[1024];
+    const int a = blockIdx.y;
+    const bool single = P.work.chunks == nullptr;
+    AdapterView ad;
+    int cnt;
+    if (single) {
+        ad = P.work.single;
+        cnt = P.items;
+    } else {
+        ad = load_adapter(P.work.adapters, a);
+        cnt = P.ad_items[a];
+    }
+    const int r = ad.r;
+    if (r < 1 || r > P.work.r_cap || ad.dA == nullptr) return;  // uniform over the work-group
+    const int nbt = (r + 15) >> 4;
+    const int rpa = 16 * (nbt <= 1 ? 1 : nbt <= 2 ? 2 : nbt <= 4 ? 4 : 8);
+    if ((size_t)blockIdx.x * 256 * 4 >= (size_t)P.k * rpa) return;  // past this adapter's block
+    const int f = blockIdx.x * 256 + threadIdx.x;
+    const int col = 4 * f / rpa, r0 = 4 * f % rpa;
+    const bool active = col < P.k && r0 < r;
+    const size_t istride = (size_t)P.nct * 256 * P.RPT / 4;  // float4s per item slot
+    const float4 *src = (const float4 *)P.part + f;
+    const int nit = cnt <= 0 ? 0 : single ? P.items : min(P.work.chunk_count[0], P.items);
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    // the work items' adapters, a window of up to 1024 at a time in LDS; each
+    // thread walks the window in order and loads 8 of a's items at once
+    for (int base = 0; base < nit; base += 1024) {
+        const int nw = min(1024, nit - base);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nw; i += 256) s_ad[i] = single ? a : P.work.chunks[base + i].adapter;
+        __syncthreads();
+        int i = 0;
+        while (i < nw) {
+            int id[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                while (i < nw && s_ad[i] != a) ++i;
+                id[u] = i < nw ? base + i : -1;
+                if (i < nw) ++i;
+            }
+            float4 t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                t[u] = (active && id[u] >= 0) ? src[(size_t)id[u] * istride] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                sum.x += t[u].x;
+                sum.y += t[u].y;
+                sum.z += t[u].z;
+                sum.w += t[u].w;
+            }
+        }
+    }
+    if (!active) return;
+    const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+    uint16_t *dst = ad.dA + (size_t)col * r + r0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (r0 + e < r) dst[e] = (uint16_t)f32_to_bf16_rne(v[e]);
+}
+
 // ----- B1 streaming (ranks <= 32 per rank tile).  Work-group = one row group
 // (rows of one adapter) x C1 = 256*CW columns; rows go in sub-blocks of 32
 // through a 3-stage ring of direct-to-LDS loads (dY as CW swizzled 256-column
@@ -1328,7 +1627,8 @@ static hipError_t finish_launch(int slot, hipStream_t stream) {
 hipError_t launch_router(const int64_t *seg_off, const int32_t *seg_adapter, int nseg, int m,
                          const lora_adapter *adapters, int nad, int r_cap, ChunkEntry *t_f1,
                          int32_t *c_f1, int cap_f1, ChunkEntry *t_bwd, int32_t *c_bwd, int rows_bwd, int cap_bwd,
-                         ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream) {
+                         ChunkEntry *t_b1, int32_t *c_b1, int rows_b1, int cap_b1, hipStream_t stream,
+                         int32_t *ad_items) {
     RouterTables T;
     T.tab[0] = RouterTable{t_f1, c_f1, kF1Rows, cap_f1};
     T.tab[1] = RouterTable{t_bwd, c_bwd, rows_bwd, cap_bwd};
@@ -1336,7 +1636,7 @@ hipError_t launch_router(const int64_t *seg_off, const int32_t *seg_adapter, int
     (void)hipGetLastError();
     const int slot = prof_begin("router", stream);
     hipLaunchKernelGGL(router_kernel, dim3(1), dim3(1024), 0, stream, seg_off, seg_adapter, nseg, m,
-                       adapters, nad, r_cap, T);
+                       adapters, nad, r_cap, T, ad_items);
     return finish_launch(slot, stream);
 }
 
@@ -1509,6 +1809,49 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
     return finish_launch(slot, stream);
 }
 
+hipError_t launch_b2w(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS, int rows,
+                      const AdapterSource &src, int items, float *part, const int32_t *ad_items, hipStream_t stream) {
+    B2WParams P;
+    P.X = (const uint16_t *)X;
+    P.keep = keep;
+    P.dS = dS;
+    P.m = m;
+    P.k = k;
+    P.RS = RS;
+    P.KW = (k + 31) / 32;
+    P.work = make_work(src, kTabBwd);
+    P.work.rows_per_chunk = rows;
+    P.nct = cdiv(k, 256);
+    P.part = part;
+    const int mt = b2w_blocks(r_lds_of(src));
+    (void)hipGetLastError();
+    if (items > 0 && m > 0) {
+        const dim3 grid((unsigned)items, (unsigned)P.nct);
+        const int slot = prof_begin("b2_da", stream);
+        switch (mt) {
+        case 1: launch_with_lds(b2w_kernel<1>, grid, (size_t)B2W<1>::LDS, stream, P); break;
+        case 2: launch_with_lds(b2w_kernel<2>, grid, (size_t)B2W<2>::LDS, stream, P); break;
+        case 4: launch_with_lds(b2w_kernel<4>, grid, (size_t)B2W<4>::LDS, stream, P); break;
+        default: launch_with_lds(b2w_kernel<8>, grid, (size_t)B2W<8>::LDS, stream, P); break;
+        }
+        const hipError_t e = finish_launch(slot, stream);
+        if (e != hipSuccess) return e;
+    }
+    DAReduceParams R;
+    R.part = part;
+    R.k = k;
+    R.nct = P.nct;
+    R.RPT = 16 * mt;
+    R.work = P.work;
+    R.items = src.table ? items : (m > 0 ? items : 0);
+    R.ad_items = ad_items;
+    const int nad = src.table ? src.num_adapters : 1;
+    const size_t f4 = (size_t)P.nct * 256 * R.RPT / 4;
+    const int slot = prof_begin("reduce_da", stream);
+    hipLaunchKernelGGL(da_reduce_kernel, dim3((unsigned)((f4 + 255) / 256), (unsigned)nad), dim3(256), 0, stream, R);
+    return finish_launch(slot, stream);
+}
+
 static GradReduceParams grad_params(int which, const float *part, int m, int k, int n, int RS,
                                     const AdapterSource &src, int rows, int slots) {
     GradReduceParams P;
@@ -1552,7 +1895,7 @@ hipError_t launch_b1_reduce(const float *dSpart, int nparts, float *dS, const fl
     P.db = grad_params(0, dBpart, m, 0, n, RS, src, rows, slots);
     P.db_gx = grad_gx(0, 0, n, RS);
     const int nad = src.table ? src.num_adapters : 1;
-    const size_t blocks = (size_t)P.ds_blocks + (size_t)P.db_gx * nad;
+    const size_t blocks = std::max<size_t>(1, (size_t)P.ds_blocks + (size_t)P.db_gx * nad);
     if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
     (void)hipGetLastError();
     const int slot = prof_begin("reduce_ds_db", stream);
