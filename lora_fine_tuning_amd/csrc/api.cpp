@@ -219,33 +219,39 @@ struct FwdPlan {
     int RS;
     int chunk_cap_f1;  // grid size of F1 (upper bound on chunks)
     int chunk_cap_bwd;
+    bool f1w;          // ranks 33..128: 64-row chunks sharing A, k in KS slices
     int KS, ksl;
     int s2_rp;  // > 0: F1 writes alpha*S as bf16 hi | lo rows of 2*s2_rp for the GEMM's extra K
     size_t off_spart, off_s2, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
     size_t bytes;
 };
 
-// For ranks up to 32 F1 covers all of k inside each work-group (KS = 1).
-// Larger ranks split k into KS slices (multiples of its 128-column staging
-// slice) so the grid has about 1024 work-groups; partials are summed by a
-// second pass.
+// Ranks up to 32: F1 covers all of k inside each work-group (KS = 1).
+// Ranks 33..128: 64-row chunks share A, and k is cut into KS slices
+// (multiples of 128 columns) so the grid has about 512 work-groups; the
+// slices' partials are added by a second launch.  Larger ranks: k in slices
+// too (about 1024 work-groups), partials summed by a second pass.  KS depends
+// on m and k only, so one segment of the mixed form slices as the single
+// form does.
 FwdPlan plan_fwd(int64_t m, int64_t k, int32_t RS, bool multi, int32_t nseg) {
     FwdPlan p{};
     p.RS = RS;
     p.chunk_cap_f1 = cdiv(m, kF1Rows) + (multi ? nseg : 0);
     p.chunk_cap_bwd = cdiv(m, kBwdRows) + (multi ? nseg : 0);
+    const int rl = ((RS + 15) / 16) * 16;
+    p.f1w = f1w_ok(rl, k);
     const int kslices = cdiv(k, kF1KSub);
-    int KS = std::max(1, std::min(kslices, cdiv(1024, std::max(1, p.chunk_cap_f1))));
-    if (f1_streaming(((RS + 15) / 16) * 16, k)) KS = 1;
+    int KS = std::max(1, std::min(kslices, cdiv(p.f1w ? 512 : 1024, std::max(1, cdiv(m, kF1Rows)))));
+    if (!p.f1w && f1_streaming(rl, k)) KS = 1;
     const int per = cdiv(kslices, KS);
     p.ksl = per * kF1KSub;
     p.KS = cdiv(k, p.ksl);
-    // single adapter, ranks 33..128 (streaming F1): the up-projection runs as
-    // extra K columns of the forward GEMM, fed by F1's split of alpha*S
-    const int rl = ((RS + 15) / 16) * 16;
-    p.s2_rp = (!multi && rl > 32 && p.KS == 1) ? rank_tiles(rl) * 32 : 0;
+    // single adapter, ranks 33..128: the up-projection runs as extra K
+    // columns of the forward GEMM, fed by F1's split of alpha*S
+    p.s2_rp = (!multi && p.f1w) ? rank_tiles(rl) * 32 : 0;
+    const size_t part_w = p.f1w ? (size_t)16 * f1w_blocks(rl) : (size_t)RS;
     Carve c;
-    p.off_spart = c.take(p.KS > 1 ? (size_t)p.KS * m * RS * sizeof(float) : 0);
+    p.off_spart = c.take(p.KS > 1 ? (size_t)p.KS * m * part_w * sizeof(float) : 0);
     p.off_s2 = c.take((size_t)m * 2 * p.s2_rp * sizeof(uint16_t));
     if (multi) {
         p.off_t_f1 = c.take((size_t)p.chunk_cap_f1 * sizeof(ChunkEntry));
@@ -368,14 +374,20 @@ extern "C" lora_status lora_linear_fwd(const void *X, const void *W, const void 
     if (pl.bytes) REQ_PTR(workspace, 16);
 
     AdapterSource src = single_source(A, B, nullptr, nullptr, r, alpha, p);
-    float *sout = pl.KS > 1 ? (float *)ws_at(workspace, pl.off_spart) : S;
+    float *spart = (float *)ws_at(workspace, pl.off_spart);
     // the extra-K form needs B's rows 16-byte aligned (n % 8 == 0 is checked above)
     uint16_t *s2 = (pl.s2_rp > 0 && aligned(B, 16)) ? (uint16_t *)ws_at(workspace, pl.off_s2) : nullptr;
-    HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r, pl.KS,
-                     pl.ksl, stream, s2, pl.s2_rp), "F1 launch");
-    if (pl.KS > 1)
-        HIPCHK(launch_sum_partials(sout, pl.KS, (size_t)m * r, (size_t)m * r, S, "sum_s_partials", stream),
-               "S reduction launch");
+    if (pl.f1w) {
+        HIPCHK(launch_f1w(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, S, r, spart, pl.KS,
+                          pl.ksl, stream, s2, pl.s2_rp), "F1 launch");
+    } else {
+        float *sout = pl.KS > 1 ? spart : S;
+        HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r, pl.KS,
+                         pl.ksl, stream), "F1 launch");
+        if (pl.KS > 1)
+            HIPCHK(launch_sum_partials(sout, pl.KS, (size_t)m * r, (size_t)m * r, S, "sum_s_partials", stream),
+                   "S reduction launch");
+    }
     if (s2)
         HIPCHK(launch_gemm_kext(X, W, Y, (int)m, (int)n, (int)k, s2, 2 * pl.s2_rp, B, r, stream), "F2 launch");
     else
@@ -508,12 +520,18 @@ extern "C" lora_status multi_lora_linear_fwd(const void *X, const void *W, const
                          (ChunkEntry *)src.chunks_bwd, (int32_t *)src.count_bwd, kBwdRows, pl.chunk_cap_bwd,
                          nullptr, nullptr, 0, 0, stream),
            "router launch");
-    float *sout = pl.KS > 1 ? (float *)ws_at(workspace, pl.off_spart) : S;
-    HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r_max, pl.KS,
-                     pl.ksl, stream), "F1 launch");
-    if (pl.KS > 1)
-        HIPCHK(launch_sum_partials(sout, pl.KS, (size_t)m * r_max, (size_t)m * r_max, S, "sum_s_partials",
-                                   stream), "S reduction launch");
+    float *spart = (float *)ws_at(workspace, pl.off_spart);
+    if (pl.f1w) {
+        HIPCHK(launch_f1w(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, S, r_max, spart,
+                          pl.KS, pl.ksl, stream), "F1 launch");
+    } else {
+        float *sout = pl.KS > 1 ? spart : S;
+        HIPCHK(launch_f1(X, (int)m, (int)k, src, pl.chunk_cap_f1, seed, offset, keep_bits, sout, r_max, pl.KS,
+                         pl.ksl, stream), "F1 launch");
+        if (pl.KS > 1)
+            HIPCHK(launch_sum_partials(sout, pl.KS, (size_t)m * r_max, (size_t)m * r_max, S, "sum_s_partials",
+                                       stream), "S reduction launch");
+    }
     HIPCHK(launch_gemm(true, 1, X, W, Y, (int)m, (int)n, (int)k, S, r_max, nullptr, 0, src, stream), "F2 launch");
     return LORA_OK;
 }

@@ -94,6 +94,16 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
                      uint64_t seed, uint64_t offset, uint32_t *keep_bits, float *out, int RS,
                      int KS, int ksl, hipStream_t stream, uint16_t *s2 = nullptr, int s2_rp = 0);
 
+// F1 for 32 < r_lds <= 128: 64-row chunks sharing A, k in KS slices of ksl
+// columns (multiples of 128); with KS > 1 the slices' partials ([KS][m][16 *
+// f1w_blocks] fp32) are added by a second launch, which also writes the
+// forward GEMM's split of alpha*S when s2 is given.
+inline int f1w_blocks(int r_lds) { return r_lds <= 64 ? 4 : 8; }
+inline bool f1w_ok(int r_lds, int64_t k) { return r_lds > 32 && r_lds <= 128 && k * 64 < (int64_t(1) << 31); }
+hipError_t launch_f1w(const void *X, int m, int k, const AdapterSource &src, int chunk_cap, uint64_t seed,
+                      uint64_t offset, uint32_t *keep_bits, float *S, int RS, float *part, int KS, int ksl,
+                      hipStream_t stream, uint16_t *s2 = nullptr, int s2_rp = 0);
+
 hipError_t launch_sum_partials(const float *part, int nparts, size_t part_stride, size_t count,
                                float *out, const char *name, hipStream_t stream);
 

@@ -481,6 +481,281 @@ __global__ __launch_bounds__(64 * F1S_WAVES) void f1s_kernel(F1Params P) {
     }
 }
 
+// ----- F1 for ranks 33..128: one pass over X, A shared by 64 rows.
+// Work-group = a 64-row chunk of one adapter (4 waves x 16 rows) x one slice
+// of k.  Each 64-column unit of the slice -- the 64 rows of X (8 KiB) and A's
+// 64 k-rows (64 x RP bf16) -- comes through a 3-stage ring of direct-to-LDS
+// loads, so A is read once per 64 rows and every wave uses it (the small
+// unit keeps two or three work-groups on a CU).
+// Per 32-column step a lane hashes one Philox block for its row, masks its 8
+// elements, and runs one MFMA per 16-rank block the chunk's adapter needs
+// (the step is instantiated for 1, 2, 4 or 8 blocks).  The mask words are
+// assembled across the lanes of a row (4 x 4 byte transpose) and stored by
+// the slice that hashed them.  With one slice S (and the forward GEMM's hi |
+// lo split of alpha*S) leaves the kernel; with several, each writes its
+// partial and f1_reduce_kernel adds them in slice order.
+struct F1WParams {
+    const uint16_t *X;
+    int m, k;
+    RowWork work;  // 64-row chunks
+    uint64_t seed, offset;
+    uint32_t *keep_bits;
+    int KW;
+    float *S;
+    int RS;
+    float *part;  // several slices: [KS][m][RP], S before the dropout scale
+    int ksl, KS;
+    uint16_t *s2;  // one slice only (else f1_reduce_kernel writes it)
+    int s2_rp;
+};
+
+template <int MAXT>
+struct F1W {
+    static constexpr int RP = 16 * MAXT;
+    static constexpr int UNIT = 64;                 // k columns per stage (two MFMA steps)
+    static constexpr int X_BYTES = 64 * UNIT * 2;   // 64 rows
+    static constexpr int A_BYTES = UNIT * RP * 2;   // UNIT k-rows x RP ranks
+    static constexpr int STAGE = X_BYTES + A_BYTES;
+    static constexpr int NST = 3;
+    static constexpr int LDS = NST * STAGE;         // 2 work-groups per CU at RP = 128, 3 below
+    static constexpr int NAL = A_BYTES / 4096;      // A loads (1 KiB) per wave per stage
+    static constexpr int NPS = 2 + NAL;             // loads per wave per stage
+};
+
+// 32-byte chunk swizzle of A's slab rows (2*RP bytes): the 4 k-rows of a
+// transposing read, and those 8 k-rows further on, land on distinct chunks.
+template <int RP>
+__device__ __forceinline__ int f1w_swz(int kr) {
+    return ((kr & 3) | (((kr >> 3) & 1) << 2)) & (RP / 16 - 1);
+}
+
+template <int MAXT>
+__global__ __launch_bounds__(256) void f1w_kernel(F1WParams P) {
+    using C = F1W<MAXT>;
+    constexpr int RP = C::RP;
+    extern __shared__ uint4 f1w_smem[];
+    lds_char *smem = (lds_char *)f1w_smem;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+
+    int row_lo, row_hi;
+    AdapterView ad;
+    if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
+    const int r = ad.r;
+    const int nbt = (r + 15) >> 4;
+    const int ks = blockIdx.y, kb = ks * P.ksl, ke = min(P.k, kb + P.ksl);
+    if (kb >= ke) return;
+    const int nu = (ke - kb + C::UNIT - 1) / C::UNIT;
+    const int nrows = row_hi - row_lo;
+    const uint32_t T = drop_threshold(ad.p);
+    const uint32_t tm1x2 = ((T - 1u) & 0xFFFFu) * 0x00010001u;  // used only when T >= 1
+    const float s = drop_scale(ad.p);
+    auto clampb = [](uint64_t v) { return (uint32_t)(v < 0x7FFFFFF0ull ? v : 0x7FFFFFF0ull); };
+    const sgpr4_t dX = make_desc(P.X + (size_t)row_lo * P.k, clampb((uint64_t)nrows * P.k * 2));
+    const bool avec = (r & 7) == 0 && (((uintptr_t)ad.A) & 15) == 0;
+    const uint64_t abytes = (uint64_t)P.k * r * 2;
+    const sgpr4_t dA = make_desc(ad.A, clampb(abytes));
+
+    // X: load j of wave w covers rows 16w + 8j + lane/8, 16-byte chunk
+    // position lane%8 of the 128-byte LDS row, which holds logical chunk
+    // (lane%8) ^ (row/2 % 8) (16 consecutive rows read at one logical chunk
+    // hit 16 distinct bank groups)
+    constexpr int UNIT = C::UNIT;
+    uint32_t offX[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        offX[j] = (16 * wave + row < nrows) ? (uint32_t)(((size_t)(16 * wave + row) * P.k + 8 * c) * 2) : kOOBL;
+    }
+    auto issue = [&](int u, int st) {
+        const uint32_t base = lds0 + st * C::STAGE;
+        const int c0 = kb + UNIT * u;
+        const bool live = u < nu;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 8 * j + (lane >> 3);
+            const int c = (lane & 7) ^ ((row >> 1) & 7);
+            const bool ok = live && offX[j] != kOOBL && c0 + 8 * c < ke;
+            dma16(dX, ok ? offX[j] + (uint32_t)c0 * 2u : kOOBL, base + wave * 2048 + j * 1024);
+        }
+        const uint32_t abase = base + C::X_BYTES;
+        if (avec) {
+#pragma unroll
+            for (int i = 0; i < C::NAL; ++i) {
+                const int q = wave * C::NAL + i;
+                const int pos = q * 1024 + lane * 16;
+                const int kr = pos / (2 * RP), within = pos % (2 * RP);
+                const int cl = (within >> 5) ^ f1w_swz<RP>(kr), h = (within >> 4) & 1;
+                const int rank = 16 * cl + 8 * h;
+                const bool ok = live && c0 + kr < ke && rank < r;
+                dma16(dA, ok ? (uint32_t)(((size_t)(c0 + kr) * r + rank) * 2) : kOOBL, abase + q * 1024);
+            }
+        } else {
+            // A neither 16-byte aligned nor of a rank divisible by 8: element copy
+            lds_char *dst = smem + st * C::STAGE + C::X_BYTES;
+            for (int idx = tid; idx < UNIT * RP; idx += 256) {
+                const int kr = idx / RP, rank = idx % RP;
+                uint16_t v = 0;
+                if (live && c0 + kr < ke && rank < r) v = ad.A[(size_t)(c0 + kr) * r + rank];
+                *(uint16_t *)(dst + kr * (2 * RP) + (((rank >> 4) ^ f1w_swz<RP>(kr)) << 5) + (rank & 15) * 2) = v;
+            }
+        }
+    };
+
+    const int row = row_lo + 16 * wave + l16;
+    const bool rvalid = 16 * wave + l16 < nrows;
+    // Philox block of the lane's first element in a step at column c: (offset
+    // + row*k + c + 8g) / 8, every term a multiple of 8
+    const uint64_t blk0 = (P.offset >> 3) + (uint64_t)(rvalid ? row : row_lo) * (uint64_t)(P.k >> 3) + (uint64_t)g;
+
+    auto body = [&](auto nb_c) {
+        constexpr int NB = decltype(nb_c)::value;
+        f32x4_t acc[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < C::NST - 1; ++q) issue(q, q);
+        wait_vmcnt<C::NPS * (C::NST - 2)>();
+        __syncthreads();
+        int st = 0, ls = C::NST - 1;
+        uint32_t kw = 0;  // byte t: this lane's keep bits of step t of the 128-column pair of units
+        for (int u = 0; u < nu; ++u) {
+            issue(u + C::NST - 1, ls);
+            const lds_char *xt = smem + st * C::STAGE + wave * 2048;
+            const lds_char *at = smem + st * C::STAGE + C::X_BYTES;
+            const int c = kb + UNIT * u;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint4 x = *(const uint4 *)(xt + l16 * 128 + (((4 * t + g) ^ ((l16 >> 1) & 7)) << 4));
+                uint4 xm = x;
+                uint32_t byte = 0xFFu;
+                if (T != 0) {
+                    const PhiloxOut o = philox10(blk0 + (uint64_t)((c + 32 * t) >> 3), P.seed);
+                    byte = keep_and_mask(o, tm1x2, x, xm);
+                }
+                kw |= (c + 32 * t + 8 * g < ke ? byte : 0u) << (8 * (2 * (u & 1) + t));  // bits past the slice stay zero
+                const int kr = 32 * t + 8 * g + (l16 >> 2);
+                const int sw = f1w_swz<RP>(kr);
+#pragma unroll
+                for (int bt = 0; bt < NB; ++bt) {
+                    const lds_char *pa = at + kr * (2 * RP) + ((bt ^ sw) << 5) + 8 * (l16 & 3);
+                    const uint2 lo = lds_read_tr4(pa), hi = lds_read_tr4(pa + 4 * (2 * RP));
+                    acc[bt] = mfma16x16x32(xm, make_uint4(lo.x, lo.y, hi.x, hi.y), acc[bt]);
+                }
+            }
+            if (P.keep_bits != nullptr && ((u & 1) || u == nu - 1)) {
+                const int c = kb + UNIT * (u & ~1);  // first column of the pair
+                // 4x4 byte transpose across the lanes of a row (groups g):
+                // afterwards lane g holds the word of step g, byte j from group j
+                const uint32_t p1 = (uint32_t)__shfl_xor((int)kw, 16);
+                kw = (g & 1) ? ((kw & 0xFF00FF00u) | ((p1 & 0xFF00FF00u) >> 8))
+                             : ((kw & 0x00FF00FFu) | ((p1 & 0x00FF00FFu) << 8));
+                const uint32_t p2 = (uint32_t)__shfl_xor((int)kw, 32);
+                kw = (g & 2) ? ((kw & 0xFFFF0000u) | (p2 >> 16)) : ((kw & 0x0000FFFFu) | (p2 << 16));
+                if (rvalid && c + 32 * g < ke) P.keep_bits[(size_t)row * P.KW + ((c >> 5) + g)] = kw;
+                kw = 0;
+            }
+            wait_vmcnt<C::NPS * (C::NST - 2)>();
+            __syncthreads();
+            st = st == C::NST - 1 ? 0 : st + 1;
+            ls = ls == C::NST - 1 ? 0 : ls + 1;
+        }
+        wait_vmcnt<0>();
+        // rows 4g + v of the wave, rank 16 bt + l16
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int lr = 16 * wave + 4 * g + v;
+            if (lr >= nrows) continue;
+            const int orow = row_lo + lr;
+            if (P.KS == 1) {
+                for (int rr = l16; rr < P.RS; rr += 16) {
+                    float val = 0.f;
+#pragma unroll
+                    for (int bt = 0; bt < NB; ++bt)
+                        if (rr == 16 * bt + l16 && rr < r) val = acc[bt][v] * s;
+                    P.S[(size_t)orow * P.RS + rr] = val;
+                }
+                if (P.s2 != nullptr) {
+                    for (int rr = l16; rr < P.s2_rp; rr += 16) {
+                        float val = 0.f;
+#pragma unroll
+                        for (int bt = 0; bt < NB; ++bt)
+                            if (rr == 16 * bt + l16 && rr < r) val = acc[bt][v] * s;
+                        uint32_t hi, lo;
+                        split_bf16(ad.alpha * val, hi, lo);
+                        uint16_t *q = P.s2 + (size_t)orow * (2 * P.s2_rp) + rr;
+                        q[0] = (uint16_t)hi;
+                        q[P.s2_rp] = (uint16_t)lo;
+                    }
+                }
+            } else {
+                float *pp = P.part + ((size_t)ks * P.m + orow) * RP;
+#pragma unroll
+                for (int bt = 0; bt < MAXT; ++bt) {
+                    float val = 0.f;
+#pragma unroll
+                    for (int b2 = 0; b2 < NB; ++b2)
+                        if (b2 == bt) val = acc[b2][v];
+                    pp[16 * bt + l16] = val;
+                }
+            }
+        }
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
+    if constexpr (MAXT == 4) {
+        if (nbt <= 1) body(I1{});
+        else if (nbt <= 2) body(I2{});
+        else body(I4{});
+    } else {
+        if (nbt <= 1) body(I1{});
+        else if (nbt <= 2) body(I2{});
+        else if (nbt <= 4) body(I4{});
+        else body(I8{});
+    }
+}
+
+// S (and the forward GEMM's split of alpha*S) from f1w_kernel's slice
+// partials, added in slice order; one work-group per 64-row chunk.
+__global__ __launch_bounds__(256) void f1_reduce_kernel(F1WParams P, int RP) {
+    int row_lo, row_hi;
+    AdapterView ad;
+    if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
+    const int r = ad.r;
+    const float s = drop_scale(ad.p);
+    const int nrows = row_hi - row_lo;
+    const int width = max(P.RS, P.s2 != nullptr ? P.s2_rp : 0);
+    const int e = blockIdx.y * 256 + threadIdx.x;  // one output element per thread
+    if (e >= nrows * width) return;
+    const int lr = e / width, rr = e - lr * width;
+    const int orow = row_lo + lr;
+    float v = 0.f;
+    if (rr < r) {
+        const float *src = P.part + (size_t)orow * RP + rr;
+        const size_t qs = (size_t)P.m * RP;
+        int q = 0;
+        for (; q + 4 <= P.KS; q += 4) {
+            const float a0 = src[q * qs], a1 = src[(q + 1) * qs], a2 = src[(q + 2) * qs], a3 = src[(q + 3) * qs];
+            v = (((v + a0) + a1) + a2) + a3;
+        }
+        for (; q < P.KS; ++q) v += src[q * qs];
+        v *= s;
+    }
+    if (rr < P.RS) P.S[(size_t)orow * P.RS + rr] = v;
+    if (P.s2 != nullptr && rr < P.s2_rp) {
+        uint32_t hi, lo;
+        split_bf16(ad.alpha * v, hi, lo);
+        uint16_t *q2 = P.s2 + (size_t)orow * (2 * P.s2_rp) + rr;
+        q2[0] = (uint16_t)hi;
+        q2[P.s2_rp] = (uint16_t)lo;
+    }
+}
+
 // ===========================================================================
 // Fixed-order sum of split partials: out[i] = sum_p part[p*stride + i].  A
 // work-group covers 64 float4 columns; its four waves each sum every fourth
@@ -1709,6 +1984,40 @@ hipError_t launch_f1(const void *X, int m, int k, const AdapterSource &src, int 
     case 8: launch_with_lds(f1_kernel<8>, grid, lds, stream, P); break;
     default: launch_with_lds(f1_kernel<16>, grid, lds, stream, P); break;
     }
+    return finish_launch(slot, stream);
+}
+
+hipError_t launch_f1w(const void *X, int m, int k, const AdapterSource &src, int chunk_cap, uint64_t seed,
+                      uint64_t offset, uint32_t *keep_bits, float *S, int RS, float *part, int KS, int ksl,
+                      hipStream_t stream, uint16_t *s2, int s2_rp) {
+    F1WParams P;
+    P.X = (const uint16_t *)X;
+    P.m = m;
+    P.k = k;
+    P.work = make_work(src, kTabF1);
+    P.seed = seed;
+    P.offset = offset;
+    P.keep_bits = keep_bits;
+    P.KW = (k + 31) / 32;
+    P.S = S;
+    P.RS = RS;
+    P.part = part;
+    P.ksl = ksl;
+    P.KS = KS;
+    P.s2 = s2;
+    P.s2_rp = s2_rp;
+    const int mt = f1w_blocks(r_lds_of(src));
+    (void)hipGetLastError();
+    int slot = prof_begin("f1_mask_down", stream);
+    const dim3 grid((unsigned)chunk_cap, (unsigned)KS);
+    if (mt == 4) launch_with_lds(f1w_kernel<4>, grid, (size_t)F1W<4>::LDS, stream, P);
+    else launch_with_lds(f1w_kernel<8>, grid, (size_t)F1W<8>::LDS, stream, P);
+    hipError_t e = finish_launch(slot, stream);
+    if (e != hipSuccess || KS == 1) return e;
+    slot = prof_begin("sum_s_partials", stream);
+    const int width = std::max(RS, s2 != nullptr ? s2_rp : 0);
+    hipLaunchKernelGGL(f1_reduce_kernel, dim3((unsigned)chunk_cap, (unsigned)cdiv(kF1Rows * width, 256)), dim3(256), 0,
+                       stream, P, 16 * mt);
     return finish_launch(slot, stream);
 }
 

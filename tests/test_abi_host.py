@@ -201,13 +201,15 @@ def test_workspace_sizes():
     s2 = lf.lora_linear_bwd_workspace_size(16384, 4096, 4096, 16)
     assert 0 < s1 < s2
     # ranks up to 32: F1 finishes S inside each work-group, the GEMM epilogue
-    # reads it: no workspace.  Ranks 33..128: the split alpha*S (bf16 hi | lo,
-    # 2 * 32 * ceil(r / 32) columns) for the GEMM's extra K columns.  Larger
-    # ranks: split-k partials of S.
+    # reads it: no workspace.  Ranks 33..128: F1's k-slice partials of S
+    # (KS slices x m x 64 or 128 fp32; 64-row chunks, about 512 work-groups:
+    # KS = 4 at m = 8192) and the split alpha*S (bf16 hi | lo, 2 * 32 *
+    # ceil(r / 32) columns) for the GEMM's extra K columns.  Larger ranks:
+    # split-k partials of S.
     assert lf.lora_linear_fwd_workspace_size(512, 1024, 1024, 16) == 0
     assert lf.lora_linear_fwd_workspace_size(8192, 4096, 4096, 32) == 0
-    assert lf.lora_linear_fwd_workspace_size(8192, 4096, 4096, 128) == 8192 * 256 * 2
-    assert lf.lora_linear_fwd_workspace_size(8192, 4096, 4096, 48) == 8192 * 128 * 2
+    assert lf.lora_linear_fwd_workspace_size(8192, 4096, 4096, 128) == 4 * 8192 * 128 * 4 + 8192 * 256 * 2
+    assert lf.lora_linear_fwd_workspace_size(8192, 4096, 4096, 48) == 4 * 8192 * 64 * 4 + 8192 * 128 * 2
     assert lf.lora_linear_fwd_workspace_size(512, 1024, 1024, 256) > 0
     assert lf.multi_lora_bwd_workspace_size(8192, 28672, 8192, 128, 8, 8) > \
         lf.lora_linear_bwd_workspace_size(8192, 28672, 8192, 128)
