@@ -1616,11 +1616,13 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     const int sst = P.tiled ? 32 : P.RS;
     float *dsp = P.dSpart + (size_t)ct * P.m * P.RS;
     if (r0 >= r) {
-        // no ranks here: this tile's columns of the dS partial are zero
-        for (int i = tid; i < (row_hi - row_lo) * RL; i += 256) {
-            const int rr = i / RL, cc = r0 + i % RL;
-            if (cc < P.RS) dsp[(size_t)(row_lo + rr) * P.RS + cc] = 0.f;
-        }
+        // no ranks here; with one column tile B1 writes dS itself, whose
+        // columns past r are zero (with several, the finishing sum writes them)
+        if (gridDim.y == 1)
+            for (int i = tid; i < (row_hi - row_lo) * RL; i += 256) {
+                const int rr = i / RL, cc = r0 + i % RL;
+                if (cc < P.RS) dsp[(size_t)(row_lo + rr) * P.RS + cc] = 0.f;
+            }
         return;
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1847,26 +1849,109 @@ __global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceParams P) {
     grad_reduce_block(P, blockIdx.y, blockIdx.x, gridDim.x);
 }
 
-// dS (fixed-order sum of B1's column-tile partials) and dB (per-adapter sum of
-// its row-group partials) in one launch: work-groups [0, ds_blocks) do the
-// former, the rest the latter (db_gx per adapter).
-struct B1ReduceParams {
-    const float *dspart;
+// ===========================================================================
+// B1's finishing sums, one launch.  Work-groups [0, ds_wgs): dS of each row
+// group = the column tiles' partials added in tile order, ranks below the
+// group's adapter rank only (zeros past it up to RS); the rest: dB of each
+// adapter = its row groups' partials added in group order, a float4 per
+// thread with 8 groups' loads in flight (work-groups past the adapter's r x n
+// exit at once; an adapter with no rows gets zeros).
+// ===========================================================================
+struct B1FinishParams {
+    const float *dspart;  // [nparts][m][RS]
     int nparts;
-    size_t stride, count;
     float *ds;
-    int ds_blocks, db_gx;
-    GradReduceParams db;
+    int m, n, RS;
+    const float *dbpart;  // [group][RS][n]
+    RowWork work;         // B1 row groups (router table 2, or rows_per_chunk rows)
+    int groups;           // single: number of row groups; multi: the table's capacity
+    int ds_wpg;           // dS work-groups per row group (0: no dS sum)
+    int db_gx;            // dB work-groups per adapter
 };
 
-__global__ __launch_bounds__(256) void b1_reduce_kernel(B1ReduceParams P) {
-    const int b = blockIdx.x;
-    if (b < P.ds_blocks) {
-        sum_partials_block(P.dspart, P.nparts, P.stride, P.count, P.ds, b);
-    } else {
-        const int q = b - P.ds_blocks;
-        grad_reduce_block(P.db, q / P.db_gx, q % P.db_gx, P.db_gx);
+__global__ __launch_bounds__(256) void b1_finish_kernel(B1FinishParams P) {
+    __shared__ int s_ad[1024];
+    const int tid = threadIdx.x;
+    const bool single = P.work.chunks == nullptr;
+    const int ds_wgs = P.groups * P.ds_wpg;
+    if ((int)blockIdx.x < ds_wgs) {
+        const int grp = blockIdx.x / P.ds_wpg, sub = blockIdx.x - grp * P.ds_wpg;
+        int row_lo, row_hi;
+        AdapterView ad;
+        if (!resolve_chunk(P.work, grp, P.m, row_lo, row_hi, ad)) return;
+        const int r = min(ad.r, P.RS);
+        const size_t ps = (size_t)P.m * P.RS;
+        const int total = (row_hi - row_lo) * P.RS;
+        for (int e = sub * 256 + tid; e < total; e += P.ds_wpg * 256) {
+            const int lr = e / P.RS, rr = e - lr * P.RS;
+            const size_t idx = (size_t)(row_lo + lr) * P.RS + rr;
+            float v = 0.f;
+            if (rr < r) {
+                const float *src = P.dspart + idx;
+                int q = 0;
+                for (; q + 8 <= P.nparts; q += 8) {
+                    float t[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) t[u] = src[(size_t)(q + u) * ps];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) v += t[u];
+                }
+                for (; q < P.nparts; ++q) v += src[(size_t)q * ps];
+            }
+            P.ds[idx] = v;
+        }
+        return;
     }
+    const int y = blockIdx.x - ds_wgs;
+    const int a = y / P.db_gx, bx = y - a * P.db_gx;
+    AdapterView ad;
+    if (single) {
+        if (a != 0) return;
+        ad = P.work.single;
+    } else {
+        if (a >= P.work.num_adapters) return;
+        ad = load_adapter(P.work.adapters, a);
+    }
+    const int r = ad.r;
+    if (r < 1 || r > P.work.r_cap || ad.dB == nullptr) return;
+    if ((size_t)bx * 256 * 4 >= (size_t)r * P.n) return;  // past this adapter's r x n
+    const int f = bx * 256 + tid;
+    const bool active = (size_t)4 * f < (size_t)r * P.n;
+    const size_t gstride = (size_t)P.RS * P.n / 4;  // float4s per group partial
+    const float4 *src = (const float4 *)P.dbpart + f;
+    const int ngr = single ? P.groups : min(P.work.chunk_count[0], P.groups);
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int base = 0; base < ngr; base += 1024) {
+        const int nw = min(1024, ngr - base);
+        __syncthreads();
+        for (int i = tid; i < nw; i += 256) s_ad[i] = single ? a : P.work.chunks[base + i].adapter;
+        __syncthreads();
+        int i = 0;
+        while (i < nw) {
+            int id[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                while (i < nw && s_ad[i] != a) ++i;
+                id[u] = i < nw ? base + i : -1;
+                if (i < nw) ++i;
+            }
+            float4 t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                t[u] = (active && id[u] >= 0) ? src[(size_t)id[u] * gstride] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                sum.x += t[u].x;
+                sum.y += t[u].y;
+                sum.z += t[u].z;
+                sum.w += t[u].w;
+            }
+        }
+    }
+    if (!active) return;
+    const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ad.dB[4 * (size_t)f + e] = (uint16_t)f32_to_bf16_rne(v[e]);
 }
 
 // ===========================================================================
@@ -2194,21 +2279,27 @@ hipError_t launch_grad_reduce(int which, const float *part, int m, int k, int n,
 
 hipError_t launch_b1_reduce(const float *dSpart, int nparts, float *dS, const float *dBpart, int m, int n,
                             int RS, const AdapterSource &src, int rows, int slots, hipStream_t stream) {
-    B1ReduceParams P;
+    B1FinishParams P;
     P.dspart = dSpart;
     P.nparts = nparts;
-    P.stride = (size_t)m * RS;
-    P.count = (size_t)m * RS;
     P.ds = dS;
-    P.ds_blocks = nparts > 1 ? (int)((P.count + 255) / 256) : 0;  // one partial: B1 wrote dS itself
-    P.db = grad_params(0, dBpart, m, 0, n, RS, src, rows, slots);
-    P.db_gx = grad_gx(0, 0, n, RS);
+    P.m = m;
+    P.n = n;
+    P.RS = RS;
+    P.dbpart = dBpart;
+    P.work = make_work(src, kTabB1);
+    P.work.rows_per_chunk = rows;
+    P.groups = src.table ? slots : cdiv(m, rows);
+    // one partial: B1 wrote dS itself.  Otherwise about 4 elements per thread.
+    P.ds_wpg = (nparts > 1 && m > 0) ? std::max(1, cdiv((long)rows * RS, 1024)) : 0;
+    P.db_gx = std::max(1, cdiv((long)RS * n / 4, 256));
     const int nad = src.table ? src.num_adapters : 1;
-    const size_t blocks = std::max<size_t>(1, (size_t)P.ds_blocks + (size_t)P.db_gx * nad);
+    const size_t blocks = (size_t)P.groups * P.ds_wpg + (size_t)P.db_gx * nad;
+    if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
     (void)hipGetLastError();
     const int slot = prof_begin("reduce_ds_db", stream);
-    hipLaunchKernelGGL(b1_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P);
+    hipLaunchKernelGGL(b1_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P);
     return finish_launch(slot, stream);
 }
 
