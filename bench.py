@@ -267,7 +267,7 @@ def config_report(args):
     import torch
 
     import lora_fine_tuning_amd as lf
-    from synth import AdapterSpec, Workload, make_tensors_device, workload
+    from synth import DECODER_PROJECTIONS, decoder_projection, make_tensors_device, workload
 
     lf.load()
     stream = torch.cuda.current_stream()
@@ -343,12 +343,8 @@ def config_report(args):
     # the seven LoRA projections of one LLaMA-8B-shaped decoder layer (q, k, v, o,
     # gate, up, down; m 8192, r 16; synthetic weights, no attention), run back to
     # back as one step
-    proj = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
-            ("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)]
-    layer = []
-    for vi, (nm, kk, nn) in enumerate(proj):
-        wl = Workload(f"{nm} m8192 k{kk} n{nn} r16", 1, 10 + vi, 8192, kk, nn, [AdapterSpec(16, 2.0, 0.1)])
-        layer.append(make_tensors_device(wl, "cuda"))
+    proj = DECODER_PROJECTIONS
+    layer = [make_tensors_device(decoder_projection(vi), "cuda") for vi in range(len(proj))]
 
     def layer_fused():
         for t in layer:

@@ -134,6 +134,31 @@ def workload(config_id: int, variant: int = 0, *, m: Optional[int] = None,
     raise ValueError(f"unknown config {config_id}")
 
 
+# the seven LoRA projections of one LLaMA-8B-shaped decoder layer: name, k, n
+DECODER_PROJECTIONS = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
+                       ("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)]
+
+
+def decoder_projection(index: int, m: int = 8192, r: int = 16) -> Workload:
+    """Projection `index` of DECODER_PROJECTIONS as a single-adapter workload
+    (alpha 2, p 0.1), drawn with variant 10 + index of config 1's seeds."""
+    nm, kk, nn = DECODER_PROJECTIONS[index]
+    return Workload(f"{nm} m{m} k{kk} n{nn} r{r}", 1, 10 + index, m, kk, nn, [AdapterSpec(r, 2.0, 0.1)])
+
+
+def wide_mixed_workload(m: int = 8192) -> Workload:
+    """Four adapters r {8, 200, 13, 128} (alpha 2, 1, 0.5, 2; p 0.1, 0.1, 0.2,
+    0) over k = n 4096 in 6 Dirichlet(1) segments that use the adapters in the
+    order 0 1 2 3 1 2: a batch whose widest adapter exceeds 128 ranks next to
+    one whose rank is not a multiple of 8."""
+    rng = np.random.Generator(np.random.PCG64(2105))
+    seg_off, _ = dirichlet_segments(rng, m, 6)
+    ads = [AdapterSpec(8, 2.0, 0.1), AdapterSpec(200, 1.0, 0.1), AdapterSpec(13, 0.5, 0.2),
+           AdapterSpec(128, 2.0, 0.0)]
+    return Workload(f"mixed wide m{m} k4096 n4096 r8,200,13,128", 3, 50, m, 4096, 4096, ads, seg_off,
+                    np.array([0, 1, 2, 3, 1, 2], dtype=np.int32))
+
+
 def _bf16(t: torch.Tensor) -> torch.Tensor:
     return t.to(torch.bfloat16)
 

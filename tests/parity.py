@@ -86,13 +86,25 @@ def gpu_single(X, W, A, B, dY, alpha, p, seed=0, offset=0, stream=None):
             "dX": dX.cpu(), "dA": dA.cpu(), "dB": dB.cpu()}
 
 
-def gpu_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, seed=0, offset=0, r_max=None):
+def offset_view(t: torch.Tensor) -> torch.Tensor:
+    """The same values on the GPU, one element (2 bytes) past a 16-byte boundary."""
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device="cuda")
+    v = buf[1:1 + t.numel()].view(t.shape)
+    v.copy_(t.to("cuda"))
+    return v
+
+
+def gpu_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, seed=0, offset=0, r_max=None, unaligned=()):
+    """The mixed-adapter forward and backward on the GPU.  Adapters listed in
+    `unaligned` get A, B, dA and dB one element past a 16-byte boundary."""
     dev = "cuda"
     Xd, Wd, dYd = X.to(dev), W.to(dev), dY.to(dev)
-    Ad = [a.to(dev) for a in As]
-    Bd = [b.to(dev) for b in Bs]
-    dAd = [torch.full_like(a, 7.0) for a in Ad]  # garbage: outputs must be overwritten
-    dBd = [torch.full_like(b, 7.0) for b in Bd]
+    place = lambda a, t: offset_view(t) if a in unaligned else t.to(dev)
+    Ad = [place(a, t) for a, t in enumerate(As)]
+    Bd = [place(a, t) for a, t in enumerate(Bs)]
+    # garbage: outputs must be overwritten
+    dAd = [place(a, torch.full(t.shape, 7.0, dtype=t.dtype)) for a, t in enumerate(As)]
+    dBd = [place(a, torch.full(t.shape, 7.0, dtype=t.dtype)) for a, t in enumerate(Bs)]
     r_max = r_max or max(a.shape[1] for a in As)
     table = lf.adapter_table(Ad, Bd, alphas, ps, dAd, dBd)
     so = torch.as_tensor(np.asarray(seg_off, dtype=np.int64)).to(dev)

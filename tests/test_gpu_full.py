@@ -21,8 +21,8 @@ import torch
 
 import lora_fine_tuning_amd as lf
 import oracle
-from parity import assert_bits_equal, check_close, f64, log
-from synth import make_tensors_device, workload
+from parity import assert_bits_equal, check_close, f64, log, offset_view
+from synth import decoder_projection, make_tensors_device, wide_mixed_workload, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -114,23 +114,34 @@ def test_full_llama8b_projection(variant):
     run_single(workload(1, variant))
 
 
-@pytest.mark.parametrize("m,r", [(2048, 8), (2048, 128), (8192, 32), (8192, 128), (32768, 16), (32768, 64)])
+@pytest.mark.parametrize("m", [2048, 8192, 32768])
+@pytest.mark.parametrize("r", [8, 16, 32, 64, 128])
 def test_full_rank_token_sweep(m, r):
     run_single(workload(3, m=m, r=r))
 
 
-def run_multi(w):
+@pytest.mark.parametrize("index", [1, 6], ids=["k_proj_4096x1024", "down_proj_14336x4096"])
+def test_full_decoder_projection(index):
+    # the decoder layer's shapes that the two projection workloads above do
+    # not cover (q and o are k = n 4096; gate and up are 4096 -> 14336; v is k's)
+    run_single(decoder_projection(index))
+
+
+def run_multi(w, unaligned=()):
     log(f"full-size multi: {w.name} ranks={[a.r for a in w.adapters]} "
-        f"segments={w.seg_off.tolist()} adapters={w.seg_adapter.tolist()}")
+        f"segments={w.seg_off.tolist()} adapters={w.seg_adapter.tolist()} unaligned={list(unaligned)}")
     t = make_tensors_device(w, "cuda")
     X, W, dY = t["X"], t["W"], t["dY"]
-    As, Bs = t["A"], t["B"]
+    # adapters listed in `unaligned` sit one element past a 16-byte boundary
+    place = lambda a, v: offset_view(v) if a in unaligned else v
+    As = [place(a, v) for a, v in enumerate(t["A"])]
+    Bs = [place(a, v) for a, v in enumerate(t["B"])]
     alphas = [a.alpha for a in w.adapters]
     ps = [a.p for a in w.adapters]
     r_max = w.r_max
     lf.multi_lora_check_segments(w.seg_off, w.seg_adapter, w.m, [a.r for a in w.adapters], r_max)
-    dAs = [torch.full_like(a, 7.0) for a in As]  # outputs must be overwritten
-    dBs = [torch.full_like(b, 7.0) for b in Bs]
+    dAs = [place(a, torch.full_like(v, 7.0)) for a, v in enumerate(As)]  # outputs must be overwritten
+    dBs = [place(a, torch.full_like(v, 7.0)) for a, v in enumerate(Bs)]
     table = lf.adapter_table(As, Bs, alphas, ps, dAs, dBs)
     so = torch.as_tensor(w.seg_off).cuda()
     sa = torch.as_tensor(w.seg_adapter).cuda()
@@ -175,3 +186,9 @@ def test_full_mixed_four_adapters():
 
 def test_full_70b_down_proj_eight_adapters():
     run_multi(workload(4))
+
+
+def test_full_wide_rank_and_unaligned_adapters():
+    # ranks 8, 200, 13, 128: the widest is past 128, rank 13 is not a multiple
+    # of 8 and its A and B sit off 16-byte boundaries
+    run_multi(wide_mixed_workload(), unaligned=(2,))

@@ -10,7 +10,7 @@ import torch
 import lora_fine_tuning_amd as lf
 import oracle
 from parity import (assert_bits_equal, bf16_randn, check_close, compare_single, gpu_multi,
-                    gpu_single, log, oracle_multi, oracle_single)
+                    gpu_single, log, offset_view, oracle_multi, oracle_single)
 from synth import make_tensors, workload
 
 pytestmark = pytest.mark.gpu
@@ -72,14 +72,6 @@ def test_single_parity(m, k, n, r, alpha, p):
     o = oracle_single(X, W, A, B, dY, alpha, p, seed, offset)
     stats = compare_single(g, o, p)
     log(f"  {stats}")
-
-
-def offset_view(t: torch.Tensor) -> torch.Tensor:
-    """The same values on the GPU, one element (2 bytes) past a 16-byte boundary."""
-    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device="cuda")
-    v = buf[1:1 + t.numel()].view(t.shape)
-    v.copy_(t.to("cuda"))
-    return v
 
 
 @pytest.mark.parametrize("m,k,n,r", [(300, 264, 264, 16), (333, 264, 264, 64), (257, 512, 136, 24)])
@@ -229,6 +221,38 @@ def test_multi_parity(case):
     X, W, As, Bs, dY = multi_case(m, k, n, ranks, seed=100 + case)
     seed, offset = 77 + case, 8 * case
     g = gpu_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, seed, offset)
+    o = oracle_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, seed, offset)
+    assert_bits_equal("keep_bits", g["keep"], o["bits"])
+    check_close("S", g["S"], o["S"], rel=1e-4)
+    check_close("Y", g["Y"], o["Y"])
+    check_close("dX", g["dX"], o["dX"])
+    for a in range(len(ranks)):
+        check_close(f"dA[{a}]", g["dA"][a], o["dA"][a])
+        check_close(f"dB[{a}]", g["dB"][a], o["dB"][a])
+
+
+MIXED_WIDE_CASES = [
+    # m, k, n, ranks, alphas, ps, seg_off, seg_adapter, adapters placed off 16-byte boundaries
+    (600, 264, 264, [200, 13, 64], [2.0, 1.0, 0.5], [0.1, 0.2, 0.0],
+     [0, 150, 151, 400, 600], [1, 0, 2, 1], (1,)),            # rank 200 beside an unaligned rank-13 adapter
+    (520, 264, 136, [129, 256, 8], [1.0, 2.0, 4.0], [0.1, 0.1, 0.3],
+     [0, 100, 300, 520], [2, 1, 0], (2,)),                     # ranks 129 and 256, unaligned rank 8
+    (700, 520, 264, [16, 24, 64], [2.0, 0.5, 1.0], [0.1, 0.0, 0.2],
+     [0, 250, 500, 700], [0, 1, 2], (1,)),                     # ranks <= 64, unaligned rank 24
+    (640, 264, 264, [128, 40, 96], [1.0, 2.0, 0.5], [0.1, 0.1, 0.1],
+     [0, 64, 320, 640], [0, 1, 2], (0, 2)),                    # ranks <= 128, unaligned 128 and 96
+]
+
+
+@pytest.mark.parametrize("case", range(len(MIXED_WIDE_CASES)))
+def test_multi_wide_rank_and_unaligned_adapters(case):
+    m, k, n, ranks, alphas, ps, seg_off, seg_ad, unaligned = MIXED_WIDE_CASES[case]
+    log(f"mixed wide/unaligned case {case}: m={m} k={k} n={n} ranks={ranks} segs={seg_off} "
+        f"unaligned={unaligned}")
+    lf.multi_lora_check_segments(seg_off, seg_ad, m, ranks, max(ranks))
+    X, W, As, Bs, dY = multi_case(m, k, n, ranks, seed=300 + case)
+    seed, offset = 91 + case, 16 * case
+    g = gpu_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, seed, offset, unaligned=unaligned)
     o = oracle_multi(X, W, As, Bs, alphas, ps, seg_off, seg_ad, dY, seed, offset)
     assert_bits_equal("keep_bits", g["keep"], o["bits"])
     check_close("S", g["S"], o["S"], rel=1e-4)
