@@ -57,40 +57,36 @@ def parse():
                     help="instead of the headline step: the DoRA norm of W + alpha A B per output "
                          "feature at 8192 x 8192, ranks 16, 64 and 256 (one JSON line each)")
     ap.add_argument("--concat", action="store_true",
-                    help="instead of the headline step: at p = 0, the library's forward against the "
-                         "concatenated down-projection X [W | A] plus a separate Y += alpha S B pass")
+                    help="instead of the headline step: the forward at p = 0, concatenated [W | A] "
+                         "(one GEMM launch) against the split path and the frozen GEMM")
     return ap.parse_args()
 
 
 def concat_report(args):
-    """The concatenated down-projection for p = 0: S comes out of the base GEMM
-    as r extra output columns (X [W | A]), so X is read once, but the LoRA term
-    then needs its own pass over Y (Y += alpha S B, read and write of Y) because
-    no work-group holds S for its rows before its epilogue.  Timed from its
-    parts on the headline shapes: this library's GEMM on the k x (n + r) weight
-    (its 256-column tiles give the r extra columns a tile of their own), and
-    torch.addmm for the update (hipBLASLt with beta = 1).  Beside it, the
-    library's forward at p = 0 (the mask-free F1 pass over X, then the GEMM
-    with the LoRA term in its epilogue)."""
+    """The forward at p = 0, three ways, on the projection shapes (median of
+    cache-flushed event-timed trials):
+    * concatenated: lora_linear_fwd_concat, one GEMM launch in which every
+      256 x 256 tile also forms the 256 x r block of S = X A its rows need
+      (A's rows ride along with W's in the K loop) and adds alpha S B in its
+      epilogue -- no separate pass over X, no second pass over Y;
+    * split: lora_linear_fwd at p = 0, the pass over X that forms S, then the
+      GEMM with alpha S B in its epilogue;
+    * from parts (context): the frozen GEMM on the k x (n + r) weight [W | A]
+      gives S as r extra output columns, then torch.addmm adds alpha S B in a
+      second pass over Y.
+    Beside them, the frozen GEMM X W alone."""
     import torch
 
     import lora_fine_tuning_amd as lf
 
     lf.load()
+    stream = torch.cuda.current_stream()
+    timer = Timer(torch, stream)
     m, k, r, alpha = args.m, 4096, args.r, 2.0
     g = torch.Generator(device="cuda").manual_seed(3)
 
-    def timed(fn, iters):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters
+    def med(fn):
+        return timer.median(fn, args.steps, args.warmup)
 
     for n in (int(v) for v in args.shapes.split(",")):
         X = torch.randn(m, k, device="cuda", generator=g).bfloat16()
@@ -103,16 +99,16 @@ def concat_report(args):
         S = torch.empty(m, r, device="cuda", dtype=torch.float32)
         ws = torch.empty(max(lf.lora_linear_fwd_workspace_size(m, k, n, r), 1), dtype=torch.uint8, device="cuda")
         Sb = torch.randn(m, r, device="cuda", generator=g).bfloat16()
-        fused = timed(lambda: lf.lora_linear_fwd(X, W, A, B, alpha, 0.0, Y=Y, S=S, workspace=ws), args.steps)
-        gemm_cat = timed(lambda: lf.lora_frozen_fwd(X, Wc, Y=Yc), args.steps)
-        gemm = timed(lambda: lf.lora_frozen_fwd(X, W, Y=Y), args.steps)
-        update = timed(lambda: Y.addmm_(Sb, B, alpha=alpha), args.steps)
-        print(json.dumps({"metric": "forward ms at p = 0: fused path vs concatenated down-projection",
+        concat = med(lambda: lf.lora_linear_fwd_concat(X, W, A, B, alpha, Y=Y, S=S, stream=stream))
+        split = med(lambda: lf.lora_linear_fwd(X, W, A, B, alpha, 0.0, Y=Y, S=S, workspace=ws, stream=stream))
+        gemm = med(lambda: lf.lora_frozen_fwd(X, W, Y=Y, stream=stream))
+        parts = med(lambda: (lf.lora_frozen_fwd(X, Wc, Y=Yc, stream=stream), Y.addmm_(Sb, B, alpha=alpha)))
+        print(json.dumps({"metric": "forward ms at p = 0: concatenated [W | A] vs split (pass over X, then GEMM)",
                           "config": {"workload": f"m {m} k {k} n {n} r {r}"},
-                          "fused_fwd_ms": fused, "frozen_gemm_ms": gemm,
-                          "concat_gemm_ms": gemm_cat, "update_pass_ms": update,
-                          "concat_total_ms": gemm_cat + update,
-                          "concat_over_fused": (gemm_cat + update) / fused}), flush=True)
+                          "concat_fwd_ms": round(concat, 4), "split_fwd_ms": round(split, 4),
+                          "frozen_gemm_ms": round(gemm, 4), "from_parts_ms": round(parts, 4),
+                          "concat_over_split": round(concat / split, 4),
+                          "concat_over_frozen": round(concat / gemm, 4)}), flush=True)
         del X, W, A, B, Wc, Y, Yc, S, ws, Sb
 
 

@@ -115,6 +115,23 @@ lora_status lora_linear_fwd(const void *X, const void *W, const void *A, const v
                             void *Y, float *S, uint32_t *keep_bits,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Forward at p = 0 in the concatenated form (FALQON notes, section 5.2, the
+ * adapter's down-projection A stacked beside the frozen W as one operand; the
+ * recompute-versus-split question of the juhe.plus blog, section 4.1):
+ * Y = X W + alpha (X A) B and S = X A (fp32, m x r, row-major) in one GEMM
+ * launch.  Each 256 x 256 output tile forms, inside its own K loop, the
+ * 256 x r block of S its rows need (A's rows ride along with W's in every
+ * stage; about 6% more matrix-core work), then adds alpha S B before the
+ * single write of Y: no separate pass over X and no second pass over Y.  The
+ * tiles of the first column block also write S, which lora_linear_bwd takes
+ * with keep_bits = NULL and p = 0.  Needs no workspace.  r must be 8 or 16
+ * and A, B and S 16-byte aligned (else LORA_ERR_UNSUPPORTED; the general
+ * forward with p = 0 covers every other case).  Shapes and the other
+ * pointers as for lora_linear_fwd; m == 0 returns at once. */
+lora_status lora_linear_fwd_concat(const void *X, const void *W, const void *A, const void *B,
+                                   int64_t m, int64_t k, int64_t n, int32_t r, float alpha,
+                                   void *Y, float *S, hipStream_t stream);
+
 /* Bytes of workspace lora_linear_bwd needs for this shape. */
 size_t lora_linear_bwd_workspace_size(int64_t m, int64_t k, int64_t n, int32_t r);
 

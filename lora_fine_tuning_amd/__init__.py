@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     lora_pack_greedy,
     lora_frozen_bwd, lora_frozen_fwd, lora_linear_bwd, lora_linear_bwd_noalloc,
     lora_linear_bwd_noalloc_max_scratch, lora_linear_bwd_workspace_size,
-    lora_linear_fwd, lora_linear_fwd_workspace_size, lora_profiling_enable,
+    lora_linear_fwd, lora_linear_fwd_concat, lora_linear_fwd_workspace_size, lora_profiling_enable,
     lora_profiling_query, lora_profiling_reset, multi_lora_bwd_workspace_size,
     multi_lora_check_segments, multi_lora_fwd_workspace_size, multi_lora_linear_bwd,
     multi_lora_linear_fwd,

@@ -32,7 +32,7 @@ EXPORTS = [
     "lora_profiling_reset", "lora_profiling_query", "lora_status_string",
     "lora_last_error_message", "lora_pack_greedy", "lora_microbatch_segments",
     "lora_check_bubble_lemma", "lora_dora_norm_workspace_size", "lora_dora_norm",
-    "lora_linear_bwd_noalloc_max_scratch", "lora_linear_bwd_noalloc",
+    "lora_linear_bwd_noalloc_max_scratch", "lora_linear_bwd_noalloc", "lora_linear_fwd_concat",
 ]
 
 
@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                   SZ, P]),
         "lora_linear_bwd": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, F32, F32, P, P, P, P,
                                   SZ, P]),
+        "lora_linear_fwd_concat": (I32, [P, P, P, P, I64, I64, I64, I32, F32, P, P, P]),
         "lora_linear_bwd_noalloc_max_scratch": (SZ, []),
         "lora_linear_bwd_noalloc": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, F32, F32, P, P, P, P]),
         "multi_lora_linear_fwd": (I32, [P, P, P, I32, P, P, I32, I64, I64, I64, I32, U64, U64, P,
@@ -171,6 +172,24 @@ def lora_linear_fwd(X, W, A, B, alpha: float, p: float, seed: int = 0, offset: i
                                   offset, _ptr(Y), _ptr(S), _ptr(keep_bits), _ptr(ws), ws.numel(),
                                   _stream(stream)))
     return Y, S, keep_bits
+
+
+def lora_linear_fwd_concat(X, W, A, B, alpha: float, *, Y=None, S=None, stream=None):
+    """The forward at p = 0 with [W | A] as one operand.  Returns (Y, S);
+    outputs are allocated when not given.  r must be 8 or 16."""
+    for t, nm in ((X, "X"), (W, "W"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, nm)
+    m, k = X.shape
+    n = W.shape[1]
+    r = A.shape[1]
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    if S is None:
+        S = torch.empty((m, r), dtype=torch.float32, device=dev)
+    _check(load().lora_linear_fwd_concat(_ptr(X), _ptr(W), _ptr(A), _ptr(B), m, k, n, r, alpha, _ptr(Y),
+                                         _ptr(S), _stream(stream)))
+    return Y, S
 
 
 def lora_linear_bwd(dY, X, W, A, B, S, keep_bits, alpha: float, p: float, *, dX=None, dA=None,

@@ -395,6 +395,28 @@ extern "C" lora_status lora_linear_fwd(const void *X, const void *W, const void 
     return LORA_OK;
 }
 
+extern "C" lora_status lora_linear_fwd_concat(const void *X, const void *W, const void *A, const void *B,
+                                              int64_t m, int64_t k, int64_t n, int32_t r, float alpha,
+                                              void *Y, float *S, hipStream_t stream) {
+    CHECK(check_shape(m, k, n));
+    CHECK(check_rank(r));
+    CHECK(check_b_size(r, k, n));
+    REQ_PTR(W, 16);
+    REQ_PTR(A, 2);
+    REQ_PTR(B, 2);
+    if (r != 8 && r != 16)
+        return fail(LORA_ERR_UNSUPPORTED, "the concatenated forward takes r = 8 or 16 (r = %d)", r);
+    if (!aligned(A, 16) || !aligned(B, 16))
+        return fail(LORA_ERR_UNSUPPORTED, "the concatenated forward needs A and B 16-byte aligned");
+    if (m == 0) return LORA_OK;
+    REQ_PTR(X, 16);
+    REQ_PTR(Y, 16);
+    REQ_PTR(S, 4);
+    if (!aligned(S, 16)) return fail(LORA_ERR_UNSUPPORTED, "the concatenated forward needs S 16-byte aligned");
+    HIPCHK(launch_gemm_cat(X, W, A, B, Y, S, (int)m, (int)n, (int)k, r, alpha, stream), "concatenated F2 launch");
+    return LORA_OK;
+}
+
 extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void *W, const void *A,
                                        const void *B, const float *S, const uint32_t *keep_bits,
                                        int64_t m, int64_t k, int64_t n, int32_t r, float alpha,

@@ -77,7 +77,31 @@ struct GemmParams {
     // against B's rows (rank j for extra column j and RP + j; past r zero)
     const uint16_t *S2;
     int kx;
+    // FAST == 3 (forward at p = 0, [W | A] as one operand): A (K x ext_r) and
+    // the S output (M x ext_r fp32, written by the tiles of column 0)
+    const uint16_t *catA;
+    float *Sout;
 };
+
+// acc += a * b with the accumulator in VGPRs (the AGPRs hold the product's
+// tiles); like the in-place form, its latency is not modelled, so its result
+// is read only after mfma_drain().
+__device__ __forceinline__ void mfma16x16x32_vacc(f32x4_t &acc, const uint4 &a, const uint4 &b) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+v"(acc)
+                 : "v"(__builtin_bit_cast(i32x4_t, a)), "v"(__builtin_bit_cast(i32x4_t, b)));
+}
+
+// m ? b : a bit by bit (m is 0 or ~0, wave-uniform).  Written as one
+// v_bfi_b32 so the compiler cannot turn a select of two fragment registers
+// into an indexed access of the fragment array (which would put it in
+// scratch memory).
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t b, uint32_t a) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(b), "v"(a));
+    return r;
+}
 
 __device__ __forceinline__ void tile_coords(int wg, int G, int tiles_m, int tiles_n, int &tm, int &tn) {
     const int xcd = wg & 7, local = wg >> 3, per = G >> 3, rem = G & 7;
@@ -288,6 +312,15 @@ __device__ __forceinline__ int swz_w(int k) { return (4 * (k & 3)) ^ (2 * ((k >>
 // all its loads up front.  FAST == 2 is the r <= 16 form that folds the two
 // halves of the split row side into one MFMA.  Each is its own instantiation
 // so no kernel merges two epilogues.
+//
+// FAST == 3 (forward only, p = 0, r 8 or 16): the concatenated form of the
+// FALQON notes (section 5.2, W' = [W; A] as one operand).  Each tile forms
+// its own 256 x 16 block of S = X A inside the K loop -- A's 64 x 16 slice
+// rides along with every stage and each wave forms S for 64 of the tile's
+// rows from the row fragments it already holds (about 6% more MFMA work than
+// the 256 x 256 product) -- and then applies alpha S B in the FAST == 2
+// epilogue from LDS.  No separate pass over X forms S; the tiles of column 0 also
+// write S out for the backward.
 template <bool NN, int EPI, bool MULTI, int FAST>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     extern __shared__ uint4 gemm_smem[];
@@ -422,6 +455,32 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     }
 
     uint4 af[2][NT16], bf[2][NT16];
+    constexpr bool CAT = FAST == 3 && EPI == 1 && !MULTI;
+    // FAST == 3: A's rows k0 .. k0+63 of a stage at 24 KiB past the ring +
+    // 4 KiB per stage, 32 bytes (16 ranks; past r zero) per k-row; waves 0
+    // and 1 load them, waves 2 and 3 load zeros into the stage's spare half
+    // (every wave issues the same number of loads per stage)
+    uint4 aAf[2], xsel = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t wn_mask = wn ? ~0u : 0u;  // wave-uniform
+    f32x4_t sacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const sgpr4_t dAcat = make_desc(CAT ? (const void *)P.catA : (const void *)P.Arow,
+                                    CAT ? clamp_bytes((uint64_t)P.K * (uint64_t)P.ext_r * 2u) : 0u);
+    auto dma_a = [&](int k0, int stage) {
+        const int kr = 32 * wave + (lane >> 1), ch = lane & 1;
+        const uint32_t off = (wave < 2 && k0 + kr < P.K && 8 * ch < P.ext_r)
+            ? ((uint32_t)(k0 + kr) * (uint32_t)P.ext_r + 8u * ch) * 2u : kOOB;
+        dma16(dAcat, off, smem_lds + NST * STAGE_BYTES + 24576 + stage * 4096 + wave * 1024);
+    };
+    // column-side fragment of A for 32-deep step ks of a stage: lane l gets
+    // rank l % 16 at K slots 8 (l / 16) .. +7 (two transposing reads of 4 k-rows)
+    auto read_afrag = [&](int stage, int ks, int slot) {
+        const lds_char *pa = (const lds_char *)smem + NST * STAGE_BYTES + 24576 + stage * 4096 +
+                             (32 * ks + 8 * lg + (l16 >> 2)) * 32 + (l16 & 3) * 8;
+        const uint2 lo = lds_read_tr4(pa), hi = lds_read_tr4(pa + 128);
+        aAf[slot] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
     // the `which`-side fragment t of step ks (0/1) of LDS stage `stage` into slot `slot`
     auto read_frag = [&](int stage, int ks, int slot, int which, int t) {
         const char *base = smem + stage * STAGE_BYTES;
@@ -444,7 +503,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     // and EXTRA (the DMA is of an extra-K stage) are compile-time flags so the
     // MFMA stream carries no branches.
     auto mfma_step = [&](int sl, auto read_c, int rstage, int rks, int rsl, auto dma_c, int dk0, int dstage,
-                         auto extra_c) {
+                         auto extra_c) __attribute__((always_inline)) {
         constexpr bool READ = decltype(read_c)::value, DMA = decltype(dma_c)::value;
 #pragma unroll
         for (int i = 0; i < NT16 * NT16; ++i) {
@@ -455,6 +514,28 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             }
             if constexpr (DMA) {
                 if ((i & 3) == 2) dma_one(dk0, dstage, i >> 2, extra_c);
+            }
+            if constexpr (CAT) {
+                if constexpr (READ) {
+                    if (i == 1) read_afrag(rstage, rks, rsl);
+                }
+                if constexpr (DMA) {
+                    if (i == 63) dma_a(dk0, dstage);
+                }
+                // S of the wave's quarter of the tile's rows (row tiles 4 wn ..
+                // 4 wn + 3 of its half), one MFMA after every 16 of the
+                // product.  The row fragment is picked by select, not by a
+                // branch, so the MFMA stream stays one basic block, 12 MFMAs
+                // before the MFMA that reads it (far past the VALU-to-MFMA
+                // operand hazard); the accumulators stay in VGPRs.
+                if ((i & 15) == 3) {
+                    const int t = i >> 4;
+                    xsel.x = bitsel(wn_mask, af[sl][4 + t].x, af[sl][t].x);
+                    xsel.y = bitsel(wn_mask, af[sl][4 + t].y, af[sl][t].y);
+                    xsel.z = bitsel(wn_mask, af[sl][4 + t].z, af[sl][t].z);
+                    xsel.w = bitsel(wn_mask, af[sl][4 + t].w, af[sl][t].w);
+                }
+                if ((i & 15) == 15) mfma16x16x32_vacc(sacc[i >> 4], aAf[sl], xsel);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -472,11 +553,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     //          the W tile's chunk swizzle; B3: A rows n0 .. n0+255 (r bf16
     //          each) as one contiguous block
     //   24576  B3: mask words n0/32 .. +7 of rows m0 .. m0+255, 32 bytes each
-    constexpr bool PF = FAST == 2 && EPI != 0 && !MULTI;
-    constexpr int NPF = EPI == 2 ? 8 : 6;  // prefetch loads per wave
+    constexpr bool PF = (FAST == 2 || CAT) && EPI != 0 && !MULTI;
+    constexpr int NPF = EPI == 2 ? 8 : CAT ? 2 : 6;  // prefetch loads per wave
     const uint32_t pf_lds = smem_lds + NST * STAGE_BYTES;
     auto epi_prefetch = [&]() {
-        {
+        if (!CAT) {
             const sgpr4_t d = make_desc(P.Sx + (size_t)m0 * P.RS, clamp_bytes((uint64_t)(P.M - m0) * P.RS * 4u));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -527,6 +608,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) dma_one(0, 0, j, std::false_type{});
     }
+    if constexpr (CAT) dma_a(0, 0);
     if (KEXT && nkx < 2) {
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j, std::true_type{});
@@ -534,6 +616,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) dma_one(BK, 1, j, std::false_type{});
     }
+    if constexpr (CAT) dma_a(BK, 1);
     // B3 (not the all-loads-first forms): when the tile's items fit (see
     // plan_tile_items), A is staged in LDS for the epilogue.  The slab of the
     // first item's ranks 0..63 goes to the 32 KiB past the ring now, loaded
@@ -566,7 +649,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     }
     if constexpr (PF) epi_prefetch();
     if (lds_epi) wait_vmcnt<NDMA + 8>();
-    else wait_vmcnt<PF ? NDMA + NPF : NDMA>();
+    else wait_vmcnt<PF ? NDMA + NPF + (CAT ? 1 : 0) : NDMA>();
     asm volatile("" ::: "memory");  // keep the LDS reads below the barrier
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -575,6 +658,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
         read_frag(0, 0, 0, 0, t);
         read_frag(0, 0, 0, 1, t);
     }
+    if constexpr (CAT) read_afrag(0, 0, 0);
     // No scalar load may still be in flight when the K loop starts (the
     // compiler sinks the epilogue's kernel-argument loads to here): one would
     // make it wait for every LDS read (lgkmcnt 0) at the top of each MFMA step
@@ -584,7 +668,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     // landed everywhere and stage kt's buffer is no longer read -- step 1 with
     // the reads of step 0 of stage kt+1 and the loads of stage kt+2 into the
     // buffer stage kt released.  The last two stages drop the loads / reads.
-    auto stage_body = [&](int kt, auto read_next, auto load_next2, auto extra_c) {
+    auto stage_body = [&](int kt, auto read_next, auto load_next2, auto extra_c) __attribute__((always_inline)) {
         const int stage = kt & 1;
         mfma_step(0, T_{}, stage, 1, 1, F_{}, 0, 0, F_{});
         wait_vmcnt<0>();
@@ -602,6 +686,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
     if (kt < nk) stage_body(kt, F_{}, F_{}, F_{});
     mfma_drain();
     wait_vmcnt<0>();
+    if constexpr (CAT) {
+        // each wave's 64 rows of S go to the epilogue's S rows (fp32, 64
+        // bytes per row, chunk c of row q at c ^ ((q >> 2) & 3)); the tiles
+        // of column 0 also write them out
+        lds_char *sp = (lds_char *)smem + NST * STAGE_BYTES;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int q = wm * 128 + wn * 64 + 16 * t + l16;
+            *(f32x4_t *)(sp + q * 64 + ((lg ^ ((q >> 2) & 3)) << 4)) = sacc[t];
+            if (tni == 0 && m0 + q < P.M && 4 * lg < P.ext_r)
+                *(f32x4_t *)(P.Sout + (size_t)(m0 + q) * P.ext_r + 4 * lg) = sacc[t];
+        }
+    }
 
     const int wrow0 = m0 + wm * 128;  // first row of this wave
     const int wcol0 = n0 + wn * 128;  // first column of this wave
@@ -655,7 +752,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             // ranks 0-15, slots 16-31 the lo parts -- against the column side's
             // ranks 0-15 repeated in both halves.  Lanes of K groups 2, 3 then
             // address the ranks of groups 0, 1.
-            constexpr bool pack = FAST == 2;
+            constexpr bool pack = FAST >= 2;
             const int lgr = pack ? (lg & 1) : lg;
             const __amdgpu_buffer_rsrc_t rW = ext_rsrc<EPI>(P, it, wcol0);
             const lds_char *pf = (const lds_char *)smem + NST * STAGE_BYTES;
@@ -1263,6 +1360,31 @@ hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, voi
                                     : launch_gemm_t<false, 2, false, 0>(P, stream, "gemm_b3_bwd_dx");
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_cat(const void *X, const void *W, const void *A, const void *B, void *Y, float *S,
+                           int M, int N, int K, int r, float alpha, hipStream_t stream) {
+    GemmParams P{};
+    P.Arow = (const uint16_t *)X;
+    P.Bcol = (const uint16_t *)W;
+    P.C = (uint16_t *)Y;
+    P.M = M;
+    P.N = N;
+    P.K = K;
+    P.tiles_m = (M + GBM - 1) / GBM;
+    P.tiles_n = (N + GBN - 1) / GBN;
+    P.ext = (const uint16_t *)B;
+    P.ext_r = r;
+    P.ext_scale = alpha;
+    P.Sx = S;
+    P.RS = r;
+    P.catA = (const uint16_t *)A;
+    P.Sout = S;
+    if (P.tiles_m == 0 || P.tiles_n == 0) return hipSuccess;
+    // the kernel's fixed layout: ranks 8 or 16, A and B rows in whole 16-byte pieces
+    auto al16 = [](const void *q) { return ((uintptr_t)q & 15) == 0; };
+    if ((r != 8 && r != 16) || !al16(A) || !al16(B) || !al16(S)) return hipErrorInvalidValue;
+    return launch_gemm_t<true, 1, false, 3>(P, stream, "gemm_f2_concat_p0");
 }
 
 hipError_t launch_gemm_kext(const void *X, const void *W, void *Y, int M, int N, int K, const uint16_t *S2,

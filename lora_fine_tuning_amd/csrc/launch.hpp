@@ -192,6 +192,10 @@ hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, voi
 // where S2 holds alpha*S split into bf16 hi and lo parts of kx/2 ranks each and
 // B' repeats B's rows for both halves (rows past r zero).  B must be 16-byte
 // aligned (N is a multiple of 8).
+// Forward at p = 0 with [W | A] as one operand: Y = X W + alpha (X A) B and
+// S = X A (fp32, M x r), r 8 or 16, A / B / S 16-byte aligned.
+hipError_t launch_gemm_cat(const void *X, const void *W, const void *A, const void *B, void *Y, float *S,
+                           int M, int N, int K, int r, float alpha, hipStream_t stream);
 hipError_t launch_gemm_kext(const void *X, const void *W, void *Y, int M, int N, int K, const uint16_t *S2,
                             int kx, const void *B, int r, hipStream_t stream);
 

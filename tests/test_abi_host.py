@@ -271,3 +271,20 @@ def test_bwd_noalloc_host_checks(lib):
     assert b"scratch" in lib.lora_last_error_message()
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 60, 64, 8, 1.0, 0.1, FAKE, FAKE, FAKE, None) == INVALID
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 0, 1.0, 0.1, FAKE, FAKE, FAKE, None) == INVALID
+
+
+def test_fwd_concat_host_checks(lib):
+    f = lib.lora_linear_fwd_concat
+    base = (FAKE, FAKE, FAKE, FAKE, 64, 64, 64)
+    # ranks other than 8 and 16, and A / B off 16-byte boundaries, take the general forward
+    assert f(*base, 32, 1.0, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(*base, 5, 1.0, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE + 2, FAKE, 64, 64, 64, 16, 1.0, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE + 2, 64, 64, 64, 8, 1.0, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 16, 1.0, FAKE, FAKE + 4, None) == UNSUPPORTED
+    # shape and rank checks come first, as in the general forward
+    assert f(*base[:4], 64, 60, 64, 16, 1.0, FAKE, FAKE, None) == INVALID
+    assert f(*base, 0, 1.0, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE + 8, FAKE, FAKE, 64, 64, 64, 16, 1.0, FAKE, FAKE, None) == INVALID
+    # m == 0: nothing to do, m-sized pointers may be NULL
+    assert f(None, FAKE, FAKE, FAKE, 0, 64, 64, 16, 1.0, None, None, None) == OK

@@ -192,3 +192,25 @@ def test_full_wide_rank_and_unaligned_adapters():
     # ranks 8, 200, 13, 128: the widest is past 128, rank 13 is not a multiple
     # of 8 and its A and B sit off 16-byte boundaries
     run_multi(wide_mixed_workload(), unaligned=(2,))
+
+
+@pytest.mark.parametrize("variant", [0, 1], ids=["n4096", "n14336"])
+def test_full_concat_forward_p0(variant):
+    # the forward with [W | A] as one operand at p = 0 on the projection shapes
+    w = workload(1, variant)
+    ad = w.adapters[0]
+    log(f"full-size concatenated forward: {w.name} alpha={ad.alpha} p=0")
+    t = make_tensors_device(w, "cuda")
+    X, W, A, B, dY = t["X"], t["W"], t["A"][0], t["B"][0], t["dY"]
+    Y, S = lf.lora_linear_fwd_concat(X, W, A, B, ad.alpha)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.m, seed=w.m + ad.r)
+    a_rows = sample_features(w.k, seed=1)
+    b_cols = sample_features(w.n, seed=2)
+    o = oracle.lora_sampled(f64(X), f64(W), f64(A), f64(B), f64(dY), ad.alpha, np.float32(0.0),
+                            w.seed, w.offset, rows, a_rows, b_cols)
+    log(f"  S {check_close('S', S, o['S'], rel=1e-4)}")
+    log(f"  Y rows {check_close('Y rows', Y[torch.from_numpy(rows).cuda()], o['Y'])}")
+    ones = np.ones((w.m, w.k), dtype=np.uint8)
+    Yr, _ = torch_reference_rows(X, W, dY, [(0, w.m, A, B, ad.alpha, 0.0, ones)], w.k)
+    log(f"  torch fp32, all rows: Y {check_close('Y', Y, Yr)}")

@@ -108,6 +108,53 @@ def test_bwd_without_input_gradient():
     assert Xd.grad is None and torch.equal(Ag.grad, dA) and torch.equal(Bg.grad, dB)
 
 
+CONCAT_CASES = [
+    # m, k, n, r, alpha
+    (512, 1024, 1024, 16, 2.0),   # the small workload's shape
+    (300, 200, 136, 8, 1.5),      # ragged everywhere; K ends inside a 64-deep stage
+    (257, 264, 520, 16, 0.5),     # one row past a tile
+    (1000, 4096, 264, 8, 2.0),    # 64 K stages
+    (8, 8, 8, 16, 1.0),           # tiny
+    (600, 520, 776, 16, 0.0),     # alpha 0: Y is the frozen product, S still X A
+]
+
+
+@pytest.mark.parametrize("m,k,n,r,alpha", CONCAT_CASES)
+def test_concat_forward_p0(m, k, n, r, alpha):
+    # the forward with [W | A] as one operand at p = 0: Y and S against the
+    # oracle, S feeding the backward, and the split forward agreeing
+    log(f"concatenated forward m={m} k={k} n={n} r={r} alpha={alpha}")
+    X, W, A, B, dY = small_case(m, k, n, r, seed=7 * m + r)
+    Xd, Wd, Ad, Bd, dYd = (t.cuda() for t in (X, W, A, B, dY))
+    Y, S = lf.lora_linear_fwd_concat(Xd, Wd, Ad, Bd, alpha)
+    Y2, S2, _ = lf.lora_linear_fwd(Xd, Wd, Ad, Bd, alpha, 0.0)
+    dX, dA, dB = lf.lora_linear_bwd(dYd, Xd, Wd, Ad, Bd, S, None, alpha, 0.0)
+    torch.cuda.synchronize()
+    o = oracle_single(X, W, A, B, dY, alpha, 0.0)
+    stats = {"S": check_close("S", S.cpu(), o["S"], rel=1e-4),
+             "Y": check_close("Y", Y.cpu(), o["Y"]),
+             "dX": check_close("dX", dX.cpu(), o["dX"]),
+             "dA": check_close("dA", dA.cpu(), o["dA"]),
+             "dB": check_close("dB", dB.cpu(), o["dB"]),
+             "S vs split": check_close("S vs split", S.cpu(), S2.cpu().double().numpy(), rel=1e-5),
+             "Y vs split": check_close("Y vs split", Y.cpu(), Y2.cpu().double().numpy())}
+    log(f"  {stats}")
+
+
+def test_concat_forward_deterministic_and_unsupported():
+    X, W, A, B, _ = small_case(520, 512, 264, 16, seed=13)
+    Xd, Wd, Ad, Bd = (t.cuda() for t in (X, W, A, B))
+    a = lf.lora_linear_fwd_concat(Xd, Wd, Ad, Bd, 2.0)
+    b = lf.lora_linear_fwd_concat(Xd, Wd, Ad, Bd, 2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # other ranks are refused before any launch (the general forward covers them)
+    A24 = torch.zeros((512, 24), dtype=torch.bfloat16, device="cuda")
+    B24 = torch.zeros((24, 264), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lf.LoraError):
+        lf.lora_linear_fwd_concat(Xd, Wd, A24, B24, 2.0)
+
+
 @pytest.mark.parametrize("m,k,n,r", [(300, 264, 264, 33), (333, 264, 264, 36), (300, 264, 136, 80),
                                      (520, 1024, 264, 96), (96, 256, 264, 256), (257, 264, 520, 17)])
 def test_single_garbage_workspace(m, k, n, r):
