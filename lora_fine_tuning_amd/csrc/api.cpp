@@ -55,7 +55,11 @@ static lora_status hip_fail(hipError_t e, const char *what) {
 }
 
 extern "C" const char *lora_status_string(lora_status s) {
-    switch (s) {
+    // A C caller may pass any int; read it as one (a C++ load of an enum value
+    // outside its enumerators' range is undefined).
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case LORA_OK: return "LORA_OK";
     case LORA_ERR_INVALID_ARG: return "LORA_ERR_INVALID_ARG";
     case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED";

@@ -111,6 +111,12 @@ def test_threshold_closed_forms():
     assert oracle.threshold(np.float32(0.1)) == 6554
     assert oracle.threshold(np.float32(0.05)) == 3277
     assert oracle.threshold(np.float32(0.25)) == 16384
+    # float32(0.9999) = 0x1.fff2e4p-1 = 0.99989998340606689...; * 65536 + 0.5 = 65529.945...
+    assert oracle.threshold(np.float32(0.9999)) == 65529
+    # float32(0.95) = 0x1.e66666p-1 = 0.94999998807907104...; * 65536 + 0.5 = 62259.699...
+    assert oracle.threshold(np.float32(0.95)) == 62259
+    # float32(0.3) = 0x1.333334p-2 = 0.30000001192092896...; * 65536 + 0.5 = 19661.300...
+    assert oracle.threshold(np.float32(0.3)) == 19661
 
 
 def test_pack_bits_layout_matches_numpy_packbits():
