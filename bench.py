@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--dora", action="store_true",
                     help="instead of the headline step: the DoRA norm of W + alpha A B per output "
                          "feature at 8192 x 8192, ranks 16, 64 and 256 (one JSON line each)")
+    ap.add_argument("--hbm", action="store_true",
+                    help="instead of the headline step: the practical HBM ceiling of this part (a 2 GiB "
+                         "device copy and a 4 GiB read-only reduction, median of flushed trials)")
     ap.add_argument("--concat", action="store_true",
                     help="instead of the headline step: the forward at p = 0, concatenated [W | A] "
                          "(one GEMM launch) against the split path and the frozen GEMM")
@@ -110,6 +113,32 @@ def concat_report(args):
                           "concat_over_split": round(concat / split, 4),
                           "concat_over_frozen": round(concat / gemm, 4)}), flush=True)
         del X, W, A, B, Wc, Y, Yc, S, ws, Sb
+
+
+def hbm_report(args):
+    """What a plain streaming kernel reaches on this part, for the HBM-bound
+    kernels' fractions: a device-to-device copy of 2 GiB (bytes read + bytes
+    written per second) and torch.sum over 4 GiB of fp32 (bytes read per
+    second), median of cache-flushed event-timed trials."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    timer = Timer(torch, stream)
+    n = (2 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    copy_ms = timer.median(lambda: b.copy_(a), args.steps, args.warmup)
+    del a, b
+    x = torch.ones((4 << 30) // 4, dtype=torch.float32, device="cuda")
+    sum_ms = timer.median(lambda: x.sum(), args.steps, args.warmup)
+    del x
+    copy_gbs = 2 * (2 << 30) / (copy_ms * 1e-3) / 1e9
+    read_gbs = (4 << 30) / (sum_ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "practical HBM bandwidth (plain streaming kernels)",
+                      "copy_2GiB": {"ms": round(copy_ms, 4), "GB/s": round(copy_gbs, 1),
+                                    "frac_of_8TBs": round(copy_gbs / PEAK_HBM_GBS, 4)},
+                      "sum_read_4GiB": {"ms": round(sum_ms, 4), "GB/s": round(read_gbs, 1),
+                                        "frac_of_8TBs": round(read_gbs / PEAK_HBM_GBS, 4)}}), flush=True)
 
 
 def dora_report(args):
@@ -570,6 +599,9 @@ def main():
         return
     if args.dora:
         dora_report(args)
+        return
+    if args.hbm:
+        hbm_report(args)
         return
     if args.concat:
         concat_report(args)

@@ -1598,9 +1598,12 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     extern __shared__ uint4 b1v_smem[];
     lds_char *smem = (lds_char *)b1v_smem;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    // [NRED][4 waves][32 rows][RL]: double-buffered for RL = 16; for RL = 32 one
-    // buffer and a second barrier per sub-block, so two work-groups fit a CU
+    // [NRED][4 waves][32 rows][RLP]: double-buffered for RL = 16; for RL = 32 one
+    // buffer and a second barrier per sub-block, so two work-groups fit a CU.
+    // Rows are RL + 4 floats apart, so the four 4-row groups of a wave's
+    // stores (rows 4g + v) fall on four different 16-bank ranges.
     constexpr int NRED = MAXT == 1 ? 2 : 1;
+    constexpr int RLP = RL + 4;
     float *red = (float *)(smem + NST * STAGE);
 
     int row_lo, row_hi;
@@ -1694,7 +1697,7 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     // sum of the four waves' dS shares of sub-block sb (after the barrier)
     // thread t handles row t / 8 of the sub-block, columns t % 8, +8, ...
     auto flush_ds = [&](int sb) {
-        const float *rd = red + (sb % NRED) * (4 * 32 * RL);
+        const float *rd = red + (sb % NRED) * (4 * 32 * RLP);
         const int rr = tid >> 3, rs = row_lo + sb * 32;
         if (rs + rr >= row_hi) return;
         float *drow = dsp + (size_t)(rs + rr) * P.RS;
@@ -1702,10 +1705,10 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
         for (int j = 0; j < 4; ++j) {
             const int cl = (tid & 7) + 8 * j, cc = r0 + cl;
             if (cl >= RL || cc >= P.RS) break;
-            float v = rd[(0 * 32 + rr) * RL + cl];
-            v += rd[(1 * 32 + rr) * RL + cl];
-            v += rd[(2 * 32 + rr) * RL + cl];
-            v += rd[(3 * 32 + rr) * RL + cl];
+            float v = rd[(0 * 32 + rr) * RLP + cl];
+            v += rd[(1 * 32 + rr) * RLP + cl];
+            v += rd[(2 * 32 + rr) * RLP + cl];
+            v += rd[(3 * 32 + rr) * RLP + cl];
             drow[cc] = cc < r ? v * alpha : 0.f;
         }
     };
@@ -1733,13 +1736,13 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
                 for (int bt = 0; bt < MAXT; ++bt) accS[rb][bt] = mfma16x16x32(af, bfr[q][bt], accS[rb][bt]);
             }
         }
-        float *rw = red + (sb % NRED) * (4 * 32 * RL) + wave * 32 * RL;
+        float *rw = red + (sb % NRED) * (4 * 32 * RLP) + wave * 32 * RLP;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int bt = 0; bt < MAXT; ++bt)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) rw[(16 * rb + 4 * g + v) * RL + 16 * bt + li] = accS[rb][bt][v];
+                for (int v = 0; v < 4; ++v) rw[(16 * rb + 4 * g + v) * RLP + 16 * bt + li] = accS[rb][bt][v];
 
         // ---- dB: rank x the wave's columns, K = the 32 rows
         uint4 ahi[MAXT], alo[MAXT];
@@ -2145,7 +2148,7 @@ hipError_t launch_b1(const void *dY, const float *S, int m, int n, int RS, const
         const int rl = P.r_lds <= 16 ? 16 : 32;
         // ring depth 3: two stages in flight, two work-groups per CU
         auto lds_of = [&](int nst) {
-            return (size_t)nst * (sh.cw * B1V_SUB + 32 * 32 * 4) + (size_t)(rl == 16 ? 2 : 1) * 4 * 32 * rl * 4;
+            return (size_t)nst * (sh.cw * B1V_SUB + 32 * 32 * 4) + (size_t)(rl == 16 ? 2 : 1) * 4 * 32 * (rl + 4) * 4;
         };
         if (rl == 16) launch_with_lds(b1v_kernel<1, 1, 3>, grid, lds_of(3), stream, P);
         else launch_with_lds(b1v_kernel<1, 2, 3>, grid, lds_of(3), stream, P);
