@@ -277,8 +277,9 @@ struct BwdPlan {
     int ds_parts;  // dS partials written by B1 (one per column tile)
     bool b2w;      // the single-pass dA kernel (and its per-adapter sum launch)
     int items2;    // its grid rows of work items
+    int dss_ld;    // > 0: B1's sum also writes split s*dS rows (dss_ld bf16 apart) for B2 and B3
     size_t off_ds, off_dspart, off_dbpart, off_dapart, off_t_f1, off_c_f1, off_t_bwd, off_c_bwd;
-    size_t off_t_b1, off_c_b1, off_aditems;
+    size_t off_t_b1, off_c_b1, off_aditems, off_dss;
     size_t bytes;
 };
 
@@ -294,6 +295,7 @@ BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_
     p.ds_parts = p.b1.CT;
     p.b2w = b2w_ok(rl, RS);
     p.items2 = multi ? p.chunk_cap_bwd : cdiv(m, p.rows2);
+    p.dss_ld = p.b2w ? presplit_ld(rl) : 0;
     const int nct2 = cdiv(k, 256);
     Carve c;
     p.off_ds = c.take((size_t)m * RS * sizeof(float));
@@ -304,6 +306,7 @@ BwdPlan plan_bwd(int64_t m, int64_t k, int64_t n, int32_t RS, bool multi, int32_
     else
         p.off_dapart = c.take((size_t)p.chunk_cap_bwd * k * RS * sizeof(float));
     p.off_aditems = c.take(multi ? (size_t)nad * sizeof(int32_t) : 0);
+    p.off_dss = c.take((size_t)m * p.dss_ld * sizeof(uint16_t));
     if (multi) {
         p.off_t_f1 = c.take((size_t)p.chunk_cap_f1 * sizeof(ChunkEntry));
         p.off_c_f1 = c.take(sizeof(int32_t));
@@ -453,14 +456,15 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
     float *dSpart = pl.ds_parts > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
     float *dBpart = (float *)ws_at(workspace, pl.off_dbpart);
     float *dApart = (float *)ws_at(workspace, pl.off_dapart);
+    uint16_t *dss = pl.dss_ld > 0 ? (uint16_t *)ws_at(workspace, pl.off_dss) : nullptr;
     const int chunks = pl.chunk_cap_bwd;
     if (m > 0) HIPCHK(launch_b1(dY, S, (int)m, (int)n, r, src, pl.b1, dSpart, dBpart, stream), "B1 launch");
     HIPCHK(launch_b1_reduce(dSpart, m > 0 ? pl.ds_parts : 1, dS, dBpart, (int)m, (int)n, r, src, pl.b1.rows,
-                            pl.b1.slots, stream),
+                            pl.b1.slots, stream, dss, pl.dss_ld),
            "dS/dB reduction launch");
     if (pl.b2w) {
         HIPCHK(launch_b2w(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, pl.rows2, src, pl.items2,
-                          dApart, nullptr, stream), "B2 launch");
+                          dApart, nullptr, stream, dss, pl.dss_ld), "B2 launch");
     } else {
         if (m > 0)
             HIPCHK(launch_b2(X, p == 0.0f ? nullptr : keep_bits, dS, (int)m, (int)k, r, pl.rows2, src, chunks,
@@ -470,7 +474,7 @@ extern "C" lora_status lora_linear_bwd(const void *dY, const void *X, const void
     }
     if (m > 0 && dX != nullptr)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r, p == 0.0f ? nullptr : keep_bits,
-                           (int)((k + 31) / 32), src, stream), "B3 launch");
+                           (int)((k + 31) / 32), src, stream, dss, pl.dss_ld), "B3 launch");
     return LORA_OK;
 }
 
@@ -602,14 +606,15 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
     float *dSpart = pl.ds_parts > 1 ? (float *)ws_at(workspace, pl.off_dspart) : dS;
     float *dBpart = (float *)ws_at(workspace, pl.off_dbpart);
     float *dApart = (float *)ws_at(workspace, pl.off_dapart);
+    uint16_t *dss = pl.dss_ld > 0 ? (uint16_t *)ws_at(workspace, pl.off_dss) : nullptr;
     const int chunks = pl.chunk_cap_bwd;
     if (m > 0) HIPCHK(launch_b1(dY, S, (int)m, (int)n, r_max, src, pl.b1, dSpart, dBpart, stream), "B1 launch");
     HIPCHK(launch_b1_reduce(dSpart, m > 0 ? pl.ds_parts : 1, dS, dBpart, (int)m, (int)n, r_max, src, pl.b1.rows,
-                            pl.b1.slots, stream),
+                            pl.b1.slots, stream, dss, pl.dss_ld),
            "dS/dB reduction launch");
     if (pl.b2w) {
         HIPCHK(launch_b2w(X, keep_bits, dS, (int)m, (int)k, r_max, pl.rows2, src, pl.items2, dApart, aditems,
-                          stream), "B2 launch");
+                          stream, dss, pl.dss_ld), "B2 launch");
     } else {
         if (m > 0)
             HIPCHK(launch_b2(X, keep_bits, dS, (int)m, (int)k, r_max, pl.rows2, src, chunks, pl.C2, dApart, stream),
@@ -619,7 +624,7 @@ extern "C" lora_status multi_lora_linear_bwd(const void *dY, const void *X, cons
     }
     if (m > 0 && dX != nullptr)
         HIPCHK(launch_gemm(false, 2, dY, W, dX, (int)m, (int)k, (int)n, dS, r_max, keep_bits, (int)((k + 31) / 32),
-                           src, stream), "B3 launch");
+                           src, stream, dss, pl.dss_ld), "B3 launch");
     return LORA_OK;
 }
 

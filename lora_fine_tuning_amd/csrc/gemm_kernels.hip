@@ -81,6 +81,10 @@ struct GemmParams {
     // the S output (M x ext_r fp32, written by the tiles of column 0)
     const uint16_t *catA;
     float *Sout;
+    // B3 with A staged in LDS: optional rows of [hi | lo] bf16 of s*dS (the
+    // row's adapter's rpa ranks each, dss_ld apart), read instead of dS
+    const uint16_t *dss;
+    int dss_ld;
 };
 
 // acc += a * b with the accumulator in VGPRs (the AGPRs hold the product's
@@ -957,13 +961,27 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             const bool has_keep = P.keep != nullptr;
             const __amdgpu_buffer_rsrc_t rK = make_rsrc(has_keep ? P.keep + (size_t)min(wrow0, P.M) * P.KW : P.keep,
                                                         has_keep ? (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.KW * 4u : 0u);
-            // S / dS of band tm, chunk j: ranks rr0 + 8 (lane / 16) .. +7 of the lane's row
+            // dS of band tm, chunk j: ranks rr0 + 8 (lane / 16) .. +7 of the lane's
+            // row, as 8 fp32 values, or (split rows given) as the 8 hi and the 8
+            // lo bf16 of s*dS, bit-cast into f[0] and f[1]
+            const bool presplit = P.dss != nullptr;
+            const __amdgpu_buffer_rsrc_t rD = make_rsrc(presplit ? P.dss + (size_t)min(wrow0, P.M) * P.dss_ld : P.dss,
+                                                        presplit ? (uint64_t)max(P.M - wrow0, 0) * (uint64_t)P.dss_ld * 2u : 0u);
             auto load_slot = [&](int tm, int j, int nc0, float4 (&f)[2]) {
                 const bool second = j >= nc0;
                 const ExtItem &it = second ? ti.it[1] : ti.it[0];
                 const int rb = 32 * (second ? j - nc0 : j) + 8 * lg;
                 const int row = wrow0 + tm * 16 + l16;
                 const bool ok = row >= it.lo && row < it.hi && rb < it.r;
+                if (presplit) {
+                    const int nbt = (it.r + 15) >> 4;
+                    const int rpa = 16 * (nbt <= 1 ? 1 : nbt <= 2 ? 2 : nbt <= 4 ? 4 : 8);
+                    const uint32_t base = (uint32_t)((tm * 16 + l16) * P.dss_ld + rb) * 2u;
+                    f[0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rD, ok ? base : kOOB, 0, 0));
+                    f[1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rD, ok ? base + (uint32_t)rpa * 2u : kOOB, 0, 0));
+                    return;
+                }
                 const uint32_t off = ok ? (uint32_t)((tm * 16 + l16) * P.RS + rb) * 4u : kOOB;
                 f[0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off, 0, 0));
                 f[1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, ok ? off + 16u : kOOB, 0, 0));
@@ -987,12 +1005,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             auto mfma_slot = [&](int j, int nc0, const float4 (&f)[2], f32x4_t (&acc2)[NT16]) {
                 const bool second = j >= nc0;
                 const int rr0 = 32 * (second ? j - nc0 : j);
-                const float sc = second ? ti.it[1].scale : ti.it[0].scale;
-                float v[8] = {f[0].x, f[0].y, f[0].z, f[0].w, f[1].x, f[1].y, f[1].z, f[1].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= sc;
                 uint4 hi, lo;
-                split_frag(v, hi, lo);
+                if (presplit) {
+                    hi = __builtin_bit_cast(uint4, f[0]);
+                    lo = __builtin_bit_cast(uint4, f[1]);
+                } else {
+                    const float sc = second ? ti.it[1].scale : ti.it[0].scale;
+                    float v[8] = {f[0].x, f[0].y, f[0].z, f[0].w, f[1].x, f[1].y, f[1].z, f[1].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] *= sc;
+                    split_frag(v, hi, lo);
+                }
                 const int q = ((rr0 >> 5) & 1) * 4 + lg;  // 8-rank chunk inside the slab
                 const lds_char *sb = (const lds_char *)smem + slab_at[(second ? 2 : 0) + (rr0 >> 6)];
 #pragma unroll
@@ -1315,8 +1338,10 @@ static hipError_t launch_gemm_t(const GemmParams &P, hipStream_t stream, const c
 
 hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, void *C, int M, int N,
                        int K, const float *Sx, int RS, const uint32_t *keep, int KW,
-                       const AdapterSource &src, hipStream_t stream) {
+                       const AdapterSource &src, hipStream_t stream, const uint16_t *dss, int dss_ld) {
     GemmParams P{};
+    P.dss = epi == 2 ? dss : nullptr;
+    P.dss_ld = dss_ld;
     P.Arow = (const uint16_t *)Arow;
     P.Bcol = (const uint16_t *)Bcol;
     P.C = (uint16_t *)C;

@@ -153,8 +153,11 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
 // which = 0: dB (r x n per adapter from [chunk][RS][n]); 1: dA (k x r from [chunk][k][RS]).
 // dS = fixed-order sum of B1's nparts column-tile partials (skipped when
 // nparts == 1) and dB = per-adapter sum of its row-group partials, one launch.
+// dss (optional): also write rows of [hi | lo] bf16 of s*dS for the dA pass
+// and the dX epilogue, dss_ld (presplit_ld) bf16 apart
 hipError_t launch_b1_reduce(const float *dSpart, int nparts, float *dS, const float *dBpart, int m, int n,
-                            int RS, const AdapterSource &src, int rows, int slots, hipStream_t stream);
+                            int RS, const AdapterSource &src, int rows, int slots, hipStream_t stream,
+                            uint16_t *dss = nullptr, int dss_ld = 0);
 
 // The single-pass dA kernel (ranks up to 128 in one pass over X) serves
 // r_lds <= 128 when S / dS rows are 16-byte pieces (RS % 4 == 0).  Its
@@ -168,9 +171,12 @@ inline bool b2w_ok(int r_lds, int RS) { return r_lds <= 128 && RS % 4 == 0; }
 // items: grid rows of work items (single: ceil(m / rows); multi: the
 // backward table's capacity); ad_items: multi only (the router's
 // per-adapter counts).
+// Row stride (bf16) of the split s*dS rows the dA pass needs above 32 ranks
+// (0: the pass splits dS itself)
+inline int presplit_ld(int r_lds) { return b2w_ok(r_lds, 4) && b2w_blocks(r_lds) >= 4 ? 32 * b2w_blocks(r_lds) : 0; }
 hipError_t launch_b2w(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS, int rows,
                       const AdapterSource &src, int items, float *part, const int32_t *ad_items,
-                      hipStream_t stream);
+                      hipStream_t stream, const uint16_t *dss = nullptr, int dss_ld = 0);
 
 // rows: rows per partial of the single-adapter form; slots: partials
 // written (an upper bound in the mixed-adapter form, where the router's chunk
@@ -186,7 +192,8 @@ hipError_t launch_mask(uint64_t seed, uint64_t offset, int m, int k, float p, ui
 // epi 0: none; 1: + alpha*S*B (F2); 2: + s*keep.(dS A^T) (B3).
 hipError_t launch_gemm(bool nn, int epi, const void *Arow, const void *Bcol, void *C, int M, int N,
                        int K, const float *Sx, int RS, const uint32_t *keep, int KW,
-                       const AdapterSource &src, hipStream_t stream);
+                       const AdapterSource &src, hipStream_t stream, const uint16_t *dss = nullptr,
+                       int dss_ld = 0);
 
 // Forward GEMM with the LoRA term as kx extra K columns: Y = [X | S2] [W ; B' ]
 // where S2 holds alpha*S split into bf16 hi and lo parts of kx/2 ranks each and

@@ -1290,18 +1290,23 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
 // Work-group = one work item (rows of one adapter) x 256 columns of k, all
 // ranks at once (16 * MAXT of them).  Rows go in sub-blocks of 32 through a
 // 3- or 4-stage ring of direct-to-LDS loads: X (32 x 256 bf16, swizzled 512-byte
-// rows), the rows' mask words (32 x 8 words) and their dS (32 x RPT fp32).
+// rows), the rows' mask words (32 x 8 words) and the rank-side operand.
 // Wave w owns the 16-column blocks 4w .. 4w+3 and accumulates
 // (s*keep.X)^T dS for them over all the item's rows, then writes its part of
 // the item's partial; dA_reduce_kernel adds the partials of each adapter.
-// The rank-side operand (s*dS split into bf16 hi + lo) is the same for all
-// four waves: up to 32 ranks each wave splits it itself; above that the four
-// waves split a quarter each into a shared LDS tile (one more barrier per
-// sub-block), which the MFMAs then read with transposing LDS reads.
+// The rank-side operand is s*dS split into bf16 hi + lo, the same for all
+// four waves.  Up to 32 ranks each wave splits the fp32 dS rows itself.
+// Above that (MAXT >= 4) the split comes ready from B1's finishing launch
+// (rows of [hi of RPa ranks | lo of RPa ranks], RPa the item's 16-rank
+// blocks) and is loaded straight into a 32 x 512-byte tile with X's chunk
+// swizzle, which the MFMAs read with transposing LDS reads: no split work
+// and no extra barrier per sub-block.
 struct B2WParams {
     const uint16_t *X;
     const uint32_t *keep;
     const float *dS;
+    const uint16_t *dss;  // MAXT >= 4: split s*dS rows, dss_ld bf16 apart
+    int dss_ld;
     int m, k, RS, KW;
     RowWork work;   // work items: the router's backward table, or rows_per_chunk rows
     int nct;        // column tiles of 256
@@ -1311,13 +1316,19 @@ struct B2WParams {
 template <int MAXT>
 struct B2W {
     static constexpr int RPT = 16 * MAXT;                  // ranks per partial row
-    static constexpr int NA = 1 + (32 * RPT * 4) / 1024;   // aux 1 KiB loads: mask, then dS
-    static constexpr int NPW = (NA + 3) / 4;               // aux loads per wave (the rest hit a dummy slot)
+    static constexpr bool PRESPLIT = MAXT >= 4;            // rank side from the split rows
     static constexpr int X_BYTES = 32 * 512;
-    static constexpr int STAGE = X_BYTES + 4 * NPW * 1024;
-    static constexpr int NST = MAXT == 2 ? 3 : 4;          // ring depth (LDS: 2 WGs per CU up to 32 ranks, else 1)
-    static constexpr bool SPLIT_TILE = MAXT >= 4;           // the shared hi | lo tile (32 x 512 bytes)
-    static constexpr int LDS = NST * STAGE + (SPLIT_TILE ? 32 * 512 : 0);
+    // fp32 dS rows: aux 1 KiB loads of mask, then dS (slots past NA load zeros
+    // into the stage's spare kibibytes); split rows: 4 loads per wave of the
+    // 16 KiB tile, plus the mask (wave 0) or a dummy load (waves 1..3)
+    static constexpr int NA = PRESPLIT ? 1 : 1 + (32 * RPT * 4) / 1024;
+    static constexpr int NPW = PRESPLIT ? 5 : (NA + 3) / 4;  // aux loads per wave
+    static constexpr int SPL_OFF = X_BYTES;                   // split tile (PRESPLIT)
+    static constexpr int MASK_OFF = PRESPLIT ? X_BYTES + 16384 : X_BYTES;
+    static constexpr int DS_OFF = X_BYTES + 1024;             // fp32 dS rows (not PRESPLIT)
+    static constexpr int STAGE = PRESPLIT ? X_BYTES + 16384 + 2048 : X_BYTES + 4 * NPW * 1024;
+    static constexpr int NST = MAXT == 2 ? 3 : 4;           // ring depth
+    static constexpr int LDS = NST * STAGE;
 };
 
 template <int MAXT>
@@ -1326,7 +1337,6 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
     constexpr int RPT = C::RPT;
     extern __shared__ uint4 b2w_smem[];
     lds_char *smem = (lds_char *)b2w_smem;
-    lds_char *split = smem + C::NST * C::STAGE;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1338,6 +1348,7 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
     if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
     const int r = ad.r;
     const int nbt = (r + 15) >> 4;
+    const int rpa = 16 * (nbt <= 1 ? 1 : nbt <= 2 ? 2 : nbt <= 4 ? 4 : 8);  // the item's split row: 2 rpa bf16
     const float s = drop_scale(ad.p);
     const int nrows = row_hi - row_lo;
     const int nsb = (nrows + 31) / 32;
@@ -1346,20 +1357,21 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
     const sgpr4_t dX = make_desc(P.X + (size_t)row_lo * P.k, clampb((uint64_t)nrows * P.k * 2));
     const sgpr4_t dK = make_desc(has_mask ? P.keep + (size_t)row_lo * P.KW : P.keep,
                                  has_mask ? clampb((uint64_t)nrows * P.KW * 4) : 0u);
-    const sgpr4_t dD = make_desc(P.dS + (size_t)row_lo * P.RS, clampb((uint64_t)nrows * P.RS * 4));
+    const sgpr4_t dD = C::PRESPLIT
+        ? make_desc(P.dss + (size_t)row_lo * P.dss_ld, clampb((uint64_t)nrows * P.dss_ld * 2))
+        : make_desc(P.dS + (size_t)row_lo * P.RS, clampb((uint64_t)nrows * P.RS * 4));
 
-    // this lane's X offsets inside sub-block 0 (4 loads of 2 rows x 512 bytes)
-    uint32_t offX[4];
+    // this lane's X offsets inside sub-block 0 (4 loads of 2 rows x 512 bytes);
+    // the split rows use the same rows and chunk swizzle
+    uint32_t offX[4], offD[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int rr = 2 * (4 * wave + j) + (lane >> 5);
-        const int col = k0 + 8 * ((lane & 31) ^ swz512(rr));
+        const int c = (lane & 31) ^ swz512(rr);
+        const int col = k0 + 8 * c;
         offX[j] = col < P.k ? (uint32_t)(((size_t)rr * P.k + col) * 2) : kOOBL;
+        offD[j] = 8 * c < 2 * rpa ? (uint32_t)(((size_t)rr * P.dss_ld + 8 * c) * 2) : kOOBL;
     }
-    // aux slot q: 0 = mask words (row lane/2, words 4 (lane&1) .. +3 of the
-    // tile), 1 .. NA-1 = dS floats [(q-1) * 256 + 4 lane, +4) of the 32 x RPT
-    // block (row-major, ranks past r or RS read zeros); slots past NA are
-    // dummies loading zeros into the stage's spare kibibytes
     auto issue = [&](int sb, int stage) {
         const uint32_t base = lds0 + stage * C::STAGE;
         const bool live = sb < nsb;
@@ -1367,38 +1379,37 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             dma16(dX, (live && offX[j] != kOOBL) ? offX[j] + xo : kOOBL, base + (4 * wave + j) * 1024);
+        // mask words: row lane/2, words 4 (lane&1) .. +3 of the tile
+        auto mask_off = [&]() {
+            const int w0 = (k0 >> 5) + 4 * (lane & 1);
+            const int row = sb * 32 + (lane >> 1);
+            return (live && has_mask && w0 < P.KW && row < nrows) ? (uint32_t)(((size_t)row * P.KW + w0) * 4) : kOOBL;
+        };
+        if constexpr (C::PRESPLIT) {
+            const uint32_t so = (uint32_t)((size_t)sb * 32 * P.dss_ld * 2);
 #pragma unroll
-        for (int q0 = 0; q0 < C::NPW; ++q0) {
-            const int q = wave * C::NPW + q0;
-            const uint32_t dst = base + C::X_BYTES + q * 1024;
-            uint32_t off = kOOBL;
-            if (q == 0) {
-                const int w0 = (k0 >> 5) + 4 * (lane & 1);
-                const int row = sb * 32 + (lane >> 1);
-                if (live && has_mask && w0 < P.KW && row < nrows) off = (uint32_t)(((size_t)row * P.KW + w0) * 4);
-            } else if (q < C::NA) {
-                const int f = (q - 1) * 256 + 4 * lane;
-                const int row = sb * 32 + f / RPT, col = f % RPT;
-                if (live && row < nrows && col < r && col < P.RS) off = (uint32_t)(((size_t)row * P.RS + col) * 4);
+            for (int j = 0; j < 4; ++j) {
+                const int row = sb * 32 + 2 * (4 * wave + j) + (lane >> 5);
+                dma16(dD, (live && row < nrows && offD[j] != kOOBL) ? offD[j] + so : kOOBL,
+                      base + C::SPL_OFF + (4 * wave + j) * 1024);
             }
-            dma16(q == 0 ? dK : dD, off, dst);
-        }
-    };
-    // the shared tile: rows 8w .. 8w+7 of the sub-block's s*dS, split; lane l
-    // takes row 8w + l/8 and ranks RPL*(l%8) .. +RPL-1; hi parts go to columns
-    // 0 .. RPT-1 of the 512-byte tile row, lo parts to RPT .. 2RPT-1
-    auto coop_split = [&](const float *ds) {
-        constexpr int RPL = RPT / 8;
-        const int row = 8 * wave + (lane >> 3), c0 = RPL * (lane & 7);
+            // wave 0: the mask words; the others a dummy load into the kibibyte past them
+            dma16(dK, wave == 0 ? mask_off() : kOOBL, base + C::MASK_OFF + (wave == 0 ? 0 : 1024));
+        } else {
 #pragma unroll
-        for (int h = 0; h < RPL; h += 8) {
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = s * ds[row * RPT + c0 + h + e];
-            uint4 hi, lo;
-            split_frag(v, hi, lo);
-            *(uint4 *)(split + swz512_off(row, (c0 + h) >> 3)) = hi;
-            *(uint4 *)(split + swz512_off(row, (RPT + c0 + h) >> 3)) = lo;
+            for (int q0 = 0; q0 < C::NPW; ++q0) {
+                const int q = wave * C::NPW + q0;
+                const uint32_t dst = base + C::X_BYTES + q * 1024;
+                uint32_t off = kOOBL;
+                if (q == 0) {
+                    off = mask_off();
+                } else if (q < C::NA) {
+                    const int f = (q - 1) * 256 + 4 * lane;
+                    const int row = sb * 32 + f / RPT, col = f % RPT;
+                    if (live && row < nrows && col < r && col < P.RS) off = (uint32_t)(((size_t)row * P.RS + col) * 4);
+                }
+                dma16(q == 0 ? dK : dD, off, dst);
+            }
         }
     };
 
@@ -1408,7 +1419,6 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
     constexpr int NPS = 4 + C::NPW;  // loads per wave per stage
     auto body = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
-        constexpr bool SHARED = C::SPLIT_TILE && NB >= 4;
         f32x4_t acc[4][NB];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
@@ -1422,19 +1432,17 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
         for (int sb = 0; sb < nsb; ++sb) {
             issue(sb + C::NST - 1, lstage);
             const lds_char *xt = smem + stage * C::STAGE;
-            const uint32_t *mk = (const uint32_t *)(xt + C::X_BYTES);
-            const float *ds = (const float *)(xt + C::X_BYTES + 1024);
+            const uint32_t *mk = (const uint32_t *)(xt + C::MASK_OFF);
             // dS operand (N = rank): rows 8g .. 8g+7 of rank 16 bt + li, times s
             uint4 bhi[NB], blo[NB];
-            if constexpr (SHARED) {
-                coop_split(ds);
-                __syncthreads();  // the tile is whole (the last reads of the previous one were before the loop's barrier)
+            if constexpr (C::PRESPLIT) {
 #pragma unroll
                 for (int bt = 0; bt < NB; ++bt) {
-                    bhi[bt] = tile_rows8(split, 8 * g, bt, lane);
-                    blo[bt] = tile_rows8(split, 8 * g, RPT / 16 + bt, lane);
+                    bhi[bt] = tile_rows8(xt + C::SPL_OFF, 8 * g, bt, lane);
+                    blo[bt] = tile_rows8(xt + C::SPL_OFF, 8 * g, NB + bt, lane);
                 }
             } else {
+                const float *ds = (const float *)(xt + C::DS_OFF);
 #pragma unroll
                 for (int bt = 0; bt < NB; ++bt) {
                     float v[8];
@@ -1861,14 +1869,16 @@ __global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceParams P) {
 // exit at once; an adapter with no rows gets zeros).
 // ===========================================================================
 struct B1FinishParams {
-    const float *dspart;  // [nparts][m][RS]
+    const float *dspart;  // [nparts][m][RS] (nparts == 1: dS itself)
     int nparts;
     float *ds;
+    uint16_t *dss;        // optional: rows of [hi | lo] of s*dS for the dA pass and the dX epilogue
+    int dss_ld;
     int m, n, RS;
     const float *dbpart;  // [group][RS][n]
     RowWork work;         // B1 row groups (router table 2, or rows_per_chunk rows)
     int groups;           // single: number of row groups; multi: the table's capacity
-    int ds_wpg;           // dS work-groups per row group (0: no dS sum)
+    int ds_wpg;           // dS work-groups per row group (0: no dS pass)
     int db_gx;            // dB work-groups per adapter
 };
 
@@ -1883,25 +1893,44 @@ __global__ __launch_bounds__(256) void b1_finish_kernel(B1FinishParams P) {
         AdapterView ad;
         if (!resolve_chunk(P.work, grp, P.m, row_lo, row_hi, ad)) return;
         const int r = min(ad.r, P.RS);
+        // the split row of this group's adapter: hi of ranks 0 .. rpa-1, then
+        // their lo parts (rpa = 16 x the power-of-two 16-rank block count the
+        // dA pass runs for this rank); ranks past r are zero
+        const int nbt = (ad.r + 15) >> 4;
+        const int rpa = P.dss ? 16 * (nbt <= 1 ? 1 : nbt <= 2 ? 2 : nbt <= 4 ? 4 : 8) : 0;
+        const float s = drop_scale(ad.p);
+        const int W = max(P.RS, rpa);  // columns this pass covers per row
         const size_t ps = (size_t)P.m * P.RS;
-        const int total = (row_hi - row_lo) * P.RS;
+        const int total = (row_hi - row_lo) * W;
         for (int e = sub * 256 + tid; e < total; e += P.ds_wpg * 256) {
-            const int lr = e / P.RS, rr = e - lr * P.RS;
-            const size_t idx = (size_t)(row_lo + lr) * P.RS + rr;
+            const int lr = e / W, rr = e - lr * W;
+            const int row = row_lo + lr;
+            const size_t idx = (size_t)row * P.RS + rr;
             float v = 0.f;
             if (rr < r) {
                 const float *src = P.dspart + idx;
-                int q = 0;
-                for (; q + 8 <= P.nparts; q += 8) {
-                    float t[8];
+                if (P.nparts == 1) {
+                    v = *src;
+                } else {
+                    int q = 0;
+                    for (; q + 8 <= P.nparts; q += 8) {
+                        float t[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) t[u] = src[(size_t)(q + u) * ps];
+                        for (int u = 0; u < 8; ++u) t[u] = src[(size_t)(q + u) * ps];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) v += t[u];
+                        for (int u = 0; u < 8; ++u) v += t[u];
+                    }
+                    for (; q < P.nparts; ++q) v += src[(size_t)q * ps];
                 }
-                for (; q < P.nparts; ++q) v += src[(size_t)q * ps];
             }
-            P.ds[idx] = v;
+            if (P.nparts > 1 && rr < P.RS) P.ds[idx] = v;
+            if (rr < rpa) {
+                uint32_t hi, lo;
+                split_bf16(s * v, hi, lo);
+                uint16_t *drow = P.dss + (size_t)row * P.dss_ld;
+                drow[rr] = (uint16_t)hi;
+                drow[rpa + rr] = (uint16_t)lo;
+            }
         }
         return;
     }
@@ -2207,11 +2236,14 @@ hipError_t launch_b2(const void *X, const uint32_t *keep, const float *dS, int m
 }
 
 hipError_t launch_b2w(const void *X, const uint32_t *keep, const float *dS, int m, int k, int RS, int rows,
-                      const AdapterSource &src, int items, float *part, const int32_t *ad_items, hipStream_t stream) {
+                      const AdapterSource &src, int items, float *part, const int32_t *ad_items, hipStream_t stream,
+                      const uint16_t *dss, int dss_ld) {
     B2WParams P;
     P.X = (const uint16_t *)X;
     P.keep = keep;
     P.dS = dS;
+    P.dss = dss;
+    P.dss_ld = dss_ld;
     P.m = m;
     P.k = k;
     P.RS = RS;
@@ -2221,6 +2253,8 @@ hipError_t launch_b2w(const void *X, const uint32_t *keep, const float *dS, int 
     P.nct = cdiv(k, 256);
     P.part = part;
     const int mt = b2w_blocks(r_lds_of(src));
+    // above 32 ranks the rank side comes split from B1's finishing launch
+    if (mt >= 4 && (dss == nullptr || dss_ld < 32 * mt || (((uintptr_t)dss) & 15) != 0)) return hipErrorInvalidValue;
     (void)hipGetLastError();
     if (items > 0 && m > 0) {
         const dim3 grid((unsigned)items, (unsigned)P.nct);
@@ -2281,11 +2315,14 @@ hipError_t launch_grad_reduce(int which, const float *part, int m, int k, int n,
 }
 
 hipError_t launch_b1_reduce(const float *dSpart, int nparts, float *dS, const float *dBpart, int m, int n,
-                            int RS, const AdapterSource &src, int rows, int slots, hipStream_t stream) {
+                            int RS, const AdapterSource &src, int rows, int slots, hipStream_t stream,
+                            uint16_t *dss, int dss_ld) {
     B1FinishParams P;
     P.dspart = dSpart;
     P.nparts = nparts;
     P.ds = dS;
+    P.dss = dss;
+    P.dss_ld = dss_ld;
     P.m = m;
     P.n = n;
     P.RS = RS;
@@ -2293,8 +2330,10 @@ hipError_t launch_b1_reduce(const float *dSpart, int nparts, float *dS, const fl
     P.work = make_work(src, kTabB1);
     P.work.rows_per_chunk = rows;
     P.groups = src.table ? slots : cdiv(m, rows);
-    // one partial: B1 wrote dS itself.  Otherwise about 4 elements per thread.
-    P.ds_wpg = (nparts > 1 && m > 0) ? std::max(1, cdiv((long)rows * RS, 1024)) : 0;
+    // one partial and no split rows: B1 wrote dS itself, nothing to do.
+    // Otherwise about 4 elements per thread.
+    const int W = dss ? std::max(RS, 128) : RS;
+    P.ds_wpg = ((nparts > 1 || dss) && m > 0) ? std::max(1, cdiv((long)rows * W, 1024)) : 0;
     P.db_gx = std::max(1, cdiv((long)RS * n / 4, 256));
     const int nad = src.table ? src.num_adapters : 1;
     const size_t blocks = (size_t)P.groups * P.ds_wpg + (size_t)P.db_gx * nad;
