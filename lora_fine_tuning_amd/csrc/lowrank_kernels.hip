@@ -24,6 +24,12 @@ namespace lora {
 // non-empty segment with a valid adapter is cut into runs of at most
 // `rows` rows for each of up to three tables; one work-group scans the
 // segments.  A table with rows == 0 is skipped.
+// Chunks are ordered by the work their adapter's rank brings, heaviest first
+// (rank classes of 16-rank blocks: more than 4, 3-4, 2, 1), in segment order
+// within a class: a kernel whose grid is about one round of work-groups then
+// starts every heavy chunk at once instead of leaving the last segments'
+// chunks for a second round.  Every consumer is order-free (sums over a
+// table run in table order, which is fixed by the segment table).
 // ===========================================================================
 struct RouterTable {
     ChunkEntry *t;
@@ -35,52 +41,69 @@ struct RouterTables {
     RouterTable tab[3];
 };
 
+constexpr int kRankClasses = 4;
+__device__ __forceinline__ int rank_class(int r) {  // 3 = heaviest
+    const int nbt = (r + 15) >> 4;
+    return nbt <= 1 ? 0 : nbt <= 2 ? 1 : nbt <= 4 ? 2 : 3;
+}
+
 __global__ __launch_bounds__(1024) void router_kernel(const int64_t *seg_off, const int32_t *seg_ad,
                                                      int nseg, int m, const lora_adapter *adapters,
                                                      int nad, int r_cap, RouterTables T, int32_t *ad_items) {
-    __shared__ int sc[3][1024];
+    __shared__ int sc[3][kRankClasses][1024];
+    __shared__ int tot[3][kRankClasses];
     const int tid = threadIdx.x;
-    int carry[3] = {0, 0, 0};
     // work items of each adapter in the backward table (table 1), for the
     // fused per-adapter sums of the dA kernel
-    if (ad_items != nullptr) {
+    if (ad_items != nullptr)
         for (int i = tid; i < nad; i += 1024) ad_items[i] = 0;
-        __syncthreads();
-    }
-    for (int base = 0; base < nseg; base += 1024) {
-        const int s = base + tid;
-        int lo = 0, hi = 0, a = -1, nq[3] = {0, 0, 0};
-        if (s < nseg) {
-            const int64_t o0 = seg_off[s], o1 = seg_off[s + 1];
-            lo = (int)max((int64_t)0, min(o0, (int64_t)m));
-            hi = (int)max((int64_t)lo, min(o1, (int64_t)m));
-            a = seg_ad[s];
-            bool ok = a >= 0 && a < nad && hi > lo;
-            if (ok) {
-                const int r = adapters[a].r;
-                ok = r >= 1 && r <= r_cap;
-            }
-            if (ok)
+    if (tid < 3 * kRankClasses) tot[tid / kRankClasses][tid % kRankClasses] = 0;
+    // segment s: rows [lo, hi), adapter a, its rank class and chunk counts
+    auto seg_info = [&](int s, int &lo, int &hi, int &a, int &cls, int (&nq)[3]) {
+        lo = hi = 0;
+        a = -1;
+        cls = 0;
+        nq[0] = nq[1] = nq[2] = 0;
+        if (s >= nseg) return;
+        const int64_t o0 = seg_off[s], o1 = seg_off[s + 1];
+        lo = (int)max((int64_t)0, min(o0, (int64_t)m));
+        hi = (int)max((int64_t)lo, min(o1, (int64_t)m));
+        a = seg_ad[s];
+        if (a < 0 || a >= nad || hi <= lo) return;
+        const int r = adapters[a].r;
+        if (r < 1 || r > r_cap) return;
+        cls = rank_class(r);
 #pragma unroll
-                for (int j = 0; j < 3; ++j)
-                    nq[j] = T.tab[j].rows > 0 ? (hi - lo + T.tab[j].rows - 1) / T.tab[j].rows : 0;
-        }
+        for (int j = 0; j < 3; ++j) nq[j] = T.tab[j].rows > 0 ? (hi - lo + T.tab[j].rows - 1) / T.tab[j].rows : 0;
+    };
+    // A table of at most 64 segments (the usual case): one wave, one lane per
+    // segment, scans by lane shuffles and no work-group barrier in the scan.
+    if (nseg <= 64) {
+        __syncthreads();  // the ad_items reset is visible
+        if (tid >= 64) return;
+        int lo, hi, a, cls, nq[3];
+        seg_info(tid, lo, hi, a, cls, nq);
         if (ad_items != nullptr && nq[1] > 0) atomicAdd(&ad_items[a], nq[1]);
 #pragma unroll
-        for (int j = 0; j < 3; ++j) sc[j][tid] = nq[j];
-        __syncthreads();
-        for (int d = 1; d < 1024; d <<= 1) {
-            int v[3];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) v[j] = tid >= d ? sc[j][tid - d] : 0;
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < 3; ++j) sc[j][tid] += v[j];
-            __syncthreads();
-        }
-#pragma unroll
         for (int j = 0; j < 3; ++j) {
-            const int pos = carry[j] + sc[j][tid] - nq[j];
+            int incl[kRankClasses], total[kRankClasses];
+#pragma unroll
+            for (int c = 0; c < kRankClasses; ++c) {
+                int v = c == cls ? nq[j] : 0;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int u = __shfl_up(v, d);
+                    if (tid >= d) v += u;
+                }
+                incl[c] = v;
+                total[c] = __shfl(v, 63);
+            }
+            int pos = 0, all = 0;
+#pragma unroll
+            for (int c = kRankClasses - 1; c >= 0; --c) {  // heavier classes first
+                if (c == cls) pos = all + incl[c] - nq[j];
+                all += total[c];
+            }
             const int rows = T.tab[j].rows;
             for (int q = 0; q < nq[j]; ++q) {
                 if (pos + q < T.tab[j].cap) {
@@ -92,14 +115,91 @@ __global__ __launch_bounds__(1024) void router_kernel(const int64_t *seg_off, co
                     T.tab[j].t[pos + q] = e;
                 }
             }
-            carry[j] += sc[j][1023];
+            if (tid == 0 && rows > 0) T.tab[j].c[0] = min(all, T.tab[j].cap);
+        }
+        return;
+    }
+    __syncthreads();
+    // pass 1: chunks per table and class (integer sums: any order)
+    for (int s = tid; s < nseg; s += 1024) {
+        int lo, hi, a, cls, nq[3];
+        seg_info(s, lo, hi, a, cls, nq);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (nq[j] > 0) atomicAdd(&tot[j][cls], nq[j]);
+        if (ad_items != nullptr && nq[1] > 0) atomicAdd(&ad_items[a], nq[1]);
+    }
+    __syncthreads();
+    // first position of each class: the heavier classes come first
+    int cbase[3][kRankClasses], carry[3][kRankClasses];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        int acc = 0;
+#pragma unroll
+        for (int c = kRankClasses - 1; c >= 0; --c) {
+            cbase[j][c] = acc;
+            acc += tot[j][c];
+            carry[j][c] = 0;
+        }
+    }
+    // pass 2: positions by a scan per table and class over the segments
+    for (int base = 0; base < nseg; base += 1024) {
+        int lo, hi, a, cls, nq[3];
+        seg_info(base + tid, lo, hi, a, cls, nq);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int c = 0; c < kRankClasses; ++c) sc[j][c][tid] = c == cls ? nq[j] : 0;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {
+            int v[3][kRankClasses];
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int c = 0; c < kRankClasses; ++c) v[j][c] = tid >= d ? sc[j][c][tid - d] : 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int c = 0; c < kRankClasses; ++c) sc[j][c][tid] += v[j][c];
+            __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int rows = T.tab[j].rows;
+            int cb = 0, cc = 0, incl = 0;
+#pragma unroll
+            for (int c = 0; c < kRankClasses; ++c)
+                if (c == cls) {
+                    cb = cbase[j][c];
+                    cc = carry[j][c];
+                    incl = sc[j][c][tid];
+                }
+            const int pos = cb + cc + incl - nq[j];
+            for (int q = 0; q < nq[j]; ++q) {
+                if (pos + q < T.tab[j].cap) {
+                    ChunkEntry e;
+                    e.row_lo = lo + q * rows;
+                    e.row_hi = min(hi, lo + (q + 1) * rows);
+                    e.adapter = a;
+                    e.pad = 0;
+                    T.tab[j].t[pos + q] = e;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < kRankClasses; ++c) carry[j][c] += sc[j][c][1023];
         }
         __syncthreads();
     }
     if (tid == 0)
 #pragma unroll
         for (int j = 0; j < 3; ++j)
-            if (T.tab[j].rows > 0) T.tab[j].c[0] = min(carry[j], T.tab[j].cap);
+            if (T.tab[j].rows > 0) {
+                int total = 0;
+#pragma unroll
+                for (int c = 0; c < kRankClasses; ++c) total += tot[j][c];
+                T.tab[j].c[0] = min(total, T.tab[j].cap);
+            }
 }
 
 static RowWork make_work(const AdapterSource &src, WorkTable tab) {
@@ -514,12 +614,23 @@ struct F1W {
     static constexpr int RP = 16 * MAXT;
     static constexpr int UNIT = 64;                 // k columns per stage (two MFMA steps)
     static constexpr int X_BYTES = 64 * UNIT * 2;   // 64 rows
-    static constexpr int A_BYTES = UNIT * RP * 2;   // UNIT k-rows x RP ranks
-    static constexpr int STAGE = X_BYTES + A_BYTES;
-    static constexpr int NST = 3;
-    static constexpr int LDS = NST * STAGE;         // 2 work-groups per CU at RP = 128, 3 below
-    static constexpr int NAL = A_BYTES / 4096;      // A loads (1 KiB) per wave per stage
-    static constexpr int NPS = 2 + NAL;             // loads per wave per stage
+    static constexpr int LDS = 3 * (X_BYTES + UNIT * RP * 2);  // 2 work-groups per CU at RP = 128, 3 below
+};
+
+// The ring of a chunk whose adapter needs NB 16-rank blocks: a stage holds X
+// and A's 64 k-rows of 16 NB ranks (at least 2 KiB), and the ring takes as
+// many stages (at most 8) as the launch's LDS holds -- chunks of small rank
+// keep more of X in flight.  A loads: 1 KiB each, NB / 2 per wave (NB = 1:
+// waves 0 and 1 one each).
+template <int MAXT, int NB>
+struct F1WRing {
+    static constexpr int RPN = 16 * NB;
+    static constexpr int A_BYTES = F1W<MAXT>::UNIT * RPN * 2;
+    static constexpr int STAGE = F1W<MAXT>::X_BYTES + A_BYTES;
+    static constexpr int NST = F1W<MAXT>::LDS / STAGE < 8 ? F1W<MAXT>::LDS / STAGE : 8;
+    static constexpr int NAL = A_BYTES / 4096;      // A loads per wave per stage (NB >= 2)
+    static constexpr int NPS_LO = 2 + NAL;          // loads per wave per stage, waves 2 and 3
+    static constexpr int NPS_HI = NB == 1 ? 3 : NPS_LO;  // waves 0 and 1
 };
 
 // 32-byte chunk swizzle of A's slab rows (2*RP bytes): the 4 k-rows of a
@@ -570,41 +681,6 @@ __global__ __launch_bounds__(256) void f1w_kernel(F1WParams P) {
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         offX[j] = (16 * wave + row < nrows) ? (uint32_t)(((size_t)(16 * wave + row) * P.k + 8 * c) * 2) : kOOBL;
     }
-    auto issue = [&](int u, int st) {
-        const uint32_t base = lds0 + st * C::STAGE;
-        const int c0 = kb + UNIT * u;
-        const bool live = u < nu;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = 8 * j + (lane >> 3);
-            const int c = (lane & 7) ^ ((row >> 1) & 7);
-            const bool ok = live && offX[j] != kOOBL && c0 + 8 * c < ke;
-            dma16(dX, ok ? offX[j] + (uint32_t)c0 * 2u : kOOBL, base + wave * 2048 + j * 1024);
-        }
-        const uint32_t abase = base + C::X_BYTES;
-        if (avec) {
-#pragma unroll
-            for (int i = 0; i < C::NAL; ++i) {
-                const int q = wave * C::NAL + i;
-                const int pos = q * 1024 + lane * 16;
-                const int kr = pos / (2 * RP), within = pos % (2 * RP);
-                const int cl = (within >> 5) ^ f1w_swz<RP>(kr), h = (within >> 4) & 1;
-                const int rank = 16 * cl + 8 * h;
-                const bool ok = live && c0 + kr < ke && rank < r;
-                dma16(dA, ok ? (uint32_t)(((size_t)(c0 + kr) * r + rank) * 2) : kOOBL, abase + q * 1024);
-            }
-        } else {
-            // A neither 16-byte aligned nor of a rank divisible by 8: element copy
-            lds_char *dst = smem + st * C::STAGE + C::X_BYTES;
-            for (int idx = tid; idx < UNIT * RP; idx += 256) {
-                const int kr = idx / RP, rank = idx % RP;
-                uint16_t v = 0;
-                if (live && c0 + kr < ke && rank < r) v = ad.A[(size_t)(c0 + kr) * r + rank];
-                *(uint16_t *)(dst + kr * (2 * RP) + (((rank >> 4) ^ f1w_swz<RP>(kr)) << 5) + (rank & 15) * 2) = v;
-            }
-        }
-    };
-
     const int row = row_lo + 16 * wave + l16;
     const bool rvalid = 16 * wave + l16 < nrows;
     // Philox block of the lane's first element in a step at column c: (offset
@@ -613,19 +689,69 @@ __global__ __launch_bounds__(256) void f1w_kernel(F1WParams P) {
 
     auto body = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
+        using R = F1WRing<MAXT, NB>;
+        constexpr int RPN = R::RPN;
+        constexpr int NST = R::NST;
+        auto issue = [&](int u, int st) {
+            const uint32_t base = lds0 + st * R::STAGE;
+            const int c0 = kb + UNIT * u;
+            const bool live = u < nu;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int row = 8 * j + (lane >> 3);
+                const int c = (lane & 7) ^ ((row >> 1) & 7);
+                const bool ok = live && offX[j] != kOOBL && c0 + 8 * c < ke;
+                dma16(dX, ok ? offX[j] + (uint32_t)c0 * 2u : kOOBL, base + wave * 2048 + j * 1024);
+            }
+            const uint32_t abase = base + C::X_BYTES;
+            if (avec) {
+                auto a_load = [&](int q) {
+                    const int pos = q * 1024 + lane * 16;
+                    const int kr = pos / (2 * RPN), within = pos % (2 * RPN);
+                    const int cl = (within >> 5) ^ f1w_swz<RPN>(kr), h = (within >> 4) & 1;
+                    const int rank = 16 * cl + 8 * h;
+                    const bool ok = live && c0 + kr < ke && rank < r;
+                    dma16(dA, ok ? (uint32_t)(((size_t)(c0 + kr) * r + rank) * 2) : kOOBL, abase + q * 1024);
+                };
+                if constexpr (NB == 1) {
+                    if (wave < 2) a_load(wave);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < R::NAL; ++i) a_load(wave * R::NAL + i);
+                }
+            } else {
+                // A neither 16-byte aligned nor of a rank divisible by 8: element copy
+                lds_char *dst = smem + st * R::STAGE + C::X_BYTES;
+                for (int idx = tid; idx < UNIT * RPN; idx += 256) {
+                    const int kr = idx / RPN, rank = idx % RPN;
+                    uint16_t v = 0;
+                    if (live && c0 + kr < ke && rank < r) v = ad.A[(size_t)(c0 + kr) * r + rank];
+                    *(uint16_t *)(dst + kr * (2 * RPN) + (((rank >> 4) ^ f1w_swz<RPN>(kr)) << 5) + (rank & 15) * 2) = v;
+                }
+            }
+        };
+        // stage u+1 landed: every load but those of the NST-2 stages issued after it
+        auto wait_ring = [&]() {
+            if constexpr (R::NPS_HI != R::NPS_LO) {
+                if (wave < 2) wait_vmcnt<R::NPS_HI * (NST - 2)>();
+                else wait_vmcnt<R::NPS_LO * (NST - 2)>();
+            } else {
+                wait_vmcnt<R::NPS_LO * (NST - 2)>();
+            }
+        };
         f32x4_t acc[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < C::NST - 1; ++q) issue(q, q);
-        wait_vmcnt<C::NPS * (C::NST - 2)>();
+        for (int q = 0; q < NST - 1; ++q) issue(q, q);
+        wait_ring();
         __syncthreads();
-        int st = 0, ls = C::NST - 1;
+        int st = 0, ls = NST - 1;
         uint32_t kw = 0;  // byte t: this lane's keep bits of step t of the 128-column pair of units
         for (int u = 0; u < nu; ++u) {
-            issue(u + C::NST - 1, ls);
-            const lds_char *xt = smem + st * C::STAGE + wave * 2048;
-            const lds_char *at = smem + st * C::STAGE + C::X_BYTES;
+            issue(u + NST - 1, ls);
+            const lds_char *xt = smem + st * R::STAGE + wave * 2048;
+            const lds_char *at = smem + st * R::STAGE + C::X_BYTES;
             const int c = kb + UNIT * u;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -638,11 +764,11 @@ __global__ __launch_bounds__(256) void f1w_kernel(F1WParams P) {
                 }
                 kw |= (c + 32 * t + 8 * g < ke ? byte : 0u) << (8 * (2 * (u & 1) + t));  // bits past the slice stay zero
                 const int kr = 32 * t + 8 * g + (l16 >> 2);
-                const int sw = f1w_swz<RP>(kr);
+                const int sw = f1w_swz<RPN>(kr);
 #pragma unroll
                 for (int bt = 0; bt < NB; ++bt) {
-                    const lds_char *pa = at + kr * (2 * RP) + ((bt ^ sw) << 5) + 8 * (l16 & 3);
-                    const uint2 lo = lds_read_tr4(pa), hi = lds_read_tr4(pa + 4 * (2 * RP));
+                    const lds_char *pa = at + kr * (2 * RPN) + ((bt ^ sw) << 5) + 8 * (l16 & 3);
+                    const uint2 lo = lds_read_tr4(pa), hi = lds_read_tr4(pa + 4 * (2 * RPN));
                     acc[bt] = mfma16x16x32(xm, make_uint4(lo.x, lo.y, hi.x, hi.y), acc[bt]);
                 }
             }
@@ -658,10 +784,10 @@ __global__ __launch_bounds__(256) void f1w_kernel(F1WParams P) {
                 if (rvalid && c + 32 * g < ke) P.keep_bits[(size_t)row * P.KW + ((c >> 5) + g)] = kw;
                 kw = 0;
             }
-            wait_vmcnt<C::NPS * (C::NST - 2)>();
+            wait_ring();
             __syncthreads();
-            st = st == C::NST - 1 ? 0 : st + 1;
-            ls = ls == C::NST - 1 ? 0 : ls + 1;
+            st = st == NST - 1 ? 0 : st + 1;
+            ls = ls == NST - 1 ? 0 : ls + 1;
         }
         wait_vmcnt<0>();
         // rows 4g + v of the wave, rank 16 bt + l16

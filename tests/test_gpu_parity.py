@@ -257,6 +257,9 @@ MULTI_CASES = [
      [0, 300, 600], [0, 1]),                                   # a 16-row band meeting ranks 128 and 120 (8 chunks)
     (520, 136, 264, [128, 64, 8], [2.0, 0.5, 4.0], [0.1, 0.0, 0.3],
      [0, 200, 390, 520], [1, 0, 2]),                           # bands meeting ranks 64 | 128 and 128 | 8
+    (1210, 264, 136, [8, 40, 128], [2.0, 1.0, 0.5], [0.1, 0.2, 0.1],
+     [0] + [11 * i + (i % 3) for i in range(1, 110)] + [1210], [i % 3 for i in range(110)]),
+                                                               # 110 segments (past one wave of the router)
 ]
 
 
