@@ -96,6 +96,14 @@ __device__ __forceinline__ void mfma16x16x32_vacc(f32x4_t &acc, const uint4 &a, 
                  : "+v"(acc)
                  : "v"(__builtin_bit_cast(i32x4_t, a)), "v"(__builtin_bit_cast(i32x4_t, b)));
 }
+// acc = a * b (the accumulator input is the constant 0, so no VALU write of
+// it can be in flight when the MFMA reads it)
+__device__ __forceinline__ void mfma16x16x32_vfirst(f32x4_t &acc, const uint4 &a, const uint4 &b) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
+                 : "=v"(acc)
+                 : "v"(__builtin_bit_cast(i32x4_t, a)), "v"(__builtin_bit_cast(i32x4_t, b)));
+}
 
 // m ? b : a bit by bit (m is 0 or ~0, wave-uniform).  Written as one
 // v_bfi_b32 so the compiler cannot turn a select of two fragment registers
@@ -1002,7 +1010,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             };
             const int swl = (l16 >> 1) & 7;
             // rank-deep MFMAs of chunk j (the row side in f) into acc2
-            auto mfma_slot = [&](int j, int nc0, const float4 (&f)[2], f32x4_t (&acc2)[NT16]) {
+            auto mfma_slot = [&](int j, int nc0, const float4 (&f)[2], f32x4_t (&acc2)[NT16], auto first_c) {
                 const bool second = j >= nc0;
                 const int rr0 = 32 * (second ? j - nc0 : j);
                 uint4 hi, lo;
@@ -1018,13 +1026,23 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 }
                 const int q = ((rr0 >> 5) & 1) * 4 + lg;  // 8-rank chunk inside the slab
                 const lds_char *sb = (const lds_char *)smem + slab_at[(second ? 2 : 0) + (rr0 >> 6)];
+                uint4 cf[NT16];
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) {
                     const int c = wn * 128 + tn * 16 + l16;
-                    const uint4 cf = *(const uint4 *)(sb + c * 128 + ((q ^ swl) << 4));
-                    acc2[tn] = mfma16x16x32(cf, hi, acc2[tn]);
-                    acc2[tn] = mfma16x16x32(cf, lo, acc2[tn]);
+                    cf[tn] = *(const uint4 *)(sb + c * 128 + ((q ^ swl) << 4));
                 }
+                // the band's accumulators stay in VGPRs (the AGPRs hold the
+                // product's tiles): no copies in and out around each chunk; the
+                // hi and lo MFMAs of one accumulator are 8 MFMAs apart
+                mfma_src_ready(hi, lo);
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) {
+                    if constexpr (decltype(first_c)::value) mfma16x16x32_vfirst(acc2[tn], cf[tn], hi);
+                    else mfma16x16x32_vacc(acc2[tn], cf[tn], hi);
+                }
+#pragma unroll
+                for (int tn = 0; tn < NT16; ++tn) mfma16x16x32_vacc(acc2[tn], cf[tn], lo);
             };
             load_band(0, 0);
             wait_vmcnt<0>();
@@ -1038,14 +1056,18 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 f32x4_t acc2[NT16];
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) acc2[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                // the first chunk's MFMAs start the accumulators (zero above
+                // only for a band with no chunk)
+                if (nsl > 0) mfma_slot(0, nc0, rf[cur][0], acc2, T_{});
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (j < nsl) mfma_slot(j, nc0, rf[cur][j], acc2);
+                for (int j = 1; j < 4; ++j)
+                    if (j < nsl) mfma_slot(j, nc0, rf[cur][j], acc2, F_{});
                 for (int j = 4; j < nsl; ++j) {  // a band meeting both items
                     float4 f[2];
                     load_slot(tm, j, nc0, f);
-                    mfma_slot(j, nc0, f, acc2);
+                    mfma_slot(j, nc0, f, acc2, F_{});
                 }
+                mfma_drain();  // the band MFMAs' results are read below
                 // masked sum into the band's staging rows (rows past M and
                 // columns past N are staged too; the stores drop them)
                 lds_char *sbnd = stg + (tm & 1) * 4096;
