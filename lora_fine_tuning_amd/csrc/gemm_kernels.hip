@@ -136,16 +136,16 @@ struct ExtItem {
     float scale;
 };
 
-// Rank-deep MFMA step, row side: fp32 S/dS of `row` for ranks rr0 + 8*(lane/16)
-// .. +7, times `scale`, split into hi/lo fragments; rows outside [lo, hi) and
-// ranks past r read as zero (out-of-range buffer offsets, no branches).  rS
-// starts at row `row0` (the wave's first row), so offsets stay small.
-// `vec`: r and RS are multiples of 8 and Sx is 16-byte aligned, so the 8
-// values are two aligned 16-byte loads.
-__device__ __forceinline__ void row_ext_frags(const GemmParams &P, __amdgpu_buffer_rsrc_t rS, int row0,
-                                              const ExtItem &it, int row, int rr0, int lane, bool vec,
-                                              uint4 &hi, uint4 &lo) {
-    float v[8];
+// Rank-deep MFMA step, row side: row_ext_load reads fp32 S/dS of `row` for
+// ranks rr0 + 8*(lane/16) .. +7; rows outside [lo, hi) and ranks past r read
+// as zero (out-of-range buffer offsets, no branches).  rS starts at row `row0`
+// (the wave's first row), so offsets stay small.  `vec`: r and RS are
+// multiples of 8 and Sx is 16-byte aligned, so the 8 values are two aligned
+// 16-byte loads.  row_ext_split multiplies them by the item's scale and splits
+// them into hi/lo fragments; row_ext_frags does both.
+__device__ __forceinline__ void row_ext_load(const GemmParams &P, __amdgpu_buffer_rsrc_t rS, int row0,
+                                             const ExtItem &it, int row, int rr0, int lane, bool vec,
+                                             float (&v)[8]) {
     const bool ok = row >= it.lo && row < it.hi;
     const int rb = rr0 + 8 * (lane >> 4);
     const uint32_t base = (uint32_t)((row - row0) * P.RS + rb) * 4u;
@@ -162,9 +162,22 @@ __device__ __forceinline__ void row_ext_frags(const GemmParams &P, __amdgpu_buff
             v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, off, 0, 0));
         }
     }
+}
+
+// The loaded values times the item's scale, as hi / lo bf16 fragments.
+__device__ __forceinline__ void row_ext_split(const ExtItem &it, const float (&v)[8], uint4 &hi, uint4 &lo) {
+    float w[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= it.scale;
-    split_frag(v, hi, lo);
+    for (int e = 0; e < 8; ++e) w[e] = v[e] * it.scale;
+    split_frag(w, hi, lo);
+}
+
+__device__ __forceinline__ void row_ext_frags(const GemmParams &P, __amdgpu_buffer_rsrc_t rS, int row0,
+                                              const ExtItem &it, int row, int rr0, int lane, bool vec,
+                                              uint4 &hi, uint4 &lo) {
+    float v[8];
+    row_ext_load(P, rS, row0, it, row, rr0, lane, vec, v);
+    row_ext_split(it, v, hi, lo);
 }
 
 // Rank-deep step, column side: 8 consecutive ranks of output column `col`
@@ -994,16 +1007,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
                 f[0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, off, 0, 0));
                 f[1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rS, ok ? off + 16u : kOOB, 0, 0));
             };
-            float4 rf[2][4][2];
+            // chunk 0 of bands 0..3 is loaded before the slabs are waited for
+            // (one round trip to memory for them), that of band tm + 4 once
+            // band tm's first MFMAs have read its slot (four bands ahead);
+            // chunks 1..3 and the mask words of a band are loaded during the
+            // band before (the mask words are needed only after its MFMAs)
+            float4 rf0[4][2], rfx[2][3][2];
             uint4 kw[2];
-            int nc0b[2], nslb[2];
-            auto load_band = [&](int tm, int slot) {
+            auto load_head = [&](int tm) {
                 const int nc0 = band_nc0(tm), nsl = band_nsl(tm, nc0);
-                nc0b[slot] = nc0;
-                nslb[slot] = nsl;
+                if (nsl > 0) load_slot(tm, 0, nc0, rf0[tm & 3]);
+            };
+            auto load_tail = [&](int tm, int slot) {
+                const int nc0 = band_nc0(tm), nsl = band_nsl(tm, nc0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (j < nsl) load_slot(tm, j, nc0, rf[slot][j]);
+                for (int j = 1; j < 4; ++j)
+                    if (j < nsl) load_slot(tm, j, nc0, rfx[slot][j - 1]);
                 kw[slot] = has_keep ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                                  rK, (uint32_t)((tm * 16 + l16) * P.KW + (wcol0 >> 5)) * 4u, 0, 0))
                                     : make_uint4(~0u, ~0u, ~0u, ~0u);
@@ -1044,24 +1063,27 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) mfma16x16x32_vacc(acc2[tn], cf[tn], lo);
             };
-            load_band(0, 0);
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) load_head(tm);
+            load_tail(0, 0);
             wait_vmcnt<0>();
             __syncthreads();  // the slabs landed
             lds_char *stg = (lds_char *)smem + wave * 8192;
 #pragma unroll
             for (int tm = 0; tm < NT16; ++tm) {
                 const int cur = tm & 1;
-                if (tm + 1 < NT16) load_band(tm + 1, cur ^ 1);
-                const int nc0 = nc0b[cur], nsl = nslb[cur];
+                if (tm + 1 < NT16) load_tail(tm + 1, cur ^ 1);
+                const int nc0 = band_nc0(tm), nsl = band_nsl(tm, nc0);
                 f32x4_t acc2[NT16];
 #pragma unroll
                 for (int tn = 0; tn < NT16; ++tn) acc2[tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 // the first chunk's MFMAs start the accumulators (zero above
                 // only for a band with no chunk)
-                if (nsl > 0) mfma_slot(0, nc0, rf[cur][0], acc2, T_{});
+                if (nsl > 0) mfma_slot(0, nc0, rf0[tm & 3], acc2, T_{});
+                if (tm + 4 < NT16) load_head(tm + 4);
 #pragma unroll
                 for (int j = 1; j < 4; ++j)
-                    if (j < nsl) mfma_slot(j, nc0, rf[cur][j], acc2, F_{});
+                    if (j < nsl) mfma_slot(j, nc0, rfx[cur][j - 1], acc2, F_{});
                 for (int j = 4; j < nsl; ++j) {  // a band meeting both items
                     float4 f[2];
                     load_slot(tm, j, nc0, f);
@@ -1137,6 +1159,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             // back transposed (as the fast epilogue does); else 2-byte loads
             const bool bstage = (P.N & 7) == 0 && (((uintptr_t)it.w) & 15) == 0;
             for (int rr0 = 0; rr0 < it.r; rr0 += 32) {
+                // the row side of all 8 bands is loaded first, so the chunk
+                // waits for one round trip to memory, not one per band
+                float sv[NT16][8];
+#pragma unroll
+                for (int tm = 0; tm < NT16; ++tm) row_ext_load(P, rS, wrow0, it, wrow0 + tm * 16 + l16, rr0, lane, rvec, sv[tm]);
                 uint4 cf[NT16];
                 if (bstage) {
                     lds_char *bs = (lds_char *)smem + NST * STAGE_BYTES + wave * 8192;
@@ -1166,7 +1193,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
                 for (int tm = 0; tm < NT16; ++tm) {
                     uint4 hi, lo;
-                    row_ext_frags(P, rS, wrow0, it, wrow0 + tm * 16 + l16, rr0, lane, rvec, hi, lo);
+                    row_ext_split(it, sv[tm], hi, lo);
                     mfma_src_ready(hi, lo);
 #pragma unroll
                     for (int tn = 0; tn < NT16; ++tn) {
