@@ -216,6 +216,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ext_rsrc(const GemmParams &P, 
     return make_rsrc(it.w + (EPI == 1 ? (size_t)min(col0, P.N) : (size_t)min(col0, P.N) * it.r), total - skip);
 }
 
+// Every field of an item as a wave-uniform value (SGPRs).
+__device__ __forceinline__ ExtItem uniform_item(const ExtItem &it) {
+    ExtItem u;
+    u.lo = __builtin_amdgcn_readfirstlane(it.lo);
+    u.hi = __builtin_amdgcn_readfirstlane(it.hi);
+    u.r = __builtin_amdgcn_readfirstlane(it.r);
+    u.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, it.scale)));
+    const uint64_t w = (uint64_t)(uintptr_t)it.w;
+    const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)w), wh = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
+    u.w = (const uint16_t *)(uintptr_t)(((uint64_t)wh << 32) | wl);
+    return u;
+}
+
 template <int EPI, bool MULTI>
 __device__ __forceinline__ bool get_item(const GemmParams &P, int s, ExtItem &it) {
     if (!MULTI) {
@@ -236,6 +249,10 @@ __device__ __forceinline__ bool get_item(const GemmParams &P, int s, ExtItem &it
     it.r = ad.r;
     it.w = (const uint16_t *)(EPI == 1 ? ad.B : ad.A);
     it.scale = EPI == 1 ? ad.alpha : drop_scale(ad.p);
+    // s is the same in every lane at every call, so the item is too; saying
+    // so keeps its fields in SGPRs (a buffer resource built from VGPR fields
+    // turns each load through it into a loop over the distinct values)
+    it = uniform_item(it);
     return true;
 }
 
@@ -261,18 +278,6 @@ struct TileItems {
     int rp[2];      // ranks rounded up to a multiple of 32
 };
 
-// Every field of an item as a wave-uniform value (SGPRs).
-__device__ __forceinline__ ExtItem uniform_item(const ExtItem &it) {
-    ExtItem u;
-    u.lo = __builtin_amdgcn_readfirstlane(it.lo);
-    u.hi = __builtin_amdgcn_readfirstlane(it.hi);
-    u.r = __builtin_amdgcn_readfirstlane(it.r);
-    u.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, it.scale)));
-    const uint64_t w = (uint64_t)(uintptr_t)it.w;
-    const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)w), wh = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
-    u.w = (const uint16_t *)(uintptr_t)(((uint64_t)wh << 32) | wl);
-    return u;
-}
 
 template <bool MULTI>
 __device__ __forceinline__ bool plan_tile_items(const GemmParams &P, int m0, TileItems &ti) {
@@ -1159,21 +1164,35 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams P) {
             // back transposed (as the fast epilogue does); else 2-byte loads
             const bool bstage = (P.N & 7) == 0 && (((uintptr_t)it.w) & 15) == 0;
             for (int rr0 = 0; rr0 < it.r; rr0 += 32) {
-                // the row side of all 8 bands is loaded first, so the chunk
-                // waits for one round trip to memory, not one per band
-                float sv[NT16][8];
-#pragma unroll
-                for (int tm = 0; tm < NT16; ++tm) row_ext_load(P, rS, wrow0, it, wrow0 + tm * 16 + l16, rr0, lane, rvec, sv[tm]);
-                uint4 cf[NT16];
+                // B's staging loads, then the row side of all 8 bands (the
+                // form chosen once, outside the band loop, so each band's
+                // loads do not wait on the other form's), then B's LDS
+                // writes: the chunk waits for one round trip to memory
+                lds_char *bs = (lds_char *)smem + NST * STAGE_BYTES + wave * 8192;
+                uint4 bv[8];
                 if (bstage) {
-                    lds_char *bs = (lds_char *)smem + NST * STAGE_BYTES + wave * 8192;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int q = lane + 64 * j, rr = q >> 4, c = q & 15;
                         const uint32_t off = (rr0 + rr < it.r && wcol0 + 8 * c < P.N)
                             ? ((uint32_t)(rr0 + rr) * (uint32_t)P.N + 8u * c) * 2u : kOOB;
-                        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
-                        *(uint4 *)(bs + rr * 256 + ((c ^ swz_w(rr)) << 4)) = v;
+                        bv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
+                    }
+                }
+                float sv[NT16][8];
+                if (rvec) {
+#pragma unroll
+                    for (int tm = 0; tm < NT16; ++tm) row_ext_load(P, rS, wrow0, it, wrow0 + tm * 16 + l16, rr0, lane, true, sv[tm]);
+                } else {
+#pragma unroll
+                    for (int tm = 0; tm < NT16; ++tm) row_ext_load(P, rS, wrow0, it, wrow0 + tm * 16 + l16, rr0, lane, false, sv[tm]);
+                }
+                uint4 cf[NT16];
+                if (bstage) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int q = lane + 64 * j, rr = q >> 4, c = q & 15;
+                        *(uint4 *)(bs + rr * 256 + ((c ^ swz_w(rr)) << 4)) = bv[j];
                     }
                     const int kr = 8 * lg + (l16 >> 2);
                     const int swr = swz_w(kr);
