@@ -26,14 +26,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
-// Split v into bf16 hi + lo with v ~= hi + lo to ~2^-17 relative.
-__device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo) {
-    hi = f32_to_bf16_rne(v);
-    lo = f32_to_bf16_rne(v - bf16_to_f32(hi));
-}
-
-__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
-
 // Two fp32 values -> packed bf16 pair, round to nearest even (one gfx950
 // v_cvt_pk_bf16_f32; agrees with f32_to_bf16_rne on finite inputs).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -41,6 +33,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef float f2_t __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, bf16x2_t));
 }
+
+// Split v into bf16 hi + lo with v ~= hi + lo to ~2^-17 relative (both halves
+// rounded to nearest even; v - hi is exact in fp32).
+__device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo) {
+    hi = pack_bf16x2(v, 0.f) & 0xFFFFu;
+    lo = pack_bf16x2(v - bf16_to_f32(hi), 0.f) & 0xFFFFu;
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
+
 
 // ---------------------------------------------------------------------------
 // MFMA: D = A*B + C with 8 bf16 per lane for each operand.
@@ -91,11 +93,18 @@ __device__ __forceinline__ void mfma_src_ready(uint4 &a) {
 
 // Eight fp32 values -> hi and lo bf16 fragments.
 __device__ __forceinline__ void split_frag(const float v[8], uint4 &hi, uint4 &lo) {
-    uint32_t h[8], l[8];
+    // pairs through v_cvt_pk_bf16_f32: the hi pair, each element's residual
+    // against its hi half, the lo pair (the same bits as split_bf16 per element)
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split_bf16(v[e], h[e], l[e]);
-    hi = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
-    lo = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+    for (int p = 0; p < 4; ++p) {
+        h[p] = pack_bf16x2(v[2 * p], v[2 * p + 1]);
+        const float r0 = v[2 * p] - __uint_as_float(h[p] << 16);
+        const float r1 = v[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u);
+        l[p] = pack_bf16x2(r0, r1);
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // One half of split_frag chosen per lane: the hi parts, or (want_lo) the lo
