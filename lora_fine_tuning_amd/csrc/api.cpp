@@ -232,8 +232,10 @@ struct FwdPlan {
 
 // Ranks up to 32: F1 covers all of k inside each work-group (KS = 1).
 // Ranks 33..128: 64-row chunks share A, and k is cut into KS slices
-// (multiples of 128 columns) so the grid has about 512 work-groups; the
-// slices' partials are added by a second launch.  Larger ranks: k in slices
+// (multiples of 128 columns) so the grid has about 512 work-groups (1024 for
+// k >= 16384, where a slice's partial is under 2% of its X bytes and the
+// second round of work-groups hides the first's latency); the slices'
+// partials are added by a second launch.  Larger ranks: k in slices
 // too (about 1024 work-groups), partials summed by a second pass.  KS depends
 // on m and k only, so one segment of the mixed form slices as the single
 // form does.
@@ -245,7 +247,7 @@ FwdPlan plan_fwd(int64_t m, int64_t k, int32_t RS, bool multi, int32_t nseg) {
     const int rl = ((RS + 15) / 16) * 16;
     p.f1w = f1w_ok(rl, k);
     const int kslices = cdiv(k, kF1KSub);
-    int KS = std::max(1, std::min(kslices, cdiv(p.f1w ? 512 : 1024, std::max(1, cdiv(m, kF1Rows)))));
+    int KS = std::max(1, std::min(kslices, cdiv(p.f1w ? (k >= 16384 ? 1024 : 512) : 1024, std::max(1, cdiv(m, kF1Rows)))));
     if (!p.f1w && f1_streaming(rl, k)) KS = 1;
     const int per = cdiv(kslices, KS);
     p.ksl = per * kF1KSub;

@@ -32,11 +32,21 @@ inline bool f1_rank64(int r_lds, bool multi) {
 
 // Rows per B2 work item (the dA partials are one per item): 256, or taller
 // when the grid (items x 256-column tiles of k x rank tiles) would still have
-// about 512 work-groups -- fewer partials for wide k or many rank tiles.
+// about 512 work-groups -- fewer partials for wide k or many rank tiles -- or
+// when the partials would otherwise rival X in bytes (high ranks).
 inline int b2_rows(int64_t m, int64_t k, int r_lds) {
     const int rt = r_lds > 128 ? (r_lds + 31) / 32 : 1;
     const int64_t want = m * ((k + 255) / 256) * rt / 512;
     int64_t rows = std::max<int64_t>(kBwdRows, (want + 31) / 32 * 32);
+    if (r_lds <= 128) {
+        // the single-pass form's dA partials (a k x RP block per item) stay at
+        // most a quarter of the item's X bytes (rows >= 8 RP) while the grid
+        // keeps at least 256 work-groups
+        const int nb = (r_lds + 15) / 16;
+        const int64_t rp = 16 * (nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : 8);
+        const int64_t wg_cap = std::max<int64_t>(kBwdRows, m * ((k + 255) / 256) / 256 / 32 * 32);
+        rows = std::max<int64_t>(rows, std::min<int64_t>(8 * rp, wg_cap));
+    }
     rows = std::min<int64_t>(rows, std::max<int64_t>(kBwdRows, (m + 31) / 32 * 32));
     // the kernels address an item's rows of X with 32-bit offsets
     const int64_t cap = ((int64_t(1) << 31) - 1) / (2 * std::max<int64_t>(k, 1)) / 32 * 32;
@@ -136,6 +146,9 @@ inline B1Shape b1_shape(int64_t m, int64_t n, int r_lds, int RS, bool multi, int
         int64_t nrg = std::max<int64_t>(1, 512 / s.CT);
         nrg = std::min<int64_t>(nrg, std::max<int64_t>(1, (m + 31) / 32));
         int64_t rows = std::max<int64_t>(32, 32 * (((m + nrg - 1) / nrg + 31) / 32));
+        // a row group's dB partial (r x n fp32) at most half the bytes of its
+        // dY rows: rows >= 4 r
+        rows = std::max<int64_t>(rows, 32 * ((4 * (int64_t)r_lds + 31) / 32));
         s.rows = (int)std::min(rows, maxrows);
     }
     // mixed adapters: the router cuts each segment into runs of `rows`
