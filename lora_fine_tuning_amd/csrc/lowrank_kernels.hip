@@ -1376,7 +1376,9 @@ __global__ __launch_bounds__(256) void b2s_kernel(B2Params P) {
                 for (int q = 0; q < 4; ++q) {
                     const uint32_t w0 = mk[(8 * g + 2 * q) * 8 + (cb >> 1)];
                     const uint32_t w1 = mk[(8 * g + 2 * q + 1) * 8 + (cb >> 1)];
-                    m[q] = (((w0 >> bit) & 1u) ? 0x0000FFFFu : 0u) | (((w1 >> bit) & 1u) ? 0xFFFF0000u : 0u);
+                    const uint32_t e0 = (uint32_t)__builtin_amdgcn_sbfe((int)w0, bit, 1);
+                    const uint32_t e1 = (uint32_t)__builtin_amdgcn_sbfe((int)w1, bit, 1);
+                    m[q] = (e0 & 0x0000FFFFu) | (e1 & 0xFFFF0000u);
                 }
                 xf = make_uint4(xf.x & m[0], xf.y & m[1], xf.z & m[2], xf.w & m[3]);
             }
@@ -1588,7 +1590,11 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
                     for (int q = 0; q < 4; ++q) {
                         const uint32_t w0 = mk[(8 * g + 2 * q) * 8 + (cb >> 1)];
                         const uint32_t w1 = mk[(8 * g + 2 * q + 1) * 8 + (cb >> 1)];
-                        mm[q] = (((w0 >> bit) & 1u) ? 0x0000FFFFu : 0u) | (((w1 >> bit) & 1u) ? 0xFFFF0000u : 0u);
+                        // each keep bit sign-extended to a whole word, the pair
+                        // merged into one 16-bit mask per element (3 instructions)
+                        const uint32_t e0 = (uint32_t)__builtin_amdgcn_sbfe((int)w0, bit, 1);
+                        const uint32_t e1 = (uint32_t)__builtin_amdgcn_sbfe((int)w1, bit, 1);
+                        mm[q] = (e0 & 0x0000FFFFu) | (e1 & 0xFFFF0000u);
                     }
                     xf = make_uint4(xf.x & mm[0], xf.y & mm[1], xf.z & mm[2], xf.w & mm[3]);
                 }
