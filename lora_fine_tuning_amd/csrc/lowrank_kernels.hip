@@ -1469,11 +1469,23 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
-    const int ct = blockIdx.y, k0 = ct * 256;
+    // Work order: consecutive work-groups go to the eight XCDs in turn, so with
+    // a multiple of 8 column tiles XCD j takes column tiles j*nct/8 .. +nct/8-1
+    // of every item, item by item; an item's split rows are then fetched into
+    // one XCD's L2 once and read from there by its nct/8 tiles (otherwise
+    // the tiles of an item land on different XCDs, far apart in time).
+    int item = blockIdx.x, ct = blockIdx.y;
+    if ((P.nct & 7) == 0) {
+        const int lin = blockIdx.x + blockIdx.y * gridDim.x;
+        const int ncj = P.nct >> 3, local = lin >> 3;
+        item = local / ncj;
+        ct = (lin & 7) * ncj + local % ncj;
+    }
+    const int k0 = ct * 256;
 
     int row_lo, row_hi;
     AdapterView ad;
-    if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
+    if (!resolve_chunk(P.work, item, P.m, row_lo, row_hi, ad)) return;
     const int r = ad.r;
     const int nbt = (r + 15) >> 4;
     const int rpa = 16 * (nbt <= 1 ? 1 : nbt <= 2 ? 2 : nbt <= 4 ? 4 : 8);  // the item's split row: 2 rpa bf16
@@ -1612,7 +1624,7 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
         wait_vmcnt<0>();
         // this item's partial: columns ct*256 .. +255 of its [nct*256][16 NB]
         // block (the item's slot holds nct*256*RPT floats)
-        float *pp = P.part + (size_t)blockIdx.x * P.nct * 256 * RPT + (size_t)ct * 256 * (16 * NB);
+        float *pp = P.part + (size_t)item * P.nct * 256 * RPT + (size_t)ct * 256 * (16 * NB);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
