@@ -1459,6 +1459,14 @@ struct B2W {
     static constexpr int LDS = NST * STAGE;
 };
 
+// Word c (0..7) of row t (0..31) of a 32 x 32-byte mask tile whose 16-byte
+// slots are permuted: row-half s = 2 t + c / 4 sits in slot s ^ (((t >> 3) & 3) << 2).
+// Rows 8g + j of the four 16-lane groups g then fall in four different bank
+// ranges (unpermuted they are 256 bytes apart: the same banks).
+__device__ __forceinline__ int mask_word(int t, int c) {
+    return (((2 * t + (c >> 2)) ^ (((t >> 3) & 3) << 2)) << 2) + (c & 3);
+}
+
 template <int MAXT>
 __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
     using C = B2W<MAXT>;
@@ -1519,10 +1527,13 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             dma16(dX, (live && offX[j] != kOOBL) ? offX[j] + xo : kOOBL, base + (4 * wave + j) * 1024);
-        // mask words: row lane/2, words 4 (lane&1) .. +3 of the tile
+        // mask words: lane l fills the 16-byte slot l of the stage's mask tile
+        // with words 4 h .. 4 h + 3 of tile row t, where 2 t + h = l ^ (((l >> 4) & 3) << 2)
+        // (mask_word below reads them back)
         auto mask_off = [&]() {
-            const int w0 = (k0 >> 5) + 4 * (lane & 1);
-            const int row = sb * 32 + (lane >> 1);
+            const int s = lane ^ (((lane >> 4) & 3) << 2);
+            const int w0 = (k0 >> 5) + 4 * (s & 1);
+            const int row = sb * 32 + (s >> 1);
             return (live && has_mask && w0 < P.KW && row < nrows) ? (uint32_t)(((size_t)row * P.KW + w0) * 4) : kOOBL;
         };
         if constexpr (C::PRESPLIT) {
@@ -1600,8 +1611,8 @@ __global__ __launch_bounds__(256) void b2w_kernel(B2WParams P) {
                     uint32_t mm[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const uint32_t w0 = mk[(8 * g + 2 * q) * 8 + (cb >> 1)];
-                        const uint32_t w1 = mk[(8 * g + 2 * q + 1) * 8 + (cb >> 1)];
+                        const uint32_t w0 = mk[mask_word(8 * g + 2 * q, cb >> 1)];
+                        const uint32_t w1 = mk[mask_word(8 * g + 2 * q + 1, cb >> 1)];
                         // each keep bit sign-extended to a whole word, the pair
                         // merged into one 16-bit mask per element (3 instructions)
                         const uint32_t e0 = (uint32_t)__builtin_amdgcn_sbfe((int)w0, bit, 1);
