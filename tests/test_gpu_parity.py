@@ -60,6 +60,8 @@ SINGLE_CASES = [
     (300, 264, 136, 80, 1.0, 0.1),     # ranks past 64 with a ragged last column tile of dX
     (200, 136, 8, 4, 0.0, 0.5),        # alpha 0 (the LoRA term and its gradients vanish), n = 8
     (128, 256, 264, 16, 2.0, 0.95),    # heavy dropout: scale 20
+    (300, 2048, 264, 64, 2.0, 0.1),    # 8 column tiles of k: the dA pass's XCD-aware work order
+    (520, 4096, 136, 16, 1.0, 0.2),    # 16 column tiles of k, rank 16
 ]
 
 
@@ -257,6 +259,8 @@ MULTI_CASES = [
      [0, 300, 600], [0, 1]),                                   # a 16-row band meeting ranks 128 and 120 (8 chunks)
     (520, 136, 264, [128, 64, 8], [2.0, 0.5, 4.0], [0.1, 0.0, 0.3],
      [0, 200, 390, 520], [1, 0, 2]),                           # bands meeting ranks 64 | 128 and 128 | 8
+    (700, 2048, 136, [16, 64, 128], [2.0, 1.0, 0.5], [0.1, 0.0, 0.2],
+     [0, 200, 450, 700], [2, 0, 1]),                           # 8 column tiles of k: XCD-aware dA order
     (1210, 264, 136, [8, 40, 128], [2.0, 1.0, 0.5], [0.1, 0.2, 0.1],
      [0] + [11 * i + (i % 3) for i in range(1, 110)] + [1210], [i % 3 for i in range(110)]),
                                                                # 110 segments (past one wave of the router)
@@ -340,13 +344,25 @@ def test_multi_parity_packed_microbatch():
         check_close(f"dB[{a}]", g["dB"][a], o["dB"][a])
 
 
-def test_multi_single_segment_equals_single_bitwise():
-    m, k, n, r = 640, 512, 264, 16
+@pytest.mark.parametrize("k,r", [(512, 16), (2048, 16), (512, 32), (2048, 64), (4096, 128), (512, 200)])
+def test_multi_single_segment_equals_single_bitwise(k, r):
+    # k = 2048 and 4096 give 8 and 16 column tiles of 256: the dA pass then
+    # takes its XCD-aware work order (k = 512: grid order).  The mask, S and
+    # every gradient match bit for bit.  Y does too, except for ranks 33..128,
+    # where the single-adapter forward accumulates alpha S B as extra K stages
+    # of the GEMM and the mixed form adds it after the K loop: one rounding
+    # apart (at most one bf16 step).
+    m, n = 640, 264
+    log(f"single vs one-segment mixed, bitwise: m={m} k={k} n={n} r={r}")
     X, W, As, Bs, dY = multi_case(m, k, n, [r], seed=7)
     s = gpu_single(X, W, As[0], Bs[0], dY, 2.0, 0.1, 3, 16)
     mu = gpu_multi(X, W, As, Bs, [2.0], [0.1], [0, m], [0], dY, 3, 16)
     assert torch.equal(s["keep"], mu["keep"])
-    assert torch.equal(s["Y"], mu["Y"])
+    if 32 < r <= 128:
+        a, b = s["Y"].float(), mu["Y"].float()
+        assert torch.all((a - b).abs() <= 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 2.0 ** -16), "Y beyond one bf16 step"
+    else:
+        assert torch.equal(s["Y"], mu["Y"])
     assert torch.equal(s["S"], mu["S"])
     assert torch.equal(s["dX"], mu["dX"])
     assert torch.equal(s["dA"], mu["dA"][0])
