@@ -1769,12 +1769,25 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     constexpr int RLP = RL + 4;
     float *red = (float *)(smem + NST * STAGE);
 
+    // Work order (mixed adapters): consecutive work-groups go to the eight XCDs
+    // in turn; with a multiple of 8 column tiles, within each rank tile XCD j
+    // takes column tiles j*CT/8 .. +CT/8-1 of every row group, group by group,
+    // so a row group's S rows (r_max floats each) are fetched into one XCD's L2
+    // once for its CT/8 tiles instead of once per tile.  The single-adapter
+    // form keeps the grid order (measured faster there).
+    int grp = blockIdx.x, ct = blockIdx.y;
+    if ((gridDim.y & 7) == 0 && P.work.chunks != nullptr) {
+        const int p = blockIdx.x + gridDim.x * blockIdx.y;  // within the rank tile's plane
+        const int ncj = gridDim.y >> 3, local = p >> 3;
+        grp = local / ncj;
+        ct = (p & 7) * ncj + local % ncj;
+    }
     int row_lo, row_hi;
     AdapterView ad;
-    if (!resolve_chunk(P.work, blockIdx.x, P.m, row_lo, row_hi, ad)) return;
+    if (!resolve_chunk(P.work, grp, P.m, row_lo, row_hi, ad)) return;
     const int r = ad.r;
     const float alpha = ad.alpha;
-    const int ct = blockIdx.y, n0 = ct * 256 * CW;
+    const int n0 = ct * 256 * CW;
     const int tid = threadIdx.x, lane = tid & 63;
     // rank tile (tiled launches, RL = 32): ranks r0 .. r0+31; S rows staged as
     // 32 floats (else whole RS-float rows, r0 = 0)
@@ -1940,7 +1953,7 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     }
     wait_vmcnt<0>();
 
-    float *dbp = P.dBpart + (size_t)blockIdx.x * P.RS * P.n;
+    float *dbp = P.dBpart + (size_t)grp * P.RS * P.n;
 #pragma unroll
     for (int bt = 0; bt < MAXT; ++bt)
 #pragma unroll
