@@ -1776,7 +1776,8 @@ __global__ __launch_bounds__(256) void b1v_kernel(B1Params P) {
     // once for its CT/8 tiles instead of once per tile.  The single-adapter
     // form keeps the grid order (measured faster there).
     int grp = blockIdx.x, ct = blockIdx.y;
-    if ((gridDim.y & 7) == 0 && P.work.chunks != nullptr) {
+    if ((gridDim.y & 7) == 0 && P.work.chunks != nullptr &&
+        (uint64_t)gridDim.x * gridDim.y < (uint64_t(1) << 31)) {
         const int p = blockIdx.x + gridDim.x * blockIdx.y;  // within the rank tile's plane
         const int ncj = gridDim.y >> 3, local = p >> 3;
         grp = local / ncj;
