@@ -654,9 +654,8 @@ extern "C" lora_status multi_lora_check_segments(const int64_t *seg_off_host, co
 // DoRA norm
 // ---------------------------------------------------------------------------
 extern "C" size_t lora_dora_norm_workspace_size(int64_t k, int64_t n, int32_t r) {
-    (void)r;
     if (k <= 0 || n <= 0 || k >= (1LL << 31) || n >= (1LL << 31)) return 0;
-    const DoraPlan pl = dora_plan(k, n);
+    const DoraPlan pl = dora_plan(k, n, r);
     return (size_t)pl.splits * (size_t)n * sizeof(float);
 }
 
@@ -673,7 +672,7 @@ extern "C" lora_status lora_dora_norm(const void *W, const void *A, const void *
     REQ_PTR(norm, 4);
     if ((int64_t)(r + 32) * n * 2 >= (1LL << 31) || k * (int64_t)r * 2 >= (1LL << 31))
         return fail(LORA_ERR_UNSUPPORTED, "A or B exceeds 2 GiB");
-    const DoraPlan pl = dora_plan(k, n);
+    const DoraPlan pl = dora_plan(k, n, r);
     const size_t need = (size_t)pl.splits * (size_t)n * sizeof(float);
     if (workspace_bytes < need)
         return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);

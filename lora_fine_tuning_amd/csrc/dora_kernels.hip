@@ -11,10 +11,12 @@
 // nothing dense is stored and no cancellation between the three terms occurs.
 //
 // Work-group = a range of W's rows (a split) x 256 columns; four waves of 64
-// columns each.  W's rows stream through a 3-stage ring of direct-to-LDS loads
-// (with A's matching rows); B's fragments for the work-group's columns are
-// loaded once.  Each split writes per-column partial sums of squares; a second
-// kernel adds the splits in a fixed order and takes the square root.
+// columns each, or for ranks above 128 eight waves, two per 64 columns, each
+// taking one 16-row half of every 32-row sub-block.  W's rows stream through a
+// 3-stage ring of direct-to-LDS loads (with A's matching rows); B's fragments
+// for the work-group's columns are loaded once.  Each split writes per-column
+// partial sums of squares; a second kernel adds the splits in a fixed order and
+// takes the square root.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -33,34 +35,48 @@ struct DoraParams {
 };
 
 constexpr int DORA_SUB = 32 * 512;  // one 32-row x 256-column bf16 tile
-constexpr int DORA_NST = 3;
+constexpr int DORA_NST_BIG = 3;  // ring stages above rank 128
+constexpr int dora_nst(int rpq) { return rpq == 8 ? DORA_NST_BIG : 3; }
 
-constexpr int dora_nai(int rpq) { return rpq <= 2 ? 1 : rpq / 2; }  // 1 KiB A loads per wave per stage
+// Waves per work-group.  Above rank 128 B's staging fills a CU's LDS, so one
+// work-group runs per CU; eight waves then put two on each SIMD, and one
+// wave's matrix work overlaps the other's LDS reads and waits.
+constexpr int dora_nw(int rpq) { return rpq == 8 ? 8 : 4; }
+constexpr int dora_nai(int rpq) { return rpq <= 2 ? 1 : rpq / 2; }  // 1 KiB A loads per stage, per 4 waves
 constexpr int dora_stage(int rpq) { return DORA_SUB + 4 * dora_nai(rpq) * 1024; }
 // LDS: for r <= 32 B's one chunk sits past the ring, so both load together
 // (two work-groups still share a CU); larger ranks stage all of B's 32-rank
 // chunks in the space the ring uses afterwards
 constexpr bool dora_b_apart(int rpq) { return rpq == 1; }
-constexpr int dora_b_off(int rpq) { return dora_b_apart(rpq) ? DORA_NST * dora_stage(rpq) : 0; }
+constexpr int dora_b_off(int rpq) { return dora_b_apart(rpq) ? dora_nst(rpq) * dora_stage(rpq) : 0; }
 constexpr int dora_lds(int rpq) {
-    return dora_b_apart(rpq) ? DORA_NST * dora_stage(rpq) + DORA_SUB
-         : DORA_NST * dora_stage(rpq) > rpq * DORA_SUB ? DORA_NST * dora_stage(rpq) : rpq * DORA_SUB;
+    // (eight waves: 1 KiB past the ring for the half sums)
+    return dora_b_apart(rpq) ? dora_nst(rpq) * dora_stage(rpq) + DORA_SUB
+         : (dora_nst(rpq) * dora_stage(rpq) + (dora_nw(rpq) == 8 ? 1024 : 0) > rpq * DORA_SUB
+                ? dora_nst(rpq) * dora_stage(rpq) + (dora_nw(rpq) == 8 ? 1024 : 0)
+                : rpq * DORA_SUB);
 }
 
 // RPQ: rank steps of 32 (ceil(r / 32)); AVEC: r % 8 == 0 (16-byte A reads)
 template <int RPQ, bool AVEC>
-__global__ __launch_bounds__(256) void dora_norm_kernel(DoraParams P) {
-    constexpr int NAI = dora_nai(RPQ);
+__global__ __launch_bounds__(64 * dora_nw(RPQ)) void dora_norm_kernel(DoraParams P) {
+    constexpr int NW = dora_nw(RPQ);
+    constexpr int NH = 8 / NW;               // 16-row halves per wave
+    constexpr int NJ = 16 / NW;              // 1 KiB W (and B) loads per wave per stage
+    constexpr int NAI = dora_nai(RPQ) * 4 / NW;
     constexpr int STAGE = dora_stage(RPQ);
+    constexpr int DORA_NST = dora_nst(RPQ);
     // A's rows go through LDS only when r % 8 == 0: then every 16-byte piece of
     // a sub-block's A image lies wholly inside A (a piece straddling A's end
     // would read as zero); otherwise A's elements are read from global memory
-    constexpr int NDMA = 4 + (AVEC ? NAI : 0);  // direct-to-LDS loads per wave per stage
+    constexpr int NDMA = NJ + (AVEC ? NAI : 0);  // direct-to-LDS loads per wave per stage
     extern __shared__ uint4 dora_smem[];
     lds_char *smem = (lds_char *)dora_smem;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cw = wave & 3;   // the wave's 64 columns
+    const int hw = wave >> 2;  // its half when NH == 1
     const int g = lane >> 4, li = lane & 15;
     const int r = P.r;
     const int row_lo = (int)blockIdx.x * P.rows;
@@ -75,12 +91,12 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(DoraParams P) {
     const sgpr4_t dA = make_desc(P.A + (size_t)row_lo * r, (uint32_t)((uint64_t)nrows * r * 2));
     const uint32_t asb = 32u * (uint32_t)r * 2u;  // A bytes of one 32-row sub-block
 
-    // tile loads: instruction j of wave w fills LDS rows 2(4w+j), +1 (512 B
+    // tile loads: instruction j of wave w fills LDS rows 2(NJ w + j), +1 (512 B
     // each); LDS chunk (lane & 31) of row rr holds global chunk (lane & 31) ^ swz512(rr)
-    uint32_t offT[4];
+    uint32_t offT[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int rr = 2 * (4 * wave + j) + (lane >> 5);
+    for (int j = 0; j < NJ; ++j) {
+        const int rr = 2 * (NJ * wave + j) + (lane >> 5);
         const int col = n0 + 8 * ((lane & 31) ^ swz512(rr));
         offT[j] = col < P.n ? (uint32_t)(rr * P.n + col) * 2u : kOOBL;
     }
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(DoraParams P) {
     uint32_t offA[NAI];  // image byte -> sub-block byte of A, per load (kOOBL past the image)
 #pragma unroll
     for (int q = 0; q < NAI; ++q) {
-        const uint32_t b = (uint32_t)(4 * q + wave) * 1024u + (uint32_t)lane * 16u;
+        const uint32_t b = (uint32_t)(NW * q + wave) * 1024u + (uint32_t)lane * 16u;
         if (!AVEC || b >= asb) {
             offA[q] = kOOBL;
         } else {
@@ -109,19 +125,19 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(DoraParams P) {
         const bool live = sb < nsb;
         const uint32_t wo = live ? (uint32_t)sb * 32u * (uint32_t)P.n * 2u : 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dma16(dW, (!live || offT[j] == kOOBL) ? kOOBL : offT[j] + wo, base + (4 * wave + j) * 1024);
+        for (int j = 0; j < NJ; ++j)
+            dma16(dW, (!live || offT[j] == kOOBL) ? kOOBL : offT[j] + wo, base + (NJ * wave + j) * 1024);
         if constexpr (AVEC) {
 #pragma unroll
             for (int q = 0; q < NAI; ++q)
                 dma16(dA, (live && offA[q] != kOOBL) ? (uint32_t)sb * asb + offA[q] : kOOBL,
-                      base + DORA_SUB + (uint32_t)(4 * q + wave) * 1024u);
+                      base + DORA_SUB + (uint32_t)(NW * q + wave) * 1024u);
         }
     };
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(P.A + (size_t)row_lo * r, (uint64_t)nrows * r * 2);
 
     // B fragments (MFMA column operand): ranks 32q + 8g .. +7 of column
-    // n0 + 64w + 16b + li; all 32-rank chunks land in LDS together (chunk q
+    // n0 + 64 cw + 16b + li; all 32-rank chunks land in LDS together (chunk q
     // at q * 16 KiB), then the ring reuses the space
     constexpr int BOFF = dora_b_off(RPQ);
     uint4 bfr[RPQ][4];
@@ -129,8 +145,8 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(DoraParams P) {
     for (int q = 0; q < RPQ; ++q) {
         const uint32_t bo = (uint32_t)q * 32u * (uint32_t)P.n * 2u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dma16(dB, offT[j] == kOOBL ? kOOBL : offT[j] + bo, lds0 + BOFF + q * DORA_SUB + (4 * wave + j) * 1024);
+        for (int j = 0; j < NJ; ++j)
+            dma16(dB, offT[j] == kOOBL ? kOOBL : offT[j] + bo, lds0 + BOFF + q * DORA_SUB + (NJ * wave + j) * 1024);
     }
     if constexpr (dora_b_apart(RPQ)) {
 #pragma unroll
@@ -143,7 +159,7 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(DoraParams P) {
 #pragma unroll
     for (int q = 0; q < RPQ; ++q)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) bfr[q][b] = tile_rows8(smem + BOFF + q * DORA_SUB, 8 * g, 4 * wave + b, lane);
+        for (int b = 0; b < 4; ++b) bfr[q][b] = tile_rows8(smem + BOFF + q * DORA_SUB, 8 * g, 4 * cw + b, lane);
     if constexpr (!dora_b_apart(RPQ)) __syncthreads();  // the ring rewrites the space
 
     // The A B tile of a 16-row half h comes from MFMA with row i' = 4c + v
@@ -186,35 +202,42 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(DoraParams P) {
         issue(sb + DORA_NST - 1, lstage);
         const lds_char *wt = smem + stage * STAGE;
         const lds_char *at = wt + DORA_SUB;
-        uint4 afr[2][RPQ];
+        uint4 afr[NH][RPQ];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int q = 0; q < RPQ; ++q) afr[h][q] = a_frag(at, sb, h, q);
-        // eight independent accumulation chains (4 column blocks x 2 halves)
-        f32x4_t d0[4], d1[4];
+            for (int q = 0; q < RPQ; ++q) afr[h][q] = a_frag(at, sb, NH == 2 ? h : hw, q);
+        // 4 NH independent accumulation chains (4 column blocks x the wave's halves)
+        f32x4_t d[NH][4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) d0[b] = d1[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) d[h][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < RPQ; ++q)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                d0[b] = mfma16x16x32(afr[0][q], bfr[q][b], d0[b]);
-                d1[b] = mfma16x16x32(afr[1][q], bfr[q][b], d1[b]);
-            }
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int h = 0; h < NH; ++h) d[h][b] = mfma16x16x32(afr[h][q], bfr[q][b], d[h][b]);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const uint4 wv = tile_rows8(wt, 8 * g, 4 * wave + b, lane);
-            const uint32_t wh[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint32_t w0 = v & 1 ? wh[v >> 1] >> 16 : wh[v >> 1] & 0xFFFFu;        // row 8c + v
-                const uint32_t w1 = v & 1 ? wh[2 + (v >> 1)] >> 16 : wh[2 + (v >> 1)] & 0xFFFFu;  // row 8c + 4 + v
-                const float x0 = bf16_to_f32(w0) + alpha * d0[b][v];
-                const float x1 = bf16_to_f32(w1) + alpha * d1[b][v];
-                sq[b] += x0 * x0;
-                sq[b] += x1 * x1;
+            // W rows 8c + 4h + v of the lane's column, two to a word
+            uint32_t wh[2 * NH];
+            if constexpr (NH == 2) {
+                const uint4 wv = tile_rows8(wt, 8 * g, 4 * cw + b, lane);
+                wh[0] = wv.x, wh[1] = wv.y, wh[2] = wv.z, wh[3] = wv.w;
+            } else {
+                const uint2 wv = tile_rows4(wt, 8 * g + 4 * hw, 4 * cw + b, lane);
+                wh[0] = wv.x, wh[1] = wv.y;
             }
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t wb = v & 1 ? wh[2 * h + (v >> 1)] >> 16 : wh[2 * h + (v >> 1)] & 0xFFFFu;
+                    const float x = bf16_to_f32(wb) + alpha * d[h][b][v];
+                    sq[b] += x * x;
+                }
         }
         wait_vmcnt<NDMA * (DORA_NST - 2)>();
         __syncthreads();
@@ -223,14 +246,33 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(DoraParams P) {
     }
     wait_vmcnt<0>();
 
-    // the four lane groups hold disjoint rows of the same column
+    // the four lane groups hold disjoint rows of the same column; with one
+    // half per wave, the second half's sums pass through LDS past the ring
+    // (the loop's last barrier follows every wave's last read of the ring,
+    // and the space past it held only B)
+    float s[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        float s = sq[b];
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        const int col = n0 + 64 * wave + 16 * b + li;
-        if (g == 0 && col < P.n) P.part[(size_t)blockIdx.x * P.n + col] = s;
+        s[b] = sq[b];
+        s[b] += __shfl_xor(s[b], 16);
+        s[b] += __shfl_xor(s[b], 32);
+    }
+    if constexpr (NH == 1) {
+        static_assert(dora_lds(RPQ) >= DORA_NST * STAGE + 1024, "no room for the half sums");
+        float *hs = (float *)(smem + DORA_NST * STAGE);
+        if (hw == 1 && g == 0) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) hs[64 * cw + 16 * b + li] = s[b];
+        }
+        __syncthreads();
+        if (hw == 1) return;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) s[b] += hs[64 * cw + 16 * b + li];
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int col = n0 + 64 * cw + 16 * b + li;
+        if (g == 0 && col < P.n) P.part[(size_t)blockIdx.x * P.n + col] = s[b];
     }
 }
 
@@ -249,7 +291,7 @@ void launch_dora_t(const DoraParams &P, dim3 grid, hipStream_t stream) {
     if (lds > 64 * 1024)
         (void)hipFuncSetAttribute((const void *)dora_norm_kernel<RPQ, AVEC>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((dora_norm_kernel<RPQ, AVEC>), grid, dim3(256), lds, stream, P);
+    hipLaunchKernelGGL((dora_norm_kernel<RPQ, AVEC>), grid, dim3(64 * dora_nw(RPQ)), lds, stream, P);
 }
 
 }  // namespace

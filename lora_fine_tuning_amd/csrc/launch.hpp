@@ -222,15 +222,18 @@ hipError_t launch_gemm_kext(const void *X, const void *W, void *Y, int M, int N,
 size_t gemm_lds_bytes();
 
 // DoRA norm of W + alpha A B per output feature (column): splits of W's rows
-// (multiples of 32) so that about 512 work-groups of 256 columns run, each
+// (multiples of 32) so that about 512 work-groups of 256 columns run (two per
+// CU), or above rank 128, where one work-group fills a CU, DORA_WGS_BIG; each
 // split's rows * n * 2 bytes under 2^31.
 struct DoraPlan {
     int splits, rows;
 };
-inline DoraPlan dora_plan(int64_t k, int64_t n) {
+constexpr int64_t DORA_WGS_BIG = 256;
+inline DoraPlan dora_plan(int64_t k, int64_t n, int r) {
     const int64_t ctiles = (n + 255) / 256;
     const int64_t maxrows = std::max<int64_t>(32, ((int64_t(1) << 31) - 1) / (2 * n) / 32 * 32);
-    int64_t splits = std::max<int64_t>(1, std::min<int64_t>((512 + ctiles - 1) / ctiles, (k + 255) / 256));
+    const int64_t wgs = r > 128 ? DORA_WGS_BIG : 512;
+    int64_t splits = std::max<int64_t>(1, std::min<int64_t>((wgs + ctiles - 1) / ctiles, (k + 255) / 256));
     int64_t rows = 32 * (((k + splits - 1) / splits + 31) / 32);
     rows = std::min(rows, maxrows);
     splits = (k + rows - 1) / rows;
