@@ -101,6 +101,10 @@ DORA_CASES = [
     (300, 512, 256, 1.0),
     (1, 8, 3, 2.0),           # a single row, one 8-column group
     (4104, 256, 8, 2.0),      # several row splits, the last one ragged
+    # above rank 128 (eight waves, one half of each sub-block per wave)
+    (520, 776, 129, 2.0),     # the first such rank: element-wise A reads
+    (1000, 1032, 203, -0.7),  # ragged sub-block and column tile, element-wise A reads
+    (8200, 264, 160, 1.5),    # 33 row splits, the last one 8 rows
 ]
 
 
