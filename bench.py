@@ -142,6 +142,22 @@ def hbm_report(args):
                                         "frac_of_8TBs": round(read_gbs / PEAK_HBM_GBS, 4)}}), flush=True)
 
 
+def copy_calibration(torch, args):
+    """Ends a counter run with device copies of known size (--copy-calib-mib),
+    the scale for the byte counters."""
+    if not args.copy_calib_mib:
+        return
+    nel = args.copy_calib_mib * (1 << 20) // 4
+    src = torch.ones(nel, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + written per copy, 3 copies",
+          file=sys.stderr, flush=True)
+    del src, dst
+
+
 def dora_report(args):
     """DoRA norm on the page's 8192 x 8192 weight shape.  One pass over W is the
     compulsory traffic (bytes = 2kn + 2kr + 2rn + 4n per call); the kernel is
@@ -624,6 +640,7 @@ def main():
         return
     if args.dora:
         dora_report(args)
+        copy_calibration(torch, args)
         return
     if args.hbm:
         hbm_report(args)
@@ -686,17 +703,7 @@ def main():
             gbs = b / (kernels[nm]["avg_us"] * 1e-6) / 1e9
             hbm[nm] = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
-    if args.copy_calib_mib:
-        # ends a counter run with device copies of known size (byte-counter scale)
-        nel = args.copy_calib_mib * (1 << 20) // 4
-        src = torch.ones(nel, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + written per copy, 3 copies",
-              file=sys.stderr, flush=True)
-        del src, dst
+    copy_calibration(torch, args)
 
     # ---- the LLaMA-8B projections (r 16), each alone and both as one step
     extra = {}

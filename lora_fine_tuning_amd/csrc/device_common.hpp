@@ -330,11 +330,6 @@ __device__ __forceinline__ uint4 tile_rows8(const lds_char *tile, int row0, int 
     const uint2 hi = lds_read_tr4(tile + swz512_off(row + 4, chunk) + (a & 1) * 8);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
-// The first half of the above alone: rows row0 .. row0+3 (row0 % 4 == 0).
-__device__ __forceinline__ uint2 tile_rows4(const lds_char *tile, int row0, int cb, int lane) {
-    const int a = lane & 15;
-    return lds_read_tr4(tile + swz512_off(row0 + (a >> 2), 2 * cb + ((a & 3) >> 1)) + (a & 1) * 8);
-}
 constexpr uint32_t kOOBL = 0x80000000u;  // an offset beyond every descriptor range
 
 // ---------------------------------------------------------------------------

@@ -57,6 +57,13 @@ constexpr int dora_lds(int rpq) {
                 : rpq * DORA_SUB);
 }
 
+// Half of tile_rows8: rows row0 .. row0+3 (row0 % 4 == 0) of column
+// 16*cb + (lane % 16), 4 bf16 per lane.
+__device__ __forceinline__ uint2 tile_rows4(const lds_char *tile, int row0, int cb, int lane) {
+    const int a = lane & 15;
+    return lds_read_tr4(tile + swz512_off(row0 + (a >> 2), 2 * cb + ((a & 3) >> 1)) + (a & 1) * 8);
+}
+
 // RPQ: rank steps of 32 (ceil(r / 32)); AVEC: r % 8 == 0 (16-byte A reads)
 template <int RPQ, bool AVEC>
 __global__ __launch_bounds__(64 * dora_nw(RPQ)) void dora_norm_kernel(DoraParams P) {
