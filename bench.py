@@ -161,7 +161,8 @@ def copy_calibration(torch, args):
 def dora_report(args):
     """DoRA norm on the page's 8192 x 8192 weight shape.  One pass over W is the
     compulsory traffic (bytes = 2kn + 2kr + 2rn + 4n per call); the kernel is
-    reported against HBM.  Beside it: the eager PyTorch form that builds the
+    reported against HBM, timed as the median of flushed event-timed trials.
+    Beside it: the eager PyTorch form that builds the
     dense A B (torch.linalg.vector_norm(W + alpha A B, dim=0) in fp32), and
     the oracle on a column sample."""
     import torch
@@ -184,33 +185,20 @@ def dora_report(args):
         def eager():
             return torch.linalg.vector_norm(W.float() + 2.0 * (A.float() @ B.float()), dim=0)
 
-        for _ in range(args.warmup):
-            fused()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            fused()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        # the pass over W alone: HIP events the library records on its launch stream
+        # median of flushed event-timed trials (W, A and B come from HBM each
+        # time, not from the Infinity Cache, which would hold a 128 MiB W)
+        timer = Timer(torch, torch.cuda.current_stream())
+        ms = timer.median(fused, args.steps, args.warmup)
+        ms_b2b = sum(timer.trials(fused, args.steps, 0, flush=False)) / args.steps
+        # the pass over W alone: HIP events the library records on its launch
+        # stream, over flushed trials
         lf.lora_profiling_enable(True, capacity=4 * args.steps + 16)
         lf.lora_profiling_reset()
-        for _ in range(args.steps):
-            fused()
+        timer.trials(fused, args.steps, 0)
         c, tot = lf.lora_profiling_query("dora_norm_pass")
         kern_ms = tot / max(c, 1)
         lf.lora_profiling_enable(False)
-        for _ in range(2):
-            eager()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(5):
-            eager()
-        e1.record()
-        torch.cuda.synchronize()
-        eager_ms = e0.elapsed_time(e1) / 5
+        eager_ms = timer.median(eager, 5, 2)
         nbytes = 2 * k * n + 2 * k * r + 2 * r * n + 4 * n
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         line = {"metric": "DoRA norm of W + alpha A B per output feature, GB/s of compulsory traffic",
@@ -219,6 +207,8 @@ def dora_report(args):
                 "data": "synthetic", "config": {"workload": f"W {k} x {n}, r {r}"},
                 "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                "timing": "median of event-timed trials, 512 MiB read between trials (cache flush)",
+                "ms_back_to_back": ms_b2b,
                 "eager_torch": {"ms": eager_ms, "speedup": eager_ms / ms}}
         if not args.no_cpu_baseline:
             import numpy as np
@@ -472,20 +462,25 @@ def committed_traffic(kernel: str):
 class Timer:
     """Per-step HIP-event timing on one stream.  Each trial is bracketed by its
     own event pair; between trials (outside the events) a 512 MiB scratch
-    buffer is overwritten, which evicts the 256 MB Infinity Cache and the L2s,
-    so every trial starts from HBM (median of event-timed trials with the
-    caches flushed, the timing method of the Scaling DoRA page, "reproduction
-    and evaluation")."""
+    buffer is read, which evicts the 256 MB Infinity Cache and the L2s, so
+    every trial starts from HBM (median of event-timed trials with the caches
+    flushed, the timing method of the Scaling DoRA page, "reproduction and
+    evaluation").  The flush reads rather than writes: a written buffer would
+    leave up to 256 MB of dirty lines whose write-back lands inside the next
+    trial (it doubled a 30 us DoRA call and added about 38 us to the 70B
+    batch's first kernel), while reading also writes the previous trial's dirty
+    outputs back before the events start."""
 
     FLUSH_BYTES = 512 << 20
 
     def __init__(self, torch, stream):
         self.torch = torch
         self.stream = stream
-        self.scratch = torch.empty(self.FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.scratch = torch.ones(self.FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = None
 
     def flush(self):
-        self.scratch.fill_(1.0)
+        self.sink = self.scratch.sum()
 
     def trials(self, fn, steps, warmup, flush=True):
         torch = self.torch
@@ -752,7 +747,7 @@ def main():
                                f"{np.diff(w.seg_off).tolist()}, alpha=2, p=0.1",
                    "m": m, "k": k, "n": n, "ranks": [a.r for a in w.adapters],
                    "segments": w.seg_off.tolist(), "timing": "median of per-step HIP-event trials, "
-                   "512 MiB cache flush between trials"},
+                   "512 MiB read between trials (cache flush)"},
         "ms_per_step_mean": round(sum(t_all) / K, 4),
         "ms_per_step_min": round(ts[0], 4),
         "ms_per_step_back_to_back": round(ms_b2b, 4),
