@@ -105,6 +105,8 @@ DORA_CASES = [
     (520, 776, 129, 2.0),     # the first such rank: element-wise A reads
     (1000, 1032, 203, -0.7),  # ragged sub-block and column tile, element-wise A reads
     (8200, 264, 160, 1.5),    # 33 row splits, the last one 8 rows
+    (5, 264, 256, 1.0),       # one sub-block of 5 rows (both halves partly empty)
+    (40, 8, 250, -2.0),       # one 8-column group, element-wise A reads
 ]
 
 
