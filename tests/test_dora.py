@@ -134,8 +134,9 @@ def test_dora_large_alpha_dominated():
 
 
 @pytest.mark.gpu
-def test_dora_deterministic():
-    W, A, B = rand_case(2048, 1024, 32, seed=11)
+@pytest.mark.parametrize("r", [32, 200])
+def test_dora_deterministic(r):
+    W, A, B = rand_case(2048, 1024, r, seed=11)
     W, A, B = W.cuda(), A.cuda(), B.cuda()
     a = lf.lora_dora_norm(W, A, B, 2.0)
     b = lf.lora_dora_norm(W, A, B, 2.0)
